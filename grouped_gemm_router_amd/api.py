@@ -1,0 +1,186 @@
+"""ctypes binding of libmoe.so with the same names as the C ABI (include/moe.h).
+
+Argument marshalling only: sizes are read off the tensors, pointers and the
+current HIP stream are handed to the library, and a non-OK status raises
+``MoEError``.  Every step runs in the library's HIP kernels; there is no
+fallback of any kind.  Importing this module loads the library and raises if
+it has not been built (``python -m grouped_gemm_router_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = range(5)
+MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
+MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
+MOE_ROUTE_RENORM, MOE_ROUTE_FROM_LOGITS = 1, 2
+ABI_VERSION = 1
+
+EXPORTS = ["moe_status_string", "moe_abi_version", "moe_route", "moe_permute_workspace_size",
+           "moe_permute", "moe_grouped_gemm", "moe_grouped_gemm_fp8", "moe_combine",
+           "moe_quantize_fp8"]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (fn, status_string(status), status))
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libmoe.so is not built at %s; run `python -m "
+                          "grouped_gemm_router_amd.build`" % _LIB_PATH)
+    lib = C.CDLL(_LIB_PATH)
+    vp, i32, u32, sz = C.c_void_p, C.c_int, C.c_uint, C.c_size_t
+    lib.moe_status_string.restype = C.c_char_p
+    lib.moe_status_string.argtypes = [i32]
+    lib.moe_abi_version.restype = i32
+    lib.moe_abi_version.argtypes = []
+    lib.moe_route.restype = i32
+    lib.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp]
+    lib.moe_permute_workspace_size.restype = sz
+    lib.moe_permute_workspace_size.argtypes = [i32, i32, i32]
+    lib.moe_permute.restype = i32
+    lib.moe_permute.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                vp, vp, sz, vp]
+    lib.moe_grouped_gemm.restype = i32
+    lib.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, vp]
+    lib.moe_grouped_gemm_fp8.restype = i32
+    lib.moe_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
+                                         i32, i32, vp]
+    lib.moe_combine.restype = i32
+    lib.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp]
+    lib.moe_quantize_fp8.restype = i32
+    lib.moe_quantize_fp8.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise ImportError("libmoe.so ABI version %d, binding expects %d"
+                          % (lib.moe_abi_version(), ABI_VERSION))
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.moe_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+def _ptr(t) -> C.c_void_p:
+    if t is None:
+        return C.c_void_p(0)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor, got %r" % type(t))
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MOE_E4M3
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+# ----------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ----------------------------------------------------------------------------
+
+def moe_route(x, w_router, topk_idx, topk_w, *, logits=None, logit_bias=None, flags=0,
+              stream=None):
+    """Router scoring + top-k.  x [T][d], w_router [E][d] (fp32 or bf16);
+    topk_idx [T][k] int32 and topk_w [T][k] fp32 are written; logits [T][E]
+    fp32 is written if given (read instead with MOE_ROUTE_FROM_LOGITS)."""
+    T, k = topk_idx.shape
+    if flags & MOE_ROUTE_FROM_LOGITS:
+        E = logits.shape[1]
+        d, dt = 8, MOE_BF16
+    else:
+        d = x.shape[1]
+        E = w_router.shape[0]
+        dt = _dt(x)
+    _check("moe_route", lib.moe_route(_ptr(x), _ptr(w_router), dt, _ptr(logit_bias), T, d, E,
+                                      k, flags, _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                                      _stream(stream)))
+
+
+def moe_permute_workspace_size(T: int, k: int, E: int) -> int:
+    return int(lib.moe_permute_workspace_size(T, k, E))
+
+
+def moe_permute(x, topk_idx, E, n_shared, x_perm, counts, offsets, perm_src, flat_to_row, ws, *,
+                x_perm_scale=None, stream=None):
+    """Histogram + offsets + stable scatter.  x_perm's dtype selects the
+    output: same as x (bit copy) or uint8 (E4M3 with 1x128 scales)."""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    out_dt = _dt(x_perm)
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_permute", lib.moe_permute(_ptr(x), _dt(x), T, d, _ptr(topk_idx), k, E, n_shared,
+                                          out_dt, _ptr(x_perm), _ptr(x_perm_scale),
+                                          _ptr(counts), _ptr(offsets), _ptr(perm_src),
+                                          _ptr(flat_to_row), _ptr(ws), ws_bytes,
+                                          _stream(stream)))
+
+
+def moe_grouped_gemm(A, B, C_out, offsets, *, B2=None, epi=MOE_EPI_NONE, stream=None):
+    """C[r] = A[r] B[g]^T for rows r of group g (offsets on the device)."""
+    rows, K = A.shape
+    G, N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A is [rows][%d] but B is [G][N][%d]" % (K, K2))
+    if offsets.numel() != G + 1:
+        raise ValueError("offsets must have G + 1 = %d entries" % (G + 1))
+    _check("moe_grouped_gemm", lib.moe_grouped_gemm(_ptr(A), _ptr(B), _ptr(B2), _dt(A),
+                                                    _ptr(C_out), _dt(C_out), _ptr(offsets), G,
+                                                    rows, N, K, epi, _stream(stream)))
+
+
+def moe_grouped_gemm_fp8(A_q, A_scale, B_q, B_scale, C_out, offsets, *, B2_q=None,
+                         B2_scale=None, C_scale=None, epi=MOE_EPI_NONE, stream=None):
+    rows, K = A_q.shape
+    G, N, K2 = B_q.shape
+    if K2 != K:
+        raise ValueError("A_q is [rows][%d] but B_q is [G][N][%d]" % (K, K2))
+    if offsets.numel() != G + 1:
+        raise ValueError("offsets must have G + 1 = %d entries" % (G + 1))
+    c_dt = MOE_E4M3 if C_out.dtype in (torch.uint8, torch.float8_e4m3fn) else _dt(C_out)
+    _check("moe_grouped_gemm_fp8",
+           lib.moe_grouped_gemm_fp8(_ptr(A_q), _ptr(A_scale), _ptr(B_q), _ptr(B_scale),
+                                    _ptr(B2_q), _ptr(B2_scale), _ptr(C_out), c_dt,
+                                    _ptr(C_scale), _ptr(offsets), G, rows, N, K, epi,
+                                    _stream(stream)))
+
+
+def moe_combine(Y, flat_to_row, topk_w, out, *, n_shared=0, stream=None):
+    T, k = topk_w.shape
+    d = Y.shape[1]
+    _check("moe_combine", lib.moe_combine(_ptr(Y), _dt(Y), _ptr(flat_to_row), _ptr(topk_w), T, k,
+                                          d, n_shared, _ptr(out), _dt(out), _stream(stream)))
+
+
+def moe_quantize_fp8(src, q, scale, *, block_rows=128, block_cols=128, stream=None):
+    R, Cn = src.shape
+    _check("moe_quantize_fp8", lib.moe_quantize_fp8(_ptr(src), _dt(src), R, Cn, block_rows,
+                                                    block_cols, _ptr(q), _ptr(scale),
+                                                    _stream(stream)))

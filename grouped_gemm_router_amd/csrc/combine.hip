@@ -1,0 +1,114 @@
+// combine.hip -- gather the expert outputs back to token order, weight them
+// by the gate and sum.
+//
+// "Dense GEMM to TP MoE" §2.2 step 6: gather back in the original order,
+// multiply by the gate weight, sum.  "DeepGEMM walkthrough" §2.1: the shared
+// expert is added with weight one.
+//
+// One workgroup per token.  Each thread owns 8 consecutive columns (one
+// 16-byte bf16 piece, two for fp32): it issues all k + n_shared row loads,
+// then accumulates in fp32 in ascending j with fused multiply-adds, then the
+// shared rows, and stores once.  HBM traffic is one read of every used Y row
+// and one write of out.
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+template <int YSIZE>
+__device__ __forceinline__ void load8(const void *base, size_t elem, float v[8]) {
+  if (YSIZE == 2) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+      v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem);
+    const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+constexpr int kMaxTerms = MOE_MAX_TOPK + 8;
+
+template <int YSIZE, int OSIZE>
+__global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ Y,
+                                                      const int32_t *__restrict__ flat_to_row,
+                                                      const float *__restrict__ topk_w, int T,
+                                                      int k, int d, int n_shared,
+                                                      void *__restrict__ out) {
+  __shared__ int s_row[kMaxTerms];
+  __shared__ float s_w[kMaxTerms];
+  const int t = blockIdx.x;
+  const int nterm = k + n_shared;
+  if (threadIdx.x < nterm) {
+    const int j = threadIdx.x;
+    if (j < k) {
+      s_row[j] = flat_to_row[(size_t)t * k + j];
+      s_w[j] = topk_w[(size_t)t * k + j];
+    } else {
+      s_row[j] = flat_to_row[(size_t)T * k + (size_t)(j - k) * T + t];
+      s_w[j] = 1.0f;
+    }
+  }
+  __syncthreads();
+  const long long nrows = (long long)T * k + (long long)n_shared * T;
+  const int npiece = d / 8;
+  for (int p = threadIdx.x; p < npiece; p += blockDim.x) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j = 0; j < nterm; ++j) {
+      const int row = s_row[j];
+      if (row < 0 || row >= nrows) continue;  // dropped entry (or bad index)
+      float v[8];
+      load8<YSIZE>(Y, (size_t)row * d + (size_t)p * 8, v);
+      if (j < k) {
+        const float w = s_w[j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      }
+    }
+    if (OSIZE == 2) {
+      uint4 o;
+      o.x = f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+      o.y = f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+      o.z = f32_to_bf16_bits(acc[4]) | ((uint32_t)f32_to_bf16_bits(acc[5]) << 16);
+      o.w = f32_to_bf16_bits(acc[6]) | ((uint32_t)f32_to_bf16_bits(acc[7]) << 16);
+      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + (size_t)t * d + (size_t)p * 8) = o;
+    } else {
+      float *o = static_cast<float *>(out) + (size_t)t * d + (size_t)p * 8;
+      *reinterpret_cast<float4 *>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4 *>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void *Y, int y_dt, const int32_t *flat_to_row,
+                          const float *topk_w, int T, int k, int d, int n_shared, void *out,
+                          int out_dt, hipStream_t s) {
+  const dim3 grid(T), block(d >= 2048 ? 256 : 64);
+  if (y_dt == MOE_BF16 && out_dt == MOE_BF16)
+    hipLaunchKernelGGL((combine_kernel<2, 2>), grid, block, 0, s, Y, flat_to_row, topk_w, T, k, d,
+                       n_shared, out);
+  else if (y_dt == MOE_BF16)
+    hipLaunchKernelGGL((combine_kernel<2, 4>), grid, block, 0, s, Y, flat_to_row, topk_w, T, k, d,
+                       n_shared, out);
+  else if (out_dt == MOE_BF16)
+    hipLaunchKernelGGL((combine_kernel<4, 2>), grid, block, 0, s, Y, flat_to_row, topk_w, T, k, d,
+                       n_shared, out);
+  else
+    hipLaunchKernelGGL((combine_kernel<4, 4>), grid, block, 0, s, Y, flat_to_row, topk_w, T, k, d,
+                       n_shared, out);
+  return hipGetLastError();
+}

@@ -1,0 +1,238 @@
+// moe_internal.h -- device helpers and host launcher declarations shared by
+// the HIP translation units of libmoe.so.  Written for gfx950 (CDNA4):
+// 64-lane wavefronts, MFMA matrix cores, 160 KB of LDS per CU, 8 XCDs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte piece
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// binary32 -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// binary32 -> OCP E4M3FN, round to nearest even, saturating to +-448; the
+// input's sign is kept (so tiny values give +0 / -0).  Normal results keep
+// the top 3 mantissa bits and round on the 20 discarded ones; results below
+// 2^-6 are multiples of 2^-9 and are rounded as an integer count of 2^-9.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                 // NaN in, NaN out
+  if (a >= 0x43e00000u) return sign | 0x7eu;         // |v| >= 448
+  if (a < 0x3c800000u) {                             // |v| < 2^-6
+    float m = rintf(__uint_as_float(a) * 512.0f);    // exact scale, RNE
+    return sign | (uint32_t)m;                       // m == 8 is 2^-6 (code 8)
+  }
+  uint32_t e = (a >> 23) - 127u + 7u;                // 1..15
+  uint32_t r = (a >> 20) & 7u;
+  uint32_t rem = a & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+  if (r == 8u) { r = 0; ++e; }
+  return sign | (e << 3) | r;
+}
+
+// ---------------------------------------------------------------------------
+// wavefront reductions (butterfly; every lane ends with the result, and the
+// combination order is fixed, so results are deterministic)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// max over aligned groups of `width` lanes (width a power of two <= 64)
+__device__ __forceinline__ float group_max(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------------------
+// device-side group/tile scheduler shared by the grouped GEMM kernels.
+//
+// Each group g owns rows [o_g, o_g + M_g) with o_g = clamp(offsets[g], 0,
+// rows) and M_g = max(0, clamp(offsets[g+1]) - o_g).  Group g is cut into
+// mt_g = ceil(M_g / BM) row tiles and nt column tiles.  The linear tile id
+// runs over groups in order; inside a group it walks chunks of `chunk`
+// column tiles, and inside a chunk all row tiles of the group for each
+// column tile of the chunk in turn, so tiles that run at the same time share
+// both weight columns and activation rows.
+// ---------------------------------------------------------------------------
+
+struct TileSched {
+  int *cum;   // [G+1] cumulative row tiles (LDS)
+  int total;  // number of (row tile, column tile) pairs
+};
+
+// Block-wide: fills cum[0..G] (LDS, G+1 ints) from the device offsets array.
+// Must be called by all threads of the block.
+template <int NTHREADS>
+__device__ __forceinline__ void sched_build(const int32_t *__restrict__ offsets, int G,
+                                            int rows, int BM, int *cum, int *s_tmp) {
+  // each thread owns a contiguous run of groups
+  const int tid = threadIdx.x;
+  const int per = (G + NTHREADS - 1) / NTHREADS;
+  const int g0 = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    int g = g0 + i;
+    if (g < G) {
+      int a = min(max(offsets[g], 0), rows);
+      int b = min(max(offsets[g + 1], 0), rows);
+      int m = max(b - a, 0);
+      local += (m + BM - 1) / BM;
+    }
+  }
+  // block exclusive scan of `local`
+  const int lane = tid & (kWave - 1), wv = tid / kWave;
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) s_tmp[wv] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wv; ++w) wbase += s_tmp[w];
+  int run = wbase + incl - local;
+  for (int i = 0; i < per; ++i) {
+    int g = g0 + i;
+    if (g < G) {
+      cum[g] = run;
+      int a = min(max(offsets[g], 0), rows);
+      int b = min(max(offsets[g + 1], 0), rows);
+      int m = max(b - a, 0);
+      run += (m + BM - 1) / BM;
+    }
+  }
+  if (tid == NTHREADS - 1) cum[G] = run;
+  __syncthreads();
+}
+
+struct Tile {
+  int g;     // group
+  int m0;    // first row of the tile
+  int mend;  // one past the last valid row of the tile (<= group end)
+  int nt;    // column tile index
+};
+
+// Maps a linear tile id to (group, rows, column tile).  cum is the LDS table
+// from sched_build; nt_count column tiles per row tile.
+__device__ __forceinline__ Tile sched_tile(int L, const int *cum, int G,
+                                           const int32_t *__restrict__ offsets, int rows,
+                                           int BM, int nt_count, int chunk) {
+  // find g with cum[g] * nt_count <= L < cum[g+1] * nt_count (binary search)
+  int lo = 0, hi = G;  // invariant: cum[lo]*nt <= L < cum[hi]*nt
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cum[mid] * nt_count <= L) lo = mid; else hi = mid;
+  }
+  // cum[lo+1] > cum[lo], so group lo is never an empty group
+  int g = lo;
+  int mt_g = cum[g + 1] - cum[g];
+  int li = L - cum[g] * nt_count;
+  int per_chunk = chunk * mt_g;
+  int c = li / per_chunk;
+  int within = li - c * per_chunk;
+  int cw = min(chunk, nt_count - c * chunk);
+  int mt = within / cw;
+  int nt = c * chunk + (within - mt * cw);
+  Tile t;
+  t.g = g;
+  int a = min(max(offsets[g], 0), rows);
+  int b = min(max(offsets[g + 1], 0), rows);
+  int mg = max(b - a, 0);
+  t.m0 = a + mt * BM;
+  t.mend = min(a + mg, t.m0 + BM);
+  t.nt = nt;
+  return t;
+}
+
+// XCD-aware remap: hardware hands workgroup w to XCD (w % 8).  Give each XCD
+// a contiguous range of linear tile ids so that neighbouring tiles (which
+// share operands) run on the same XCD and share its L2.  Returns -1 for a
+// workgroup with nothing to do.
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  int per = (total + 7) / 8;
+  int x = w & 7, i = w >> 3;
+  if (i >= per) return -1;
+  int L = x * per + i;
+  return L < total ? L : -1;
+}
+
+// Upper bound on the number of row tiles over all groups, known on the host:
+// sum_g ceil(M_g / BM) <= floor(rows / BM) + G.
+inline int host_row_tile_bound(int rows, int G, int BM) { return rows / BM + G; }
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// host launchers (one per translation unit); return hipSuccess or an error.
+// Arguments are validated by the C-ABI layer before these are called.
+// ---------------------------------------------------------------------------
+
+hipError_t launch_route(const void *x, const void *w_router, int dt, const float *bias,
+                        int T, int d, int E, int k, unsigned flags, float *logits,
+                        int32_t *topk_idx, float *topk_w, hipStream_t s);
+
+size_t permute_ws_bytes(int T, int k, int E);
+hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *topk_idx,
+                          int k, int E, int n_shared, int out_dt, void *x_perm,
+                          float *x_perm_scale, int32_t *counts, int32_t *offsets,
+                          int32_t *perm_src, int32_t *flat_to_row, void *ws, hipStream_t s);
+
+hipError_t launch_gemm_bf16_mfma(const void *A, const void *B, const void *B2, void *C,
+                                 int c_dt, const int32_t *offsets, int G, int rows, int N,
+                                 int K, int epi, hipStream_t s);
+bool gemm_bf16_mfma_supports(int N, int K, int epi);
+
+hipError_t launch_gemm_simple(const void *A, const void *B, const void *B2, int ab_dt,
+                              void *C, int c_dt, const int32_t *offsets, int G, int rows,
+                              int N, int K, int epi, hipStream_t s);
+
+hipError_t launch_gemm_fp8(const uint8_t *Aq, const float *As, const uint8_t *Bq,
+                           const float *Bs, const uint8_t *B2q, const float *B2s, void *C,
+                           int c_dt, float *C_scale, const int32_t *offsets, int G, int rows,
+                           int N, int K, int epi, hipStream_t s);
+
+hipError_t launch_combine(const void *Y, int y_dt, const int32_t *flat_to_row,
+                          const float *topk_w, int T, int k, int d, int n_shared, void *out,
+                          int out_dt, hipStream_t s);
+
+hipError_t launch_quantize_fp8(const void *src, int src_dt, int R, int C, int br, int bc,
+                               uint8_t *q, float *scale, hipStream_t s);

@@ -1,0 +1,270 @@
+// permute.hip -- per-expert histogram, exclusive prefix sum and stable
+// scatter of tokens into expert-contiguous rows.
+//
+// "Dense GEMM to TP MoE" §2.2 steps 3-4: count the tokens of every expert,
+// take the prefix sum to get each expert's offset in the permuted buffer,
+// scatter the tokens there; §4.2: offsets = cumsum(counts) - counts.
+// "DeepGEMM walkthrough" §4.3: tokens of one expert laid out contiguously
+// turn expert compute into a list of contiguous GEMMs.
+//
+// Three launches, all deterministic (no order-dependent atomics):
+//   1. rank     one wave per block of 64 tokens: each lane (token) ORs its
+//               k experts into a per-expert 64-bit LDS bitmap; the rank of
+//               (t, j) inside the block is popcount(bitmap & lanes-below);
+//               the block's count per expert is popcount(bitmap).
+//               Ranks are parked in flat_to_row, counts in the workspace.
+//   2. scan     one workgroup: per expert, exclusive prefix over blocks
+//               (in place), then the exclusive prefix over experts ->
+//               offsets; block bases become absolute rows.
+//   3. scatter  rows = block base + rank -> perm_src / flat_to_row; then the
+//               row copy: every source row is read once and stored to its k
+//               destinations (plus the shared-expert rows), in 16-byte
+//               pieces; with E4M3 output each 1 x 128 group is quantised
+//               (absmax over 16 lanes, s = absmax / 448, RNE) on the way.
+// Rows within an expert come out in ascending flat index t*k + j, exactly as
+// a stable sort by expert id orders them.
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr int kBlk = 64;  // tokens per rank block (one wave)
+
+// ---- 1. rank ---------------------------------------------------------------
+__global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t *__restrict__ idx, int T,
+                                                        int k, int E, int nblk,
+                                                        int32_t *__restrict__ blk_counts,
+                                                        int32_t *__restrict__ flat_to_row) {
+  extern __shared__ unsigned long long bits[];  // [4][E]
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  const int b = blockIdx.x * 4 + wv;
+  unsigned long long *mine = bits + (size_t)wv * E;
+  for (int e = lane; e < E; e += kWave) mine[e] = 0ull;
+  __syncthreads();
+  const int t = b * kBlk + lane;
+  const bool live = (b < nblk) && (t < T);
+  if (live) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(size_t)t * k + j];
+      if (e >= 0 && e < E) atomicOr(&mine[e], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (live) {
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(size_t)t * k + j];
+      int r = -1;
+      if (e >= 0 && e < E) r = __popcll(mine[e] & below);
+      flat_to_row[(size_t)t * k + j] = r;
+    }
+  }
+  if (b < nblk)
+    for (int e = lane; e < E; e += kWave) blk_counts[(size_t)b * E + e] = __popcll(mine[e]);
+}
+
+// ---- 2. scan ---------------------------------------------------------------
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_shared, int nblk,
+                                                         int32_t *__restrict__ blk,
+                                                         int32_t *__restrict__ counts,
+                                                         int32_t *__restrict__ offsets) {
+  __shared__ int s_wave[16];
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  // per expert: exclusive prefix over blocks, in place
+  int total = 0;
+  if (tid < E) {
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blk[(size_t)b * E + tid];
+      blk[(size_t)b * E + tid] = total;
+      total += c;
+    }
+    counts[tid] = total;
+  }
+  // exclusive prefix over experts (wave scan + wave totals)
+  int incl = total;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) s_wave[wv] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wv; ++w) base += s_wave[w];
+  const int excl = base + incl - total;
+  if (tid < E) {
+    s_off[tid] = excl;
+    offsets[tid] = excl;
+  }
+  if (tid == E - 1) {
+    const int routed = excl + total;
+    offsets[E] = routed;
+    for (int s = 0; s < n_shared; ++s) offsets[E + s + 1] = routed + (s + 1) * T;
+  }
+  __syncthreads();
+  if (tid < E) {
+    const int o = s_off[tid];
+    for (int b = 0; b < nblk; ++b) blk[(size_t)b * E + tid] += o;
+  }
+}
+
+// ---- 3. scatter + row copy ----------------------------------------------------
+template <int ESIZE, bool QUANT>
+__global__ __launch_bounds__(256) void perm_scatter_kernel(
+    const void *__restrict__ xv, int T, int d, const int32_t *__restrict__ idx, int k, int E,
+    int n_shared, int tpb, const int32_t *__restrict__ blk_base,
+    const int32_t *__restrict__ offsets, int32_t *__restrict__ perm_src,
+    int32_t *__restrict__ flat_to_row, void *__restrict__ x_perm, float *__restrict__ x_scale) {
+  extern __shared__ int s_row[];  // [tpb * k]
+  const int t0 = blockIdx.x * tpb;
+  const int t1 = min(t0 + tpb, T);
+  const int nent = (t1 - t0) * k;
+  // shared-expert rows follow the routed rows: row = offsets[E] + s*T + t
+  const size_t shared_base = (size_t)offsets[E];
+  for (int i = threadIdx.x; i < (t1 - t0) * n_shared; i += blockDim.x) {
+    const int s = i / (t1 - t0), t = t0 + i % (t1 - t0);
+    flat_to_row[(size_t)T * k + (size_t)s * T + t] = (int32_t)(shared_base + (size_t)s * T + t);
+  }
+  for (int i = threadIdx.x; i < nent; i += blockDim.x) {
+    const size_t f = (size_t)t0 * k + i;
+    const int e = idx[f];
+    int row = -1;
+    if (e >= 0 && e < E) {
+      const int t = (int)(f / k);
+      row = blk_base[(size_t)(t / kBlk) * E + e] + flat_to_row[f];
+      perm_src[row] = (int32_t)f;
+    }
+    flat_to_row[f] = row;
+    s_row[i] = row;
+  }
+  __syncthreads();
+  const char *x = static_cast<const char *>(xv);
+  if (!QUANT) {
+    // 16-byte pieces; d * ESIZE is a multiple of 16
+    const int cpr = d * ESIZE / 16;
+    const int items = (t1 - t0) * cpr;
+    uint4 *dst = static_cast<uint4 *>(x_perm);
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+      const int tt = it / cpr, c = it - tt * cpr;
+      const int t = t0 + tt;
+      const uint4 v = reinterpret_cast<const uint4 *>(x + (size_t)t * d * ESIZE)[c];
+      for (int j = 0; j < k; ++j) {
+        const int row = s_row[tt * k + j];
+        if (row >= 0) dst[(size_t)row * cpr + c] = v;
+      }
+      for (int s = 0; s < n_shared; ++s)
+        dst[(shared_base + (size_t)s * T + t) * cpr + c] = v;
+    }
+  } else {
+    // one 1 x 128 group per 16 lanes, 8 elements per lane
+    const int gpr = d / 128;
+    const int items = (t1 - t0) * gpr;
+    const int lane16 = threadIdx.x & 15;
+    uint8_t *dst = static_cast<uint8_t *>(x_perm);
+    // every 16-lane group iterates the same number of times, so the
+    // shuffles below always see their whole group
+    for (int base = threadIdx.x >> 4; base < ((items + 15) / 16) * 16; base += blockDim.x >> 4) {
+      const int it = base;
+      const bool ok = it < items;
+      const int tt = ok ? it / gpr : 0, gi = ok ? it - tt * gpr : 0;
+      const int t = t0 + tt;
+      float v[8];
+      const size_t e0 = (size_t)t * d + gi * 128 + lane16 * 8;
+      if (ok) {
+        if (ESIZE == 2) {
+          const uint4 raw = *reinterpret_cast<const uint4 *>(x + e0 * 2);
+          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+            v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+          }
+        } else {
+          const float4 a = *reinterpret_cast<const float4 *>(x + e0 * 4);
+          const float4 b2 = *reinterpret_cast<const float4 *>(x + e0 * 4 + 16);
+          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+          v[4] = b2.x; v[5] = b2.y; v[6] = b2.z; v[7] = b2.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      amax = group_max(amax, 16);
+      const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] / sc) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] / sc) << (8 * i);
+      const uint2 q = make_uint2(lo, hi);
+      if (ok) {
+        for (int j = 0; j < k + n_shared; ++j) {
+          size_t row;
+          if (j < k) {
+            const int r = s_row[tt * k + j];
+            if (r < 0) continue;
+            row = (size_t)r;
+          } else {
+            row = shared_base + (size_t)(j - k) * T + t;
+          }
+          *reinterpret_cast<uint2 *>(dst + row * d + gi * 128 + lane16 * 8) = q;
+          if (lane16 == 0) x_scale[row * gpr + gi] = sc;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int T, int k, int E) {
+  (void)k;
+  const size_t nblk = ((size_t)T + kBlk - 1) / kBlk;
+  return nblk * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *topk_idx, int k,
+                          int E, int n_shared, int out_dt, void *x_perm, float *x_perm_scale,
+                          int32_t *counts, int32_t *offsets, int32_t *perm_src,
+                          int32_t *flat_to_row, void *ws, hipStream_t s) {
+  const int nblk = (T + kBlk - 1) / kBlk;
+  int32_t *blk = static_cast<int32_t *>(ws);
+  hipLaunchKernelGGL(perm_rank_kernel, dim3((nblk + 3) / 4), dim3(256),
+                     sizeof(unsigned long long) * 4 * (size_t)E, s, topk_idx, T, k, E, nblk, blk,
+                     flat_to_row);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, T, E, n_shared, nblk, blk,
+                     counts, offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int tpb = T >= 4096 ? 16 : (T >= 1024 ? 4 : 1);
+  const dim3 grid((T + tpb - 1) / tpb), block(256);
+  const size_t lds = sizeof(int) * (size_t)tpb * k;
+  const bool quant = out_dt == MOE_E4M3;
+  if (x_dt == MOE_BF16) {
+    if (quant)
+      hipLaunchKernelGGL((perm_scatter_kernel<2, true>), grid, block, lds, s, x, T, d, topk_idx,
+                         k, E, n_shared, tpb, blk, offsets, perm_src, flat_to_row, x_perm,
+                         x_perm_scale);
+    else
+      hipLaunchKernelGGL((perm_scatter_kernel<2, false>), grid, block, lds, s, x, T, d, topk_idx,
+                         k, E, n_shared, tpb, blk, offsets, perm_src, flat_to_row, x_perm,
+                         x_perm_scale);
+  } else {
+    if (quant)
+      hipLaunchKernelGGL((perm_scatter_kernel<4, true>), grid, block, lds, s, x, T, d, topk_idx,
+                         k, E, n_shared, tpb, blk, offsets, perm_src, flat_to_row, x_perm,
+                         x_perm_scale);
+    else
+      hipLaunchKernelGGL((perm_scatter_kernel<4, false>), grid, block, lds, s, x, T, d, topk_idx,
+                         k, E, n_shared, tpb, blk, offsets, perm_src, flat_to_row, x_perm,
+                         x_perm_scale);
+  }
+  return hipGetLastError();
+}

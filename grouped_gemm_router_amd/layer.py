@@ -1,0 +1,133 @@
+"""One MoE expert layer forward on one GPU, as five calls into libmoe.so.
+
+    route -> permute -> grouped GEMM gate/up (+SwiGLU) -> grouped GEMM down
+          -> combine
+
+("Dense GEMM to TP MoE" §2.2 data flow; "DeepGEMM walkthrough" §2.1 layer
+formula with the shared expert.)  This module only allocates buffers with
+torch and passes pointers; every step runs in the library's HIP kernels, on
+the current stream, with no host synchronisation and no host round trip of
+the per-expert sizes.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import api
+
+
+class MoELayer:
+    """Weights: w_router [E][d]; w_gate, w_up [G][dff][d]; w_down [G][d][dff]
+    with G = E + n_shared (shared experts last), all on the GPU.
+
+    dtype is taken from w_router: fp32 or bf16.  ``fp8=True`` quantises the
+    expert weights to E4M3 with 128 x 128 block scales (moe_quantize_fp8) and
+    runs both GEMMs in FP8 with 1 x 128 activation scales; the router stays in
+    the activation dtype and the output is bf16.
+    """
+
+    def __init__(self, w_router, w_gate, w_up, w_down, k, *, n_shared=0, bias=None, fp8=False,
+                 renorm=False, keep_logits=True):
+        self.E, self.d = w_router.shape
+        self.G, self.dff, d2 = w_gate.shape
+        assert d2 == self.d and self.G == self.E + n_shared
+        assert w_up.shape == w_gate.shape and w_down.shape == (self.G, self.d, self.dff)
+        self.k, self.n_shared, self.fp8 = k, n_shared, fp8
+        self.w_router = w_router.contiguous()
+        self.bias = None if bias is None else bias.to(torch.float32).contiguous()
+        self.flags = api.MOE_ROUTE_RENORM if renorm else 0
+        self.keep_logits = keep_logits
+        self.act_dtype = w_router.dtype
+        self.device = w_router.device
+        if fp8:
+            self.wg_q, self.wg_s = self._quant(w_gate)
+            self.wu_q, self.wu_s = self._quant(w_up)
+            self.wd_q, self.wd_s = self._quant(w_down)
+        else:
+            self.w_gate = w_gate.contiguous()
+            self.w_up = w_up.contiguous()
+            self.w_down = w_down.contiguous()
+        self._T = None
+
+    def _quant(self, w):
+        G, R, Cn = w.shape
+        q = torch.empty((G, R, Cn), dtype=torch.uint8, device=self.device)
+        s = torch.empty((G, R // 128, Cn // 128), dtype=torch.float32, device=self.device)
+        api.moe_quantize_fp8(w.contiguous().view(G * R, Cn), q.view(G * R, Cn),
+                             s.view(G * R // 128, Cn // 128), block_rows=128, block_cols=128)
+        return q, s
+
+    @property
+    def out_dtype(self):
+        return torch.bfloat16 if self.fp8 else self.act_dtype
+
+    def alloc(self, T: int):
+        """(Re)allocate the intermediate buffers for T tokens."""
+        if self._T == T:
+            return
+        dev, E, k, G, ns = self.device, self.E, self.k, self.G, self.n_shared
+        rows = T * k + ns * T
+        i32, f32 = torch.int32, torch.float32
+        self.logits = torch.empty((T, E), dtype=f32, device=dev) if self.keep_logits else None
+        self.topk_idx = torch.empty((T, k), dtype=i32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=f32, device=dev)
+        self.counts = torch.empty((E,), dtype=i32, device=dev)
+        self.offsets = torch.empty((G + 1,), dtype=i32, device=dev)
+        self.perm_src = torch.empty((T * k,), dtype=i32, device=dev)
+        self.flat_to_row = torch.empty((T * k + ns * T,), dtype=i32, device=dev)
+        ws = api.moe_permute_workspace_size(T, k, E)
+        self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
+        if self.fp8:
+            self.x_perm = torch.empty((rows, self.d), dtype=torch.uint8, device=dev)
+            self.x_scale = torch.empty((rows, self.d // 128), dtype=f32, device=dev)
+            self.h = torch.empty((rows, self.dff), dtype=torch.uint8, device=dev)
+            self.h_scale = torch.empty((rows, self.dff // 128), dtype=f32, device=dev)
+            self.y = torch.empty((rows, self.d), dtype=torch.bfloat16, device=dev)
+        else:
+            self.x_perm = torch.empty((rows, self.d), dtype=self.act_dtype, device=dev)
+            self.x_scale = None
+            self.h = torch.empty((rows, self.dff), dtype=self.act_dtype, device=dev)
+            self.h_scale = None
+            # expert outputs stay fp32 until the combine: a bf16 Y plus a bf16
+            # out would be two roundings of the largest outputs
+            self.y = torch.empty((rows, self.d), dtype=torch.float32, device=dev)
+        self._T = T
+
+    def steps(self, x, out):
+        """The five calls, as (name, thunk) pairs, for timing each one."""
+        E, ns = self.E, self.n_shared
+        s = [("route", lambda: api.moe_route(x, self.w_router, self.topk_idx, self.topk_w,
+                                             logits=self.logits, logit_bias=self.bias,
+                                             flags=self.flags)),
+             ("permute", lambda: api.moe_permute(x, self.topk_idx, E, ns, self.x_perm,
+                                                 self.counts, self.offsets, self.perm_src,
+                                                 self.flat_to_row, self.ws,
+                                                 x_perm_scale=self.x_scale))]
+        if self.fp8:
+            s.append(("gemm_gate_up", lambda: api.moe_grouped_gemm_fp8(
+                self.x_perm, self.x_scale, self.wg_q, self.wg_s, self.h, self.offsets,
+                B2_q=self.wu_q, B2_scale=self.wu_s, C_scale=self.h_scale,
+                epi=api.MOE_EPI_SWIGLU)))
+            s.append(("gemm_down", lambda: api.moe_grouped_gemm_fp8(
+                self.h, self.h_scale, self.wd_q, self.wd_s, self.y, self.offsets)))
+        else:
+            s.append(("gemm_gate_up", lambda: api.moe_grouped_gemm(
+                self.x_perm, self.w_gate, self.h, self.offsets, B2=self.w_up,
+                epi=api.MOE_EPI_SWIGLU)))
+            s.append(("gemm_down", lambda: api.moe_grouped_gemm(
+                self.h, self.w_down, self.y, self.offsets)))
+        s.append(("combine", lambda: api.moe_combine(self.y, self.flat_to_row, self.topk_w, out,
+                                                     n_shared=ns)))
+        return s
+
+    def forward(self, x, out=None):
+        T, d = x.shape
+        assert d == self.d and x.dtype == self.act_dtype and x.is_contiguous()
+        self.alloc(T)
+        if out is None:
+            out = torch.empty((T, d), dtype=self.out_dtype, device=self.device)
+        for _, fn in self.steps(x, out):
+            fn()
+        return out
+
+    __call__ = forward

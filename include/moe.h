@@ -1,0 +1,231 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward pass of a Mixture-of-Experts
+ * expert layer on one AMD Instinct MI355X (gfx950), as hand-written HIP
+ * kernels.
+ *
+ * The layer (source pages, by short title):
+ *   "DeepGEMM walkthrough" -- the MegaMoE maths / DeepGEMM source
+ *       walk-through page: §2.1 gives the router p = Softmax(W_r x), the
+ *       top-k selection and y = E_shared(x) + sum_{i in top-k} p_i E_i(x);
+ *       §2.3 gives the FP8 form C ~ (A_q / scale_A)(B_q / scale_B) scale_C;
+ *       §4.3 the grouped GEMM over an expert-contiguous layout; §5.1-5.3
+ *       scales, double buffering and ragged tails.
+ *   "Dense GEMM to TP MoE" -- the grouped-GEMM / tensor-parallel MoE page:
+ *       §2.2 gives the six-step data flow (score, top-k, per-expert count and
+ *       prefix sum, scatter, grouped GEMM, gather + gate weight + sum);
+ *       §2.3 the grouped_gemm(A_ptrs, B_ptrs, C_ptrs, expert_sizes, N, K,
+ *       workspace, stream) call and the rule that expert sizes stay on the
+ *       GPU; §4.2 the router and offset computation; §5.3-5.4 workspace
+ *       sizing and GPU-built pointer arrays.
+ *
+ * One forward pass is five calls on one stream, with no host round trip:
+ *   moe_route -> moe_permute -> moe_grouped_gemm(_fp8) (gate/up, SwiGLU)
+ *             -> moe_grouped_gemm(_fp8) (down) -> moe_combine
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to dense row-major arrays with
+ *     no strides, 16-byte aligned.  The caller allocates and frees every
+ *     buffer; the library never allocates, frees, synchronises or copies
+ *     device data to the host.
+ *   - Every call only enqueues kernels on `stream` (a hipStream_t; NULL is
+ *     the null stream) and returns; results are ready when the stream is.
+ *   - Sizes are checked on the host before anything is launched; a failed
+ *     check returns a status and launches nothing.  T == 0 is a no-op.
+ *   - Per-expert row counts exist only in the device array `offsets`; the
+ *     host passes only sizes it already knows (T, k, E, rows = T*k +
+ *     n_shared*T).
+ *   - Weights are stored [group][out][in] (the F.linear orientation), so a
+ *     GEMM computes C[r][n] = sum_k A[r][k] * B[g][n][k].  Routed experts are
+ *     groups 0..E-1; shared experts are groups E..E+n_shared-1.
+ *   - Kernels are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* bad argument: null/misaligned pointer, size out of range */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but not implemented (dtype combination, shape) */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than the size query returned */
+  MOE_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch */
+} moe_status_t;
+
+typedef enum {
+  MOE_F32 = 0,  /* IEEE binary32 */
+  MOE_BF16 = 1, /* bfloat16 */
+  MOE_E4M3 = 2  /* OCP FP8 E4M3FN: bias 7, no infinities, max 448 */
+} moe_dtype_t;
+
+typedef enum {
+  MOE_EPI_NONE = 0,  /* C = A B^T */
+  MOE_EPI_SWIGLU = 1 /* C = silu(A B^T) * (A B2^T), silu(z) = z / (1 + e^-z) */
+} moe_epilogue_t;
+
+typedef void *moe_stream_t; /* a hipStream_t */
+
+/* moe_route flags */
+#define MOE_ROUTE_RENORM 1u      /* w[t][j] /= sum_j w[t][j] (softmax over the k selected logits) */
+#define MOE_ROUTE_FROM_LOGITS 2u /* `logits` is an input; x, w_router and logit_bias are ignored */
+
+/* Library limits (checked on the host). */
+#define MOE_MAX_EXPERTS 1024 /* E */
+#define MOE_MAX_TOPK 32      /* k */
+#define MOE_MAX_GROUPS 1040  /* G = E + n_shared in a grouped GEMM */
+
+/* Static text for a status code (never NULL). */
+const char *moe_status_string(moe_status_t status);
+
+/* ABI version of this header; bumped on any incompatible change. */
+int moe_abi_version(void);
+
+/*
+ * Router scoring and top-k selection ("DeepGEMM walkthrough" §2.1; "Dense
+ * GEMM to TP MoE" §2.2 steps 1-2 and §4.2).
+ *
+ *   logits[t][e] = sum_c x[t][c] * w_router[e][c] + logit_bias[e]
+ *                  (fp32 accumulation; bias optional)
+ *   topk_idx[t][j] = the k experts with the largest logits, ordered by
+ *                  (logit descending, expert index ascending): equal logits
+ *                  (including -0 and +0) go to the lower index
+ *   topk_w[t][j]   = p[topk_idx[t][j]], p = softmax(logits[t][.]) over all E
+ *                  experts (max-subtracted, fp32); with MOE_ROUTE_RENORM
+ *                  divided by sum_j topk_w[t][j]
+ *
+ * x [T][d] and w_router [E][d] are both of type `dt` (MOE_F32 or MOE_BF16).
+ * logit_bias [E] fp32 or NULL.  logits [T][E] fp32: written if non-NULL; with
+ * MOE_ROUTE_FROM_LOGITS it is read instead (and must be non-NULL).
+ * topk_idx [T][k] int32, topk_w [T][k] fp32 are written.
+ * Requires 1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS, d % 8 == 0.
+ * Non-finite logits are a caller error (selection is then unspecified).
+ */
+moe_status_t moe_route(const void *x, const void *w_router, moe_dtype_t dt,
+                       const float *logit_bias, int T, int d, int E, int k,
+                       unsigned flags, float *logits, int32_t *topk_idx,
+                       float *topk_w, moe_stream_t stream);
+
+/* Bytes of device workspace moe_permute needs for these sizes. */
+size_t moe_permute_workspace_size(int T, int k, int E);
+
+/*
+ * Per-expert histogram, exclusive prefix sum and stable scatter of tokens
+ * into expert-contiguous order ("Dense GEMM to TP MoE" §2.2 steps 3-4, §4.2;
+ * "DeepGEMM walkthrough" §4.3 on the contiguous per-expert layout).
+ *
+ *   counts[e]   = #{(t, j) : topk_idx[t][j] == e}                 [E]
+ *   offsets[g]  = exclusive prefix sum of the group sizes          [E+n_shared+1]
+ *                 (routed experts first, then n_shared groups of T rows each)
+ *   perm_src[offsets[e] + r] = the r-th flat index f = t*k + j (ascending)
+ *                 whose expert is e (a stable counting sort)       [T*k]
+ *   flat_to_row[f] = the row that flat index f lands on, and
+ *   flat_to_row[T*k + s*T + t] = the row of token t in shared group s
+ *                 (= offsets[E] + s*T + t)             [T*k + n_shared*T]
+ *   x_perm[row]  = x[perm_src[row] / k] for routed rows, and
+ *   x_perm[offsets[E] + s*T + t] = x[t] for the shared groups
+ *                                                    [T*k + n_shared*T][d]
+ *
+ * out_dt == x_dt copies rows bit for bit.  out_dt == MOE_E4M3 (x_dt F32 or
+ * BF16) quantises every row in 1 x 128 groups ("DeepGEMM walkthrough" §2.3:
+ * per-token, per-group scales): s = absmax / 448 (1 if the group is all
+ * zero), q = E4M3 round-to-nearest-even of (x / s) with IEEE fp32 division,
+ * saturating at +-448; x_perm_scale [rows][d/128] receives s (d % 128 == 0
+ * required).  Otherwise x_perm_scale must be NULL.
+ * Each token's k experts must be distinct (top-k output always is).  An
+ * entry of topk_idx outside [0, E) is dropped: it is counted nowhere, its
+ * flat_to_row is -1 and no row is written for it; the rows stay compact
+ * (offsets[E] is then below T*k).  Requires d % 8 == 0.
+ * ws must hold moe_permute_workspace_size(T, k, E) bytes (else
+ * MOE_ERR_WORKSPACE).
+ */
+moe_status_t moe_permute(const void *x, moe_dtype_t x_dt, int T, int d,
+                         const int32_t *topk_idx, int k, int E, int n_shared,
+                         moe_dtype_t out_dt, void *x_perm, float *x_perm_scale,
+                         int32_t *counts, int32_t *offsets, int32_t *perm_src,
+                         int32_t *flat_to_row, void *ws, size_t ws_bytes,
+                         moe_stream_t stream);
+
+/*
+ * Grouped GEMM over ragged groups in one launch ("DeepGEMM walkthrough"
+ * §4.3; "Dense GEMM to TP MoE" §2.1, §2.3).  Group g owns rows
+ * offsets[g] .. offsets[g+1]-1 of A (device array, read by the kernel's own
+ * tile scheduler -- the group sizes never reach the host):
+ *   C[r][n] = sum_k A[r][k] * B[g][n][k]                       (MOE_EPI_NONE)
+ *   C[r][n] = silu(sum_k A[r][k] B[g][n][k]) * sum_k A[r][k] B2[g][n][k]
+ *                                                             (MOE_EPI_SWIGLU)
+ * A [rows][K], B and B2 [G][N][K] of type ab_dt (MOE_F32 or MOE_BF16),
+ * accumulation in fp32, C [rows][N] of type c_dt (MOE_F32 or MOE_BF16).
+ * B2 must be NULL unless epi == MOE_EPI_SWIGLU.  Rows of C outside every
+ * group are not written.  offsets values are clamped to [0, rows], so a bad
+ * offsets array gives wrong results but no out-of-bounds access.
+ * Requires K % 8 == 0, 1 <= G <= MOE_MAX_GROUPS.
+ */
+moe_status_t moe_grouped_gemm(const void *A, const void *B, const void *B2,
+                              moe_dtype_t ab_dt, void *C, moe_dtype_t c_dt,
+                              const int32_t *offsets, int G, int rows, int N,
+                              int K, moe_epilogue_t epi, moe_stream_t stream);
+
+/*
+ * FP8 block-scaled grouped GEMM ("DeepGEMM walkthrough" §2.3 and §5.1).
+ * The stored scales are dequantisation multipliers (the reciprocal of the
+ * page's scale_A / scale_B; scale_C = 1):
+ *   A[r][k]    ~ A_q[r][k] * A_scale[r][k/128]          A_scale [rows][K/128]
+ *   B[g][n][k] ~ B_q[g][n][k] * B_scale[g][n/128][k/128]
+ *                                                  B_scale [G][N/128][K/128]
+ *   C = A B^T (or the SwiGLU form with B2) computed as
+ *       sum_kb A_scale[r][kb] B_scale[g][n/128][kb] * (sum_{k in kb} A_q B_q)
+ *   with fp32 accumulation.
+ * c_dt == MOE_BF16 writes bf16.  c_dt == MOE_E4M3 quantises each output row
+ * in 1 x 128 groups exactly as moe_permute does and writes C_scale
+ * [rows][N/128]; C_scale must be NULL otherwise.
+ * Requires N % 128 == 0 and K % 128 == 0.
+ */
+moe_status_t moe_grouped_gemm_fp8(const uint8_t *A_q, const float *A_scale,
+                                  const uint8_t *B_q, const float *B_scale,
+                                  const uint8_t *B2_q, const float *B2_scale,
+                                  void *C, moe_dtype_t c_dt, float *C_scale,
+                                  const int32_t *offsets, int G, int rows,
+                                  int N, int K, moe_epilogue_t epi,
+                                  moe_stream_t stream);
+
+/*
+ * Gather back to token order, weight by the gate and sum ("Dense GEMM to TP
+ * MoE" §2.2 step 6; "DeepGEMM walkthrough" §2.1, shared expert weight 1):
+ *   out[t][c] = sum_{j=0}^{k-1} topk_w[t][j] * Y[flat_to_row[t*k+j]][c]
+ *               + sum_s Y[flat_to_row[T*k + s*T + t]][c]
+ * fp32 sum in ascending j, then the shared rows; flat_to_row
+ * [T*k + n_shared*T] is the array moe_permute wrote.  Y [T*k + n_shared*T][d]
+ * of type y_dt, out [T][d] of type out_dt (MOE_F32 or MOE_BF16 each).  A
+ * flat_to_row entry < 0 (a dropped entry) contributes nothing.
+ * Requires d % 8 == 0.
+ */
+moe_status_t moe_combine(const void *Y, moe_dtype_t y_dt,
+                         const int32_t *flat_to_row, const float *topk_w,
+                         int T, int k, int d, int n_shared, void *out,
+                         moe_dtype_t out_dt, moe_stream_t stream);
+
+/*
+ * Block FP8 quantisation of a matrix, for preparing expert weights
+ * ("DeepGEMM walkthrough" §2.3, §5.1: per-block scales):
+ *   src [R][C] (MOE_F32 or MOE_BF16) cut into block_rows x block_cols blocks,
+ *   s = absmax(block) / 448 (1 for an all-zero block),
+ *   q = E4M3 round-to-nearest-even of (src / s), fp32 IEEE division,
+ *       saturating at +-448.
+ * q [R][C] uint8, scale [R/block_rows][C/block_cols] fp32.  Requires
+ * block_rows in {1, 128}, block_cols == 128, R % block_rows == 0,
+ * C % 128 == 0.
+ */
+moe_status_t moe_quantize_fp8(const void *src, moe_dtype_t src_dt, int R,
+                              int C, int block_rows, int block_cols,
+                              uint8_t *q, float *scale, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

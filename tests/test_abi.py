@@ -1,0 +1,146 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/moe.h declares, and the host-side argument checks return the
+documented status without launching anything (no GPU is touched: every call
+below fails validation, or is a documented no-op, before any launch)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "grouped_gemm_router_amd", "libmoe.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16, E4M3 = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from grouped_gemm_router_amd import build
+        build.build()
+    L = C.CDLL(LIB)
+    vp, i32, u32, sz = C.c_void_p, C.c_int, C.c_uint, C.c_size_t
+    L.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp]
+    L.moe_permute_workspace_size.restype = sz
+    L.moe_permute_workspace_size.argtypes = [i32, i32, i32]
+    L.moe_permute.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                              vp, sz, vp]
+    L.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, vp]
+    L.moe_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
+                                       i32, i32, vp]
+    L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp]
+    L.moe_quantize_fp8.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.moe_status_string.restype = C.c_char_p
+    L.moe_status_string.argtypes = [i32]
+    return L
+
+
+P = C.c_void_p(0x10000)      # an aligned, never-dereferenced stand-in pointer
+P2 = C.c_void_p(0x20000)
+MIS = C.c_void_p(0x10002)    # misaligned
+NUL = C.c_void_p(0)
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), "libmoe.so does not export %s" % n
+
+
+def test_status_strings_and_version(lib):
+    for s in range(5):
+        assert lib.moe_status_string(s)
+    assert lib.moe_abi_version() == 1
+
+
+def test_route_validation(lib):
+    r = lambda *a: lib.moe_route(*a)  # noqa: E731
+    # k > E, k < 1, E > max, d % 8, dtype, null outputs, misaligned x
+    assert r(P, P, BF16, NUL, 16, 64, 4, 5, 0, NUL, P, P, NUL) == INVALID
+    assert r(P, P, BF16, NUL, 16, 64, 4, 0, 0, NUL, P, P, NUL) == INVALID
+    assert r(P, P, BF16, NUL, 16, 64, 2000, 2, 0, NUL, P, P, NUL) == UNSUPPORTED
+    assert r(P, P, BF16, NUL, 16, 60, 8, 2, 0, NUL, P, P, NUL) == UNSUPPORTED
+    assert r(P, P, E4M3, NUL, 16, 64, 8, 2, 0, NUL, P, P, NUL) == UNSUPPORTED
+    assert r(P, P, BF16, NUL, 16, 64, 8, 2, 0, NUL, NUL, P, NUL) == INVALID
+    assert r(MIS, P, BF16, NUL, 16, 64, 8, 2, 0, NUL, P, P, NUL) == INVALID
+    assert r(P, P, BF16, NUL, 16, 64, 8, 2, 8, NUL, P, P, NUL) == INVALID  # unknown flag
+    assert r(NUL, NUL, BF16, NUL, 16, 64, 8, 2, 2, NUL, P, P, NUL) == INVALID  # from-logits, no logits
+    assert r(P, P, BF16, NUL, -1, 64, 8, 2, 0, NUL, P, P, NUL) == INVALID
+    assert r(P, P, BF16, NUL, 0, 64, 8, 2, 0, NUL, P, P, NUL) == OK  # T == 0: no-op
+
+
+def test_permute_validation_and_workspace(lib):
+    ws = lib.moe_permute_workspace_size(4096, 8, 256)
+    assert ws >= 64 * 256 * 4
+    assert lib.moe_permute_workspace_size(-1, 2, 8) == 0
+    p = lambda x_dt, T, d, k, E, ns, odt, scale, wsb: lib.moe_permute(  # noqa: E731
+        P, x_dt, T, d, P, k, E, ns, odt, P, scale, P, P, P, P, P, wsb, NUL)
+    assert p(BF16, 4096, 4096, 2, 8, 0, BF16, NUL, 0) == WORKSPACE
+    # (a large enough workspace passes validation and would launch, so only
+    # failing cases are exercised here)
+    assert p(BF16, 64, 4096, 2, 8, 0, F32, NUL, 1 << 20) == UNSUPPORTED   # dtype change
+    assert p(BF16, 64, 4100, 2, 8, 0, E4M3, P, 1 << 20) == UNSUPPORTED    # d % 128 for fp8
+    assert p(BF16, 64, 4096, 2, 8, 0, E4M3, NUL, 1 << 20) == INVALID      # fp8 needs scales
+    assert p(BF16, 64, 4096, 2, 8, 0, BF16, P, 1 << 20) == INVALID        # scales only for fp8
+    assert p(BF16, 64, 4096, 9, 8, 0, BF16, NUL, 1 << 20) == INVALID      # k > E
+    assert p(BF16, 0, 4096, 2, 8, 0, BF16, NUL, 0) == OK                  # T == 0
+
+
+def test_permute_workspace_error_is_reported(lib):
+    need = lib.moe_permute_workspace_size(1000, 2, 8)
+    assert need > 0
+    rc = lib.moe_permute(P, BF16, 1000, 64, P, 2, 8, 0, BF16, P, NUL, P, P, P, P, P, need - 1, NUL)
+    assert rc == WORKSPACE
+
+
+def test_gemm_validation(lib):
+    g = lambda A, B, B2, dt, cdt, G, rows, N, K, epi: lib.moe_grouped_gemm(  # noqa: E731
+        A, B, B2, dt, P, cdt, P, G, rows, N, K, epi, NUL)
+    assert g(P, P, NUL, BF16, BF16, 0, 10, 256, 64, 0) == INVALID        # G < 1
+    assert g(P, P, NUL, BF16, BF16, 5000, 10, 256, 64, 0) == UNSUPPORTED  # G > max
+    assert g(P, P, NUL, BF16, BF16, 2, 10, 256, 60, 0) == UNSUPPORTED    # K % 8
+    assert g(P, P, NUL, E4M3, BF16, 2, 10, 256, 64, 0) == UNSUPPORTED    # fp8 via bf16 entry
+    assert g(P, P, NUL, BF16, BF16, 2, 10, 256, 64, 1) == INVALID        # SwiGLU needs B2
+    assert g(P, P, P2, BF16, BF16, 2, 10, 256, 64, 0) == INVALID         # B2 without SwiGLU
+    assert g(P, P, NUL, BF16, BF16, 2, 10, 256, 64, 7) == INVALID        # bad epilogue
+    assert g(MIS, P, NUL, BF16, BF16, 2, 10, 256, 64, 0) == INVALID
+    assert g(P, P, NUL, BF16, BF16, 2, 0, 256, 64, 0) == OK              # no rows: no-op
+
+
+def test_gemm_fp8_validation(lib):
+    f = lambda N, K, cdt, cs, b2, b2s, epi: lib.moe_grouped_gemm_fp8(  # noqa: E731
+        P, P, P, P, b2, b2s, P, cdt, cs, P, 2, 10, N, K, epi, NUL)
+    assert f(200, 256, BF16, NUL, NUL, NUL, 0) == UNSUPPORTED   # N % 128
+    assert f(256, 200, BF16, NUL, NUL, NUL, 0) == UNSUPPORTED   # K % 128
+    assert f(256, 256, F32, NUL, NUL, NUL, 0) == UNSUPPORTED    # output dtype
+    assert f(256, 256, E4M3, NUL, NUL, NUL, 0) == INVALID       # fp8 output needs scales
+    assert f(256, 256, BF16, P, NUL, NUL, 0) == INVALID         # scales only for fp8 output
+    assert f(256, 256, BF16, NUL, NUL, NUL, 1) == INVALID       # SwiGLU needs B2
+    assert f(256, 256, BF16, NUL, P, P, 0) == INVALID           # B2 without SwiGLU
+
+
+def test_combine_and_quant_validation(lib):
+    c = lambda T, k, d, ns, ydt, odt: lib.moe_combine(  # noqa: E731
+        P, ydt, P, P, T, k, d, ns, P, odt, NUL)
+    assert c(16, 0, 64, 0, BF16, BF16) == INVALID
+    assert c(16, 2, 60, 0, BF16, BF16) == UNSUPPORTED
+    assert c(16, 2, 64, 0, E4M3, BF16) == UNSUPPORTED
+    assert c(16, 40, 64, 0, BF16, BF16) == UNSUPPORTED
+    assert c(0, 2, 64, 0, BF16, BF16) == OK
+    q = lambda R, Cn, br, bc, dt: lib.moe_quantize_fp8(P, dt, R, Cn, br, bc, P, P, NUL)  # noqa: E731
+    assert q(256, 256, 64, 128, F32) == UNSUPPORTED
+    assert q(256, 256, 128, 64, F32) == UNSUPPORTED
+    assert q(200, 256, 128, 128, F32) == UNSUPPORTED
+    assert q(256, 200, 1, 128, F32) == UNSUPPORTED
+    assert q(256, 256, 128, 128, E4M3) == UNSUPPORTED
+    assert q(0, 256, 128, 128, F32) == OK

@@ -1,0 +1,172 @@
+"""GPU parity of the FP8 entry points against the oracle.
+
+* moe_quantize_fp8: codes and scales bit-exact (128 x 128 and 1 x 128
+  blocks), including blocks whose absmax is 448 (scale exactly 1), so every
+  E4M3 code point and rounding midpoint goes through the device rounding.
+* moe_grouped_gemm_fp8 against the oracle's fp64 product of the dequantised
+  operands, elementwise within a bound derived from the arithmetic: products
+  of E4M3 values are exact in fp32; each 128-deep block sum and the fp32
+  scale fold give at most (128 + K/128 + 4) u sum |a_k b_k| (u = 2^-24);
+  SwiGLU propagates it (|silu'| <= 1.1); a bf16 store adds 2^-8 |y|.  E4M3
+  output: the scale is absmax / 448 of the GPU's own h, so it is within
+  (group max of the h bound) / 448 of the oracle's; each dequantised value is
+  within 2^-4 of |h| (RNE with 3 mantissa bits) plus half the subnormal
+  spacing s 2^-10, plus the h bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+from grouped_gemm_router_amd import synth
+from gpu_util import DEV, U32, abs_operand, assert_within, offsets_from_sizes, swiglu_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def api():
+    from grouped_gemm_router_amd import api as a
+    return a
+
+
+def gpu_quant(src: torch.Tensor, br: int):
+    a = api()
+    R, Cn = src.shape
+    q = torch.empty((R, Cn), dtype=torch.uint8, device=DEV)
+    s = torch.empty((R // br, Cn // 128), dtype=torch.float32, device=DEV)
+    a.moe_quantize_fp8(src, q, s, block_rows=br, block_cols=128)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def code_points_and_midpoints(orc):
+    vals = np.array([orc.e4m3_value(c) for c in range(127)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    below = np.nextafter(mids.astype(np.float32), np.float32(0))
+    above = np.nextafter(mids.astype(np.float32), np.float32(1e9))
+    pos = np.concatenate([vals, mids, below, above, [447.9, 448.0]]).astype(np.float32)
+    return np.concatenate([pos, -pos, [0.0, -0.0]]).astype(np.float32)
+
+
+@pytest.mark.parametrize("br", [1, 128])
+def test_quantize_every_code_point_and_midpoint(orc, br):
+    v = code_points_and_midpoints(orc)
+    n = len(v)
+    R = 128 if br == 128 else 8
+    Cn = 128 * ((n + 127) // 128 + 1)
+    M = np.zeros((R, Cn), dtype=np.float32)
+    flat = np.resize(v, R * (Cn - 128))
+    M[:, 128:] = flat.reshape(R, Cn - 128)
+    M[:, 128:][:, ::128] = 448.0        # every block's absmax is 448: scale exactly 1
+    M[:, :128] = 0.0                    # an all-zero block column
+    q, s = gpu_quant(torch.from_numpy(M).to(DEV), br)
+    rq, rs = orc.quant_blocks(M, br, 128)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(q, rq)
+    assert (s[:, 1:] == 1.0).all() and (s[:, 0] == 1.0).all()
+
+
+@pytest.mark.parametrize("br,dt", [(128, "f32"), (128, "bf16"), (1, "f32"), (1, "bf16")])
+def test_quantize_random_matches_oracle(orc, br, dt):
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    src = synth.randn((512, 768), 0.05, 61, DEV, tdt)
+    src[0:128, 0:128].mul_(1e-3)
+    q, s = gpu_quant(src, br)
+    rq, rs = orc.quant_blocks(src.float().cpu().numpy(), br, 128)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(q, rq)
+
+
+def make_fp8(sizes, N, K, seed, swiglu):
+    offs = offsets_from_sizes(sizes)
+    rows = int(offs[-1])
+    G = len(sizes)
+    Aq = synth.random_e4m3_codes((max(rows, 1), K), seed)[:rows].contiguous()
+    As = synth.random_scales((max(rows, 1), K // 128), seed + 1)[:rows].contiguous()
+    Bq = synth.random_e4m3_codes((G, N, K), seed + 2)
+    Bs = synth.random_scales((G, N // 128, K // 128), seed + 3)
+    if swiglu:
+        B2q = synth.random_e4m3_codes((G, N, K), seed + 4)
+        B2s = synth.random_scales((G, N // 128, K // 128), seed + 5)
+    else:
+        B2q = B2s = None
+    return offs, Aq, As, Bq, Bs, B2q, B2s
+
+
+def fp8_ref_and_bound(orc, Aq, As, Bq, Bs, B2q, B2s, offs, rows, swiglu, store_rel):
+    K = Aq.shape[1]
+    gam = (128 + K // 128 + 4) * U32
+    g = orc.gemm_fp8_rows(Aq, As, Bq, Bs, offs, rows)
+    eg = gam * orc.gemm_fp8_rows(abs_operand(Aq), As, abs_operand(Bq), Bs, offs, rows)
+    if not swiglu:
+        return g, eg + (2 * U32 + store_rel) * np.abs(g)
+    u = orc.gemm_fp8_rows(Aq, As, B2q, B2s, offs, rows)
+    eu = gam * orc.gemm_fp8_rows(abs_operand(Aq), As, abs_operand(B2q), B2s, offs, rows)
+    bound, h = swiglu_bound(g, u, eg, eu, store_rel)
+    return h, bound
+
+
+def to_dev(*ts):
+    return [None if t is None else t.to(DEV) for t in ts]
+
+
+@pytest.mark.parametrize("sizes", [[0, 1, 127, 128, 129, 300], [64], [5, 0, 200]])
+@pytest.mark.parametrize("N,K,swiglu", [(256, 128, False), (384, 256, False), (128, 384, True),
+                                        (256, 128, True)])
+def test_fp8_gemm_bf16_out(orc, sizes, N, K, swiglu):
+    offs, Aq, As, Bq, Bs, B2q, B2s = make_fp8(sizes, N, K, 70 + N + K, swiglu)
+    a = api()
+    rows = int(offs[-1])
+    dAq, dAs, dBq, dBs, dB2q, dB2s = to_dev(Aq, As, Bq, Bs, B2q, B2s)
+    C = torch.full((rows, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    a.moe_grouped_gemm_fp8(dAq, dAs, dBq, dBs, C, torch.from_numpy(offs).to(DEV), B2_q=dB2q,
+                           B2_scale=dB2s, epi=a.MOE_EPI_SWIGLU if swiglu else a.MOE_EPI_NONE)
+    torch.cuda.synchronize()
+    ref, bound = fp8_ref_and_bound(orc, Aq.numpy(), As.numpy(), Bq.numpy(), Bs.numpy(),
+                                   None if B2q is None else B2q.numpy(),
+                                   None if B2s is None else B2s.numpy(), offs, np.arange(rows),
+                                   swiglu, 2.0 ** -8)
+    assert_within(C.float().cpu().numpy(), ref, bound)
+
+
+@pytest.mark.parametrize("sizes", [[0, 3, 129, 256], [40]])
+@pytest.mark.parametrize("N,K", [(256, 256), (128, 128)])
+def test_fp8_gemm_e4m3_out_swiglu(orc, sizes, N, K):
+    offs, Aq, As, Bq, Bs, B2q, B2s = make_fp8(sizes, N, K, 90 + N, True)
+    a = api()
+    rows = int(offs[-1])
+    dAq, dAs, dBq, dBs, dB2q, dB2s = to_dev(Aq, As, Bq, Bs, B2q, B2s)
+    C = torch.zeros((rows, N), dtype=torch.uint8, device=DEV)
+    Cs = torch.zeros((rows, N // 128), dtype=torch.float32, device=DEV)
+    a.moe_grouped_gemm_fp8(dAq, dAs, dBq, dBs, C, torch.from_numpy(offs).to(DEV), B2_q=dB2q,
+                           B2_scale=dB2s, C_scale=Cs, epi=a.MOE_EPI_SWIGLU)
+    torch.cuda.synchronize()
+    h, hb = fp8_ref_and_bound(orc, Aq.numpy(), As.numpy(), Bq.numpy(), Bs.numpy(), B2q.numpy(),
+                              B2s.numpy(), offs, np.arange(rows), True, 0.0)
+    check_e4m3_output(orc, C.cpu().numpy(), Cs.cpu().numpy(), h, hb)
+
+
+def check_e4m3_output(orc, gq, gs, h, hb):
+    rows, N = h.shape
+    G = N // 128
+    amax = np.abs(h).reshape(rows, G, 128).max(axis=2)
+    amax_b = hb.reshape(rows, G, 128).max(axis=2)
+    s_ref = amax / 448.0
+    assert (np.abs(gs - s_ref) <= amax_b / 448.0 + 4 * U32 * s_ref + 1e-30).all(), "scales"
+    s_full = np.repeat(gs.astype(np.float64), 128, axis=1)
+    deq = orc.e4m3_decode(gq) * s_full
+    bound = hb + 2.0 ** -4 * (np.abs(h) + hb) + s_full * 2.0 ** -10
+    assert_within(deq, h, bound, "dequantised E4M3 output")
+
+
+def test_fp8_gemm_e4m3_out_plain(orc):
+    offs, Aq, As, Bq, Bs, _, _ = make_fp8([100, 0, 60], 256, 256, 3, False)
+    a = api()
+    rows = int(offs[-1])
+    dAq, dAs, dBq, dBs = to_dev(Aq, As, Bq, Bs)
+    C = torch.zeros((rows, 256), dtype=torch.uint8, device=DEV)
+    Cs = torch.zeros((rows, 2), dtype=torch.float32, device=DEV)
+    a.moe_grouped_gemm_fp8(dAq, dAs, dBq, dBs, C, torch.from_numpy(offs).to(DEV), C_scale=Cs)
+    torch.cuda.synchronize()
+    c, cb = fp8_ref_and_bound(orc, Aq.numpy(), As.numpy(), Bq.numpy(), Bs.numpy(), None, None,
+                              offs, np.arange(rows), False, 0.0)
+    check_e4m3_output(orc, C.cpu().numpy(), Cs.cpu().numpy(), c, cb)

@@ -1,0 +1,153 @@
+"""GPU parity of moe_grouped_gemm (bf16 MFMA path and the fp32 / off-grid
+vector path) against the oracle's fp64 grouped GEMM.
+
+Tolerance, elementwise, derived from the arithmetic: fp32 accumulation of K
+exact products errs by at most (K + 2) u sum_k |a_k b_k| (u = 2^-24); the
+SwiGLU epilogue propagates that through silu(g) u (|silu'| <= 1.1) plus a few
+fp32 roundings; storing to bf16 adds at most 2^-8 |y| (fp32: u |y|).
+
+Small cases compare every row; the full Mixtral-shape gate/up and down GEMMs
+(in the launch configuration the benchmark times) compare sampled rows from
+every group.
+"""
+import numpy as np
+import pytest
+import torch
+
+from grouped_gemm_router_amd import synth
+from gpu_util import (DEV, U32, abs_operand, assert_within, np_of, offsets_from_sizes,
+                      sample_rows, swiglu_bound)
+
+pytestmark = pytest.mark.gpu
+
+
+def api():
+    from grouped_gemm_router_amd import api as a
+    return a
+
+
+def make(sizes, N, K, dt, seed, swiglu):
+    offs = offsets_from_sizes(sizes)
+    rows = int(offs[-1])
+    G = len(sizes)
+    A = synth.randn((max(rows, 1), K), 1.0, seed, DEV, dt)[:rows]
+    B = synth.randn((G, N, K), 1.0 / np.sqrt(K), seed + 1, DEV, dt)
+    B2 = synth.randn((G, N, K), 1.0 / np.sqrt(K), seed + 2, DEV, dt) if swiglu else None
+    return A.contiguous(), B, B2, offs
+
+
+def ref_and_bound(orc, An, Bn, B2n, offs, rows, swiglu, store_rel):
+    K = An.shape[1]
+    g = orc.gemm_rows(An, Bn, offs, rows)
+    eg = (K + 2) * U32 * orc.gemm_rows(abs_operand(An), abs_operand(Bn), offs, rows)
+    if not swiglu:
+        return g, eg + (2 * U32 + store_rel) * np.abs(g)
+    u = orc.gemm_rows(An, B2n, offs, rows)
+    eu = (K + 2) * U32 * orc.gemm_rows(abs_operand(An), abs_operand(B2n), offs, rows)
+    bound, h = swiglu_bound(g, u, eg, eu, store_rel)
+    return h, bound
+
+
+def gpu_gemm(A, B, B2, offs, out_dtype, swiglu):
+    a = api()
+    rows = A.shape[0]
+    N = B.shape[1]
+    C = torch.full((rows, N), float("nan"), dtype=out_dtype, device=DEV)
+    a.moe_grouped_gemm(A, B, C, torch.from_numpy(offs).to(DEV), B2=B2,
+                       epi=a.MOE_EPI_SWIGLU if swiglu else a.MOE_EPI_NONE)
+    torch.cuda.synchronize()
+    return C
+
+
+SIZES = [
+    [0, 1, 127, 129, 255, 256, 257, 600],
+    [1000],
+    [3, 0, 0, 5],
+    [256, 256],
+]
+
+
+@pytest.mark.parametrize("sizes", SIZES)
+@pytest.mark.parametrize("N,K,swiglu", [(256, 64, False), (512, 192, False), (128, 256, True),
+                                        (384, 128, True)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_bf16_mfma_all_rows(orc, sizes, N, K, swiglu, out):
+    A, B, B2, offs = make(sizes, N, K, torch.bfloat16, 100 + N + K, swiglu)
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    C = gpu_gemm(A, B, B2, offs, odt, swiglu)
+    ref, bound = ref_and_bound(orc, np_of(A), np_of(B), None if B2 is None else np_of(B2), offs,
+                               np.arange(A.shape[0]), swiglu, 2.0 ** -8 if out == "bf16" else U32)
+    assert_within(C.float().cpu().numpy(), ref, bound)
+
+
+@pytest.mark.parametrize("sizes", [[0, 5, 64, 65, 1], [200]])
+@pytest.mark.parametrize("N,K,swiglu", [(256, 128, True), (128, 256, False), (100, 40, False),
+                                        (72, 24, True)])
+def test_fp32_vector_path(orc, sizes, N, K, swiglu):
+    A, B, B2, offs = make(sizes, N, K, torch.float32, 200 + N, swiglu)
+    C = gpu_gemm(A, B, B2, offs, torch.float32, swiglu)
+    ref, bound = ref_and_bound(orc, np_of(A), np_of(B), None if B2 is None else np_of(B2), offs,
+                               np.arange(A.shape[0]), swiglu, U32)
+    assert_within(C.cpu().numpy(), ref, bound)
+
+
+def test_bf16_off_grid_shape_uses_vector_path(orc):
+    A, B, B2, offs = make([7, 70], 200, 40, torch.bfloat16, 7, False)
+    C = gpu_gemm(A, B, B2, offs, torch.bfloat16, False)
+    ref, bound = ref_and_bound(orc, np_of(A), np_of(B), None, offs, np.arange(A.shape[0]), False,
+                               2.0 ** -8)
+    assert_within(C.float().cpu().numpy(), ref, bound)
+
+
+def test_rows_outside_groups_untouched():
+    A, B, B2, offs = make([10, 20], 256, 64, torch.bfloat16, 9, False)
+    a = api()
+    C = torch.full((A.shape[0], 256), 7.0, dtype=torch.bfloat16, device=DEV)
+    offs2 = offs.copy()
+    offs2[-1] = 25   # last group shortened: rows 25..29 belong to no group
+    a.moe_grouped_gemm(A, B, C, torch.from_numpy(offs2).to(DEV))
+    torch.cuda.synchronize()
+    assert (C[25:].float() == 7.0).all()
+
+
+def _sampled_check(orc, A, B, B2, offs, C, swiglu, per_group=4):
+    rows = sample_rows(offs, per_group=per_group, seed=1)
+    An = np_of(A[torch.from_numpy(rows).to(DEV)])
+    got = C[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    ref = np.empty_like(got, dtype=np.float64)
+    bound = np.empty_like(got, dtype=np.float64)
+    groups = np.searchsorted(offs, rows, side="right") - 1
+    for g in np.unique(groups):
+        sel = np.where(groups == g)[0]
+        Bg = np_of(B[g:g + 1])
+        B2g = np_of(B2[g:g + 1]) if swiglu else None
+        ref[sel], bound[sel] = ref_and_bound(orc, An[sel], Bg, B2g,
+                                             np.array([0, len(sel)], np.int32),
+                                             np.arange(len(sel)), swiglu, 2.0 ** -8)
+    assert_within(got, ref, bound)
+
+
+def mixtral_sizes():
+    idx = synth.random_selection(4096, 8, 2, s=77).numpy()
+    return np.bincount(idx.ravel(), minlength=8)
+
+
+def test_mixtral_gate_up_full_size_sampled(orc):
+    sizes = mixtral_sizes()
+    A, B, B2, offs = make(sizes, 14336, 4096, torch.bfloat16, 300, True)
+    C = gpu_gemm(A, B, B2, offs, torch.bfloat16, True)
+    _sampled_check(orc, A, B, B2, offs, C, True, per_group=2)
+
+
+def test_mixtral_down_full_size_sampled(orc):
+    sizes = mixtral_sizes()
+    A, B, _, offs = make(sizes, 4096, 14336, torch.bfloat16, 400, False)
+    C = gpu_gemm(A, B, None, offs, torch.bfloat16, False)
+    _sampled_check(orc, A, B, None, offs, C, False, per_group=2)
+
+
+def test_gemm_is_deterministic():
+    A, B, B2, offs = make([300, 700, 0, 1024], 1024, 512, torch.bfloat16, 5, True)
+    c1 = gpu_gemm(A, B, B2, offs, torch.bfloat16, True)
+    c2 = gpu_gemm(A, B, B2, offs, torch.bfloat16, True)
+    assert torch.equal(c1, c2)

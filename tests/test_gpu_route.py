@@ -1,0 +1,137 @@
+"""GPU parity of moe_route against the oracle.
+
+* From given fp32 logits (MOE_ROUTE_FROM_LOGITS): indices bit-exact, weights
+  within 1e-6, for random logits and logits full of exact ties.
+* Full scoring: logits within the fp32 accumulation bound of the oracle's
+  fp64 logits (d u sum |x w|, u = 2^-24).  Selection: a token whose oracle
+  ordering of its top k + 1 logits has every gap wider than twice the
+  largest deviation of that token's GPU logits from the exact ones has one
+  correct answer, which must be matched exactly; otherwise several answers
+  are correct and the GPU's must be one of them (each selected logit within
+  twice that deviation of the oracle's j-th largest).
+"""
+import numpy as np
+import pytest
+import torch
+
+from grouped_gemm_router_amd import synth
+from gpu_util import DEV, np_of
+
+pytestmark = pytest.mark.gpu
+
+
+def api():
+    from grouped_gemm_router_amd import api as a
+    return a
+
+
+def run_from_logits(lg: np.ndarray, k: int, renorm=False):
+    a = api()
+    T, E = lg.shape
+    logits = torch.from_numpy(lg).to(DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    flags = a.MOE_ROUTE_FROM_LOGITS | (a.MOE_ROUTE_RENORM if renorm else 0)
+    a.moe_route(None, None, idx, w, logits=logits, flags=flags)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (37, 8, 2), (300, 8, 2), (129, 256, 8),
+                                   (64, 32, 32), (50, 1000, 32), (33, 65, 3)])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_from_logits_random(orc, T, E, k, renorm):
+    rng = np.random.default_rng(T * 1000 + E + k)
+    lg = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    idx, w = run_from_logits(lg, k, renorm)
+    ridx, rw = orc.topk(lg, k, renorm)
+    np.testing.assert_array_equal(idx, ridx)
+    np.testing.assert_allclose(w, rw, atol=1e-6, rtol=0)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (256, 8), (16, 16), (70, 5)])
+def test_from_logits_exact_ties(orc, E, k):
+    rng = np.random.default_rng(E + k)
+    pool = np.array([-2.0, -0.0, 0.0, 0.5, 0.5, 1.25], dtype=np.float32)
+    lg = rng.choice(pool, size=(200, E)).astype(np.float32)
+    lg[0, :] = 0.0
+    lg[1, :] = -0.0
+    lg[2, ::2] = -0.0
+    idx, w = run_from_logits(lg, k)
+    ridx, rw = orc.topk(lg, k)
+    np.testing.assert_array_equal(idx, ridx)
+    np.testing.assert_allclose(w, rw, atol=1e-6, rtol=0)
+
+
+def check_selection(idx, lg_ref, bound, k):
+    """idx (GPU) against the oracle's fp64 logits with per-token error bound."""
+    T, E = lg_ref.shape
+    l32 = lg_ref.astype(np.float32).astype(np.float64)
+    n_ambig = 0
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -l32[t]))
+        top = order[: min(k + 1, E)]
+        gaps = np.abs(np.diff(l32[t, top]))
+        sel = idx[t]
+        assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < E
+        if gaps.size == 0 or gaps.min() > 2 * bound[t] + 1e-7:
+            np.testing.assert_array_equal(sel, order[:k], err_msg="token %d" % t)
+        else:
+            n_ambig += 1
+            np.testing.assert_allclose(lg_ref[t, sel], lg_ref[t, order[:k]],
+                                       atol=2 * bound[t] + 1e-6)
+    return n_ambig
+
+
+@pytest.mark.parametrize("dt,T,d,E,k,bias", [
+    ("f32", 256, 128, 8, 2, False),
+    ("bf16", 300, 4096, 8, 2, False),
+    ("bf16", 200, 4096, 8, 2, True),
+    ("bf16", 96, 7168, 256, 8, False),
+    ("bf16", 40, 256, 1000, 4, False),
+    ("bf16", 17, 64, 3, 3, False),
+])
+def test_scoring_and_selection(orc, dt, T, d, E, k, bias):
+    a = api()
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    x = synth.randn((T, d), 1.0, 11 + T, DEV, tdt)
+    wr = synth.randn((E, d), 0.02 if d >= 1024 else 0.3, 12 + E, DEV, tdt)
+    b = synth.randn((E,), 0.5, 13, DEV) if bias else None
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    a.moe_route(x, wr, idx, w, logits=logits, logit_bias=b)
+    torch.cuda.synchronize()
+    lg_ref, absdot = orc.router_logits(np_of(x), np_of(wr), None if b is None else np_of(b))
+    got = logits.cpu().numpy().astype(np.float64)
+    # fp32 accumulation of exact products: |err| <= d * 2^-24 * sum|x w| (+ bias rounding)
+    bound_el = d * 2.0 ** -24 * absdot + 1e-6 * np.abs(lg_ref)
+    assert (np.abs(got - lg_ref) <= bound_el + 1e-7).all()
+    dev_max = np.abs(got - lg_ref).max(axis=1)
+    bound = bound_el.max(axis=1)
+    gi = idx.cpu().numpy()
+    n_ambig = check_selection(gi, lg_ref, dev_max, k)
+    assert n_ambig <= max(2, T // 50)
+    # weights: softmax of the oracle logits at the GPU's selection
+    l64 = lg_ref.astype(np.float32).astype(np.float64)
+    p = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    ref_w = np.take_along_axis(p, gi.astype(np.int64), axis=1)
+    tol = 1e-6 + 4 * bound[:, None] * ref_w
+    assert (np.abs(w.cpu().numpy() - ref_w) <= tol).all()
+
+
+def test_route_is_deterministic():
+    a = api()
+    T, d, E, k = 512, 7168, 256, 8
+    x = synth.randn((T, d), 1.0, 5, DEV, torch.bfloat16)
+    wr = synth.randn((E, d), 0.02, 6, DEV, torch.bfloat16)
+    outs = []
+    for _ in range(2):
+        lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
+        idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+        a.moe_route(x, wr, idx, w, logits=lg)
+        outs.append((lg.cpu(), idx.cpu(), w.cpu()))
+    for u, v in zip(*outs):
+        assert torch.equal(u, v)
