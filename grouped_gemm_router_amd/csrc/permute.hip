@@ -15,8 +15,9 @@
 //               Ranks are parked in flat_to_row, counts in the workspace.
 //   2. scan     one workgroup: per expert, exclusive prefix over blocks
 //               (in place), then the exclusive prefix over experts ->
-//               offsets; block bases become absolute rows.
-//   3. scatter  rows = block base + rank -> perm_src / flat_to_row; then the
+//               offsets.
+//   3. scatter  row = offsets[e] + block prefix + rank -> perm_src /
+//               flat_to_row; then the
 //               row copy: every source row is read once and stored to its k
 //               destinations (plus the shared-expert rows), in 16-byte
 //               pieces; with E4M3 output each 1 x 128 group is quantised
@@ -65,20 +66,27 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t *__restric
 }
 
 // ---- 2. scan ---------------------------------------------------------------
+// Thread e walks its expert's column of block counts 16 blocks at a time (the
+// 16 loads are independent, so they are in flight together) and leaves the
+// exclusive prefix over blocks in place; the exclusive prefix over experts
+// becomes offsets.  The scatter adds the two.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_shared, int nblk,
                                                          int32_t *__restrict__ blk,
                                                          int32_t *__restrict__ counts,
                                                          int32_t *__restrict__ offsets) {
   __shared__ int s_wave[16];
-  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-  // per expert: exclusive prefix over blocks, in place
   int total = 0;
   if (tid < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk[(size_t)b * E + tid];
-      blk[(size_t)b * E + tid] = total;
-      total += c;
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = (b0 + i < nblk) ? blk[(size_t)(b0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (b0 + i < nblk) blk[(size_t)(b0 + i) * E + tid] = total;
+        total += c[i];
+      }
     }
     counts[tid] = total;
   }
@@ -94,19 +102,11 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_sha
   int base = 0;
   for (int w = 0; w < wv; ++w) base += s_wave[w];
   const int excl = base + incl - total;
-  if (tid < E) {
-    s_off[tid] = excl;
-    offsets[tid] = excl;
-  }
+  if (tid < E) offsets[tid] = excl;
   if (tid == E - 1) {
     const int routed = excl + total;
     offsets[E] = routed;
     for (int s = 0; s < n_shared; ++s) offsets[E + s + 1] = routed + (s + 1) * T;
-  }
-  __syncthreads();
-  if (tid < E) {
-    const int o = s_off[tid];
-    for (int b = 0; b < nblk; ++b) blk[(size_t)b * E + tid] += o;
   }
 }
 
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
     int row = -1;
     if (e >= 0 && e < E) {
       const int t = (int)(f / k);
-      row = blk_base[(size_t)(t / kBlk) * E + e] + flat_to_row[f];
+      row = offsets[e] + blk_base[(size_t)(t / kBlk) * E + e] + flat_to_row[f];
       perm_src[row] = (int32_t)f;
     }
     flat_to_row[f] = row;

@@ -68,10 +68,10 @@ SIZES = [
 
 
 @pytest.mark.parametrize("sizes", SIZES)
-@pytest.mark.parametrize("N,K,swiglu", [(256, 64, False), (512, 192, False), (128, 256, True),
-                                        (384, 128, True)])
+@pytest.mark.parametrize("N,K,swiglu", [(256, 128, False), (512, 384, False), (128, 256, True),
+                                        (384, 128, True), (256, 64, False), (128, 192, True)])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
-def test_bf16_mfma_all_rows(orc, sizes, N, K, swiglu, out):
+def test_bf16_all_rows(orc, sizes, N, K, swiglu, out):
     A, B, B2, offs = make(sizes, N, K, torch.bfloat16, 100 + N + K, swiglu)
     odt = torch.bfloat16 if out == "bf16" else torch.float32
     C = gpu_gemm(A, B, B2, offs, odt, swiglu)
