@@ -9,9 +9,10 @@
 // batched: N and K shared, M_i ragged; expert sizes stay on the GPU).
 //
 // Design (CDNA4, 64-wide waves):
-//   * output tile 256 x 256, K step 32, 4 or 8 waves in a 2 x (NW/2) grid;
-//     each wave owns 128 x (256/(NW/2)) = 4 x NB blocks of
-//     v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs for 4 waves);
+//   * output tile BM x 256 (BM = 256, or 128 when groups average fewer than
+//     ~192 rows, so small experts do not pay for a mostly empty tile), K
+//     step 32, 4 or 8 waves in a 2 x (NW/2) grid; each wave owns
+//     BM/2 x (256/(NW/2)) = MI x NB blocks of v_mfma_f32_32x32x16_bf16;
 //   * operand tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no
 //     staging registers) into a 4-stage LDS ring (4 x 32 KB), issued three
 //     steps ahead; each step waits only for its own stage (vmcnt) and meets
@@ -39,9 +40,10 @@ namespace {
 
 using namespace moe;
 
-constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int PIECES = BK / 8;       // 16-byte pieces per tile row
-constexpr int SLOTS = BM * PIECES;   // 16-byte slots per operand stage (16 KB)
+constexpr int BM_MAX = 256, BN = 256, BK = 32;
+constexpr int PIECES = BK / 8;             // 16-byte pieces per tile row
+constexpr int SLOTS_MAX = BM_MAX * PIECES; // 16-byte slots per A stage (16 KB at most)
+constexpr int SLOTS_B = BN * PIECES;       // 16-byte slots per B stage (16 KB)
 
 __device__ __forceinline__ int swz(int row, int p) { return p ^ ((row ^ (row >> 2)) & 3); }
 
@@ -70,19 +72,28 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int NB>
+// LDS-direct load: lane i's SZ bytes from g land at l + i * SZ
+template <int SZ>
+__device__ __forceinline__ void dma_to_lds(const uint16_t *g, u32x4 *l) {
+  if constexpr (SZ == 16)
+    __builtin_amdgcn_global_load_lds((const void *)g, (lds_void *)l, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((const void *)g, (lds_void *)l, 4, 0, 0);
+}
+
+template <int MI, int NB>
 struct Frag {
-  bf16x8 a[4];
+  bf16x8 a[MI];
   bf16x8 b[NB];
 };
 
-template <bool SWIGLU, int NB, int NWN>
-__device__ __forceinline__ void read_frag(Frag<NB> &f, const u32x4 *tA, const u32x4 *tB, int ks,
-                                          int wm, int wn, int fr, int fh) {
+template <bool SWIGLU, int MI, int NB, int NWN>
+__device__ __forceinline__ void read_frag(Frag<MI, NB> &f, const u32x4 *tA, const u32x4 *tB,
+                                          int ks, int wm, int wn, int fr, int fh) {
   const int pc = ks * 2 + fh;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int r = wm * 128 + mi * 32 + fr;
+  for (int mi = 0; mi < MI; ++mi) {
+    const int r = wm * (MI * 32) + mi * 32 + fr;
     f.a[mi] = __builtin_bit_cast(bf16x8, tA[r * PIECES + swz(r, pc)]);
   }
 #pragma unroll
@@ -92,10 +103,10 @@ __device__ __forceinline__ void read_frag(Frag<NB> &f, const u32x4 *tA, const u3
   }
 }
 
-template <int NB>
-__device__ __forceinline__ void mfma_frag(f32x16 (&acc)[4][NB], const Frag<NB> &f) {
+template <int MI, int NB>
+__device__ __forceinline__ void mfma_frag(f32x16 (&acc)[MI][NB], const Frag<MI, NB> &f) {
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[nb], acc[mi][nb], 0, 0, 0);
@@ -112,43 +123,60 @@ __device__ __forceinline__ void interleave_mfma_ds_read() {
   __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
 }
 
-template <bool SWIGLU, bool OUT_F32, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
-    const uint16_t *__restrict__ B2, void *__restrict__ C, const int32_t *__restrict__ offsets,
-    int G, int rows, int N, int K, int nt_count) {
-  __shared__ u32x4 sA0[SLOTS], sA1[SLOTS], sA2[SLOTS], sA3[SLOTS];
-  __shared__ u32x4 sB0[SLOTS], sB1[SLOTS], sB2[SLOTS], sB3[SLOTS];
-  __shared__ int s_cum[MOE_MAX_GROUPS + 1];
-  __shared__ int s_tmp[NW];
-  constexpr int NTH = NW * 64;
+// One output tile of height BM (rows [tile.m0, tile.mend), at most BM of
+// them) over the whole K range, through the 4-stage LDS ring.
+template <int BM, bool SWIGLU, bool OUT_F32, int NW>
+__device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__restrict__ A,
+                                         const uint16_t *__restrict__ B,
+                                         const uint16_t *__restrict__ B2, void *__restrict__ C,
+                                         int rows, int N, int K, u32x4 *sA0, u32x4 *sA1,
+                                         u32x4 *sA2, u32x4 *sA3, u32x4 *sB0, u32x4 *sB1,
+                                         u32x4 *sB2, u32x4 *sB3) {
   constexpr int NWN = NW / 2;                 // wave columns (2 wave rows)
+  constexpr int MI = BM / 64;                 // 32-row blocks per wave
   constexpr int NB = (BN / NWN) / 32;         // 32-column blocks per wave
-  constexpr int INSTR = SLOTS / NW / 64;      // DMA instructions per operand per stage
-  constexpr int NM = 4 * NB;                  // MFMAs per 16-deep step
-  constexpr int NR = 4 + NB;                  // fragment reads per 16-deep step
-
-  sched_build<NTH>(offsets, G, rows, BM, s_cum, s_tmp);
-  const int total = s_cum[G] * nt_count;
-  const int L = xcd_remap(blockIdx.x, total);
-  if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM, nt_count, 8);
+  constexpr int SLOTS_A = BM * PIECES;        // 16-byte slots per A stage
+  // A stage smaller than one 16-byte load per lane (64-row tile, 8 waves):
+  // load it 4 bytes per lane instead, so every wave issues the same count
+  constexpr bool A_DW = SLOTS_A < NW * 64;
+  constexpr int IA = A_DW ? (SLOTS_A * 4) / NW / 64 : SLOTS_A / NW / 64;
+  constexpr int IB = SLOTS_B / NW / 64;       // B DMA instructions per wave per stage
+  constexpr int PER_STAGE = IA + IB;          // vmcnt units per stage
+  constexpr int NM = MI * NB;                 // MFMAs per 16-deep step
+  constexpr int NR = MI + NB;                 // fragment reads per 16-deep step
+  static_assert(IA >= 1 && IB >= 1, "tile too small for the wave count");
 
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
   const int wm = wv / NWN, wn = wv % NWN;
 
-  // DMA sources: wave wv fills slots [wv*SLOTS/NW, +SLOTS/NW) of each stage,
-  // 64 slots per instruction; slot s holds piece swz(row, s % 4) of row s / 4
-  const uint16_t *ga[INSTR];
-  const uint16_t *gb[INSTR];
+  // DMA sources.  16-byte mode: wave wv fills slots [wv*SLOTS/NW, +SLOTS/NW)
+  // of each operand stage, 64 slots per instruction; slot s holds piece
+  // swz(row, s % 4) of row s / 4.  4-byte mode (A only): instruction i of
+  // wave wv fills dwords [(wv*IA + i)*64, +64), dword q belonging to slot q/4.
+  const uint16_t *ga[IA];
+  const uint16_t *gb[IB];
   const size_t goff = (size_t)tile.g * N * K;
 #pragma unroll
-  for (int i = 0; i < INSTR; ++i) {
-    const int s = wv * (SLOTS / NW) + i * 64 + lane;
-    const int r = s / PIECES;
-    const int p = swz(r, s % PIECES);
+  for (int i = 0; i < IA; ++i) {
+    int r, off;
+    if (A_DW) {
+      const int q = (wv * IA + i) * 64 + lane;
+      const int sl = q / 4;
+      r = sl / PIECES;
+      off = swz(r, sl % PIECES) * 8 + (q % 4) * 2;
+    } else {
+      const int sl = wv * (SLOTS_A / NW) + i * 64 + lane;
+      r = sl / PIECES;
+      off = swz(r, sl % PIECES) * 8;
+    }
     const int m = min(tile.m0 + r, rows - 1);
-    ga[i] = A + (size_t)m * K + p * 8;
+    ga[i] = A + (size_t)m * K + off;
+  }
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int sl = wv * (SLOTS_B / NW) + i * 64 + lane;
+    const int r = sl / PIECES;
+    const int p = swz(r, sl % PIECES);
     if (SWIGLU) {
       const int n = tile.nt * 128 + (r & 127);
       gb[i] = (r < 128 ? B : B2) + goff + (size_t)n * K + p * 8;
@@ -156,18 +184,20 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
       gb[i] = B + goff + (size_t)(tile.nt * 256 + r) * K + p * 8;
     }
   }
-  const int dma_base = wv * (SLOTS / NW);
+  // LDS destinations of lane 0, in 16-byte units
+  const int dma_a = A_DW ? wv * IA * 16 : wv * (SLOTS_A / NW);
+  constexpr int STEP_A = A_DW ? 16 : 64;
+  const int dma_b = wv * (SLOTS_B / NW);
 #define MOE_ISSUE(dA, dB, k0)                                                              \
-  _Pragma("unroll") for (int i = 0; i < INSTR; ++i) {                                     \
-    __builtin_amdgcn_global_load_lds((const void *)(ga[i] + (k0)),                        \
-                                     (lds_void *)((dA) + dma_base + i * 64), 16, 0, 0);   \
+  _Pragma("unroll") for (int i = 0; i < IA; ++i)                                          \
+    dma_to_lds<A_DW ? 4 : 16>(ga[i] + (k0), (dA) + dma_a + i * STEP_A);                  \
+  _Pragma("unroll") for (int i = 0; i < IB; ++i)                                          \
     __builtin_amdgcn_global_load_lds((const void *)(gb[i] + (k0)),                        \
-                                     (lds_void *)((dB) + dma_base + i * 64), 16, 0, 0);   \
-  }
+                                     (lds_void *)((dB) + dma_b + i * 64), 16, 0, 0);
 
-  f32x16 acc[4][NB];
+  f32x16 acc[MI][NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
   const int fr = lane & 31, fh = lane >> 5;
@@ -176,10 +206,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   MOE_ISSUE(sA0, sB0, 0);
   MOE_ISSUE(sA1, sB1, BK);
   MOE_ISSUE(sA2, sB2, 2 * BK);
-  wait_vmcnt<4 * INSTR>();  // stage 0 landed (stages 1, 2 may be in flight)
+  wait_vmcnt<2 * PER_STAGE>();  // stage 0 landed (stages 1, 2 may be in flight)
   stage_barrier();
-  Frag<NB> f0, f1;
-  read_frag<SWIGLU, NB, NWN>(f0, sA0, sB0, 0, wm, wn, fr, fh);
+  Frag<MI, NB> f0, f1;
+  read_frag<SWIGLU, MI, NB, NWN>(f0, sA0, sB0, 0, wm, wn, fr, fh);
 
   // One stage: second-half fragments of this stage are read under the
   // first-half MFMAs; then the barrier that makes stage s+1 visible (and
@@ -188,14 +218,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   // three stages re-load the final K step into buffers nobody reads, so the
   // wait count never changes.
 #define MOE_STAGE(tA, tB, nA, nB, dA, dB, s)                                               \
-  read_frag<SWIGLU, NB, NWN>(f1, tA, tB, 1, wm, wn, fr, fh);                                 \
-  mfma_frag<NB>(acc, f0);                                                                     \
+  read_frag<SWIGLU, MI, NB, NWN>(f1, tA, tB, 1, wm, wn, fr, fh);                             \
+  mfma_frag<MI, NB>(acc, f0);                                                                 \
   interleave_mfma_ds_read<NM, NR>();                                                          \
-  wait_vmcnt<2 * INSTR>();                                                                    \
+  wait_vmcnt<PER_STAGE>();                                                                    \
   stage_barrier();                                                                            \
   MOE_ISSUE(dA, dB, min((s) + 3, KT - 1) * BK);                                               \
-  read_frag<SWIGLU, NB, NWN>(f0, nA, nB, 0, wm, wn, fr, fh);                                 \
-  mfma_frag<NB>(acc, f1);                                                                     \
+  read_frag<SWIGLU, MI, NB, NWN>(f0, nA, nB, 0, wm, wn, fr, fh);                             \
+  mfma_frag<MI, NB>(acc, f1);                                                                 \
   interleave_mfma_ds_read<NM, NR>();
 
   for (int kt = 0; kt < KT; kt += 4) {
@@ -214,12 +244,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   if (SWIGLU) {
     constexpr int HB = NB / 2;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int nb = 0; nb < HB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = tile.m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
+          const int m = tile.m0 + wm * (MI * 32) + mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
           if (m < tile.mend) {
             const int n = tile.nt * 128 + wn * (128 / NWN) + nb * 32 + col;
             const float g = acc[mi][nb][r], u = acc[mi][nb + HB][r];
@@ -232,12 +262,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
         }
   } else {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = tile.m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
+          const int m = tile.m0 + wm * (MI * 32) + mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
           if (m < tile.mend) {
             const int n = tile.nt * 256 + wn * (256 / NWN) + nb * 32 + col;
             const float v = acc[mi][nb][r];
@@ -250,11 +280,44 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   }
 }
 
+// One launch over all groups.  Groups are cut into 256-row tiles; the
+// last, partial tile of a group runs with the smallest height in
+// {64, 128, 256} that holds its rows, chosen here from the device offsets,
+// so a group of 40 rows (or the 40-row tail of a 1064-row group) costs a
+// quarter of the matrix-core work and 5/8 of the operand traffic of a full
+// tile.
+template <bool SWIGLU, bool OUT_F32, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+    const uint16_t *__restrict__ B2, void *__restrict__ C, const int32_t *__restrict__ offsets,
+    int G, int rows, int N, int K, int nt_count) {
+  __shared__ u32x4 sA0[SLOTS_MAX], sA1[SLOTS_MAX], sA2[SLOTS_MAX], sA3[SLOTS_MAX];
+  __shared__ u32x4 sB0[SLOTS_B], sB1[SLOTS_B], sB2[SLOTS_B], sB3[SLOTS_B];
+  __shared__ int s_cum[MOE_MAX_GROUPS + 1];
+  __shared__ int s_tmp[NW];
+
+  sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_tmp);
+  const int total = s_cum[G] * nt_count;
+  const int L = xcd_remap(blockIdx.x, total);
+  if (L < 0) return;
+  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM_MAX, nt_count, 8);
+  const int h = tile.mend - tile.m0;  // wave-uniform
+  if (h > 128)
+    run_tile<256, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, sA0, sA1, sA2, sA3, sB0,
+                                       sB1, sB2, sB3);
+  else if (h > 64)
+    run_tile<128, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, sA0, sA1, sA2, sA3, sB0,
+                                       sB1, sB2, sB3);
+  else
+    run_tile<64, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, sA0, sA1, sA2, sA3, sB0,
+                                      sB1, sB2, sB3);
+}
+
 template <bool SWIGLU, bool OUT_F32, int NW>
 void launch_t(const void *A, const void *B, const void *B2, void *C, const int32_t *offsets,
               int G, int rows, int N, int K, hipStream_t s) {
   const int nt = SWIGLU ? N / 128 : N / 256;
-  const long long bound = (long long)host_row_tile_bound(rows, G, BM) * nt;
+  const long long bound = (long long)host_row_tile_bound(rows, G, BM_MAX) * nt;
   hipLaunchKernelGGL((gemm_bf16_kernel<SWIGLU, OUT_F32, NW>), dim3((unsigned)((bound + 7) / 8 * 8)),
                      dim3(NW * 64), 0, s, static_cast<const uint16_t *>(A),
                      static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(B2), C,
@@ -271,7 +334,7 @@ bool gemm_bf16_mfma_supports(int N, int K, int epi) {
 hipError_t launch_gemm_bf16_mfma(const void *A, const void *B, const void *B2, void *C, int c_dt,
                                  const int32_t *offsets, int G, int rows, int N, int K, int epi,
                                  hipStream_t s) {
-  // measured on the Mixtral shapes: 8 waves for gate/up, 4 for down
+  // wave counts measured on the Mixtral shapes: 8 for gate/up, 4 for down
   if (epi == MOE_EPI_SWIGLU) {
     if (c_dt == MOE_F32) launch_t<true, true, 8>(A, B, B2, C, offsets, G, rows, N, K, s);
     else launch_t<true, false, 8>(A, B, B2, C, offsets, G, rows, N, K, s);

@@ -59,11 +59,15 @@ def gpu_gemm(A, B, B2, offs, out_dtype, swiglu):
     return C
 
 
+# Group sizes chosen so that the last tile of a group takes each height the
+# kernel picks from its row count (64, 128 or 256 rows) on both sides of
+# every switch point: 64/65, 128/129, 256/257, 320 = 256 + 64, 384 = 256 + 128.
 SIZES = [
     [0, 1, 127, 129, 255, 256, 257, 600],
     [1000],
     [3, 0, 0, 5],
     [256, 256],
+    [64, 65, 128, 320, 384, 385, 63],
 ]
 
 
@@ -144,6 +148,27 @@ def test_mixtral_down_full_size_sampled(orc):
     A, B, _, offs = make(sizes, 4096, 14336, torch.bfloat16, 400, False)
     C = gpu_gemm(A, B, None, offs, torch.bfloat16, False)
     _sampled_check(orc, A, B, None, offs, C, False, per_group=2)
+
+
+def test_deepseek_shaped_groups_sampled(orc):
+    """257 groups of ~128 rows (256 routed experts at T=4096, k=8, plus a
+    4096-row shared group): most tiles are the 128- or 256-row kind; K as
+    the DeepSeek gate/up, N cut to 256 to keep the weights small."""
+    rng = np.random.default_rng(11)
+    sizes = np.concatenate([rng.integers(98, 166, 256), [4096]])
+    A, B, B2, offs = make(sizes, 256, 7168, torch.bfloat16, 500, True)
+    C = gpu_gemm(A, B, B2, offs, torch.bfloat16, True)
+    _sampled_check(orc, A, B, B2, offs, C, True, per_group=2)
+
+
+def test_decode_shaped_groups_all_rows(orc):
+    """Skewed decode: 256 rows over 8 experts, every tile 64 or 128 rows."""
+    sizes = [89, 55, 41, 27, 19, 12, 9, 4]
+    A, B, _, offs = make(sizes, 512, 1024, torch.bfloat16, 600, False)
+    C = gpu_gemm(A, B, None, offs, torch.bfloat16, False)
+    ref, bound = ref_and_bound(orc, np_of(A), np_of(B), None, offs, np.arange(A.shape[0]), False,
+                               2.0 ** -8)
+    assert_within(C.float().cpu().numpy(), ref, bound)
 
 
 def test_gemm_is_deterministic():
