@@ -19,9 +19,10 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH 
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_ROUTE_RENORM, MOE_ROUTE_FROM_LOGITS = 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
-EXPORTS = ["moe_status_string", "moe_abi_version", "moe_route", "moe_permute_workspace_size",
+EXPORTS = ["moe_status_string", "moe_abi_version", "moe_route_workspace_size", "moe_route",
+           "moe_permute_workspace_size",
            "moe_permute", "moe_grouped_gemm", "moe_grouped_gemm_fp8", "moe_combine",
            "moe_quantize_fp8"]
 
@@ -43,7 +44,9 @@ def _load():
     lib.moe_abi_version.restype = i32
     lib.moe_abi_version.argtypes = []
     lib.moe_route.restype = i32
-    lib.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp]
+    lib.moe_route_workspace_size.restype = sz
+    lib.moe_route_workspace_size.argtypes = [i32, i32, i32]
+    lib.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp, sz, vp]
     lib.moe_permute_workspace_size.restype = sz
     lib.moe_permute_workspace_size.argtypes = [i32, i32, i32]
     lib.moe_permute.restype = i32
@@ -106,22 +109,33 @@ def _stream(stream) -> C.c_void_p:
 # entry points (same names as the C ABI)
 # ----------------------------------------------------------------------------
 
-def moe_route(x, w_router, topk_idx, topk_w, *, logits=None, logit_bias=None, flags=0,
+def moe_route_workspace_size(T: int, d: int, E: int) -> int:
+    return int(lib.moe_route_workspace_size(T, d, E))
+
+
+def moe_route(x, w_router, topk_idx, topk_w, *, logits=None, logit_bias=None, flags=0, ws=None,
               stream=None):
     """Router scoring + top-k.  x [T][d], w_router [E][d] (fp32 or bf16);
     topk_idx [T][k] int32 and topk_w [T][k] fp32 are written; logits [T][E]
-    fp32 is written if given (read instead with MOE_ROUTE_FROM_LOGITS)."""
+    fp32 is written if given (read instead with MOE_ROUTE_FROM_LOGITS).
+    ws: device workspace of moe_route_workspace_size(T, d, E) bytes; when
+    None, one is allocated here for this call."""
     T, k = topk_idx.shape
     if flags & MOE_ROUTE_FROM_LOGITS:
         E = logits.shape[1]
         d, dt = 8, MOE_BF16
+        ws_bytes = 0
     else:
         d = x.shape[1]
         E = w_router.shape[0]
         dt = _dt(x)
+        if ws is None:
+            ws = torch.empty(moe_route_workspace_size(T, d, E), dtype=torch.uint8,
+                             device=topk_idx.device)
+        ws_bytes = ws.numel() * ws.element_size()
     _check("moe_route", lib.moe_route(_ptr(x), _ptr(w_router), dt, _ptr(logit_bias), T, d, E,
                                       k, flags, _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
-                                      _stream(stream)))
+                                      _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_permute_workspace_size(T: int, k: int, E: int) -> int:

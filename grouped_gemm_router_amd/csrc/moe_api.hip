@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -38,9 +38,15 @@ const char *moe_status_string(moe_status_t status) {
 
 int moe_abi_version(void) { return kAbiVersion; }
 
+size_t moe_route_workspace_size(int T, int d, int E) {
+  if (T < 0 || d < 1 || E < 1) return 0;
+  return route_ws_bytes(T, d, E);
+}
+
 moe_status_t moe_route(const void *x, const void *w_router, moe_dtype_t dt,
                        const float *logit_bias, int T, int d, int E, int k, unsigned flags,
-                       float *logits, int32_t *topk_idx, float *topk_w, moe_stream_t stream) {
+                       float *logits, int32_t *topk_idx, float *topk_w, void *ws,
+                       size_t ws_bytes, moe_stream_t stream) {
   if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (flags & ~(MOE_ROUTE_RENORM | MOE_ROUTE_FROM_LOGITS)) return MOE_ERR_INVALID;
@@ -53,10 +59,13 @@ moe_status_t moe_route(const void *x, const void *w_router, moe_dtype_t dt,
     if (d < 8 || d % 8 != 0) return MOE_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID;
     if (!opt_aligned4(logits) || !opt_aligned4(logit_bias)) return MOE_ERR_INVALID;
+    const size_t need = route_ws_bytes(T, d, E);
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (need > 0 && !aligned4(ws)) return MOE_ERR_INVALID;
   }
   if (T == 0) return MOE_OK;
   return launched(launch_route(x, w_router, dt, logit_bias, T, d, E, k, flags, logits, topk_idx,
-                               topk_w, as_stream(stream)));
+                               topk_w, static_cast<float *>(ws), as_stream(stream)));
 }
 
 size_t moe_permute_workspace_size(int T, int k, int E) {

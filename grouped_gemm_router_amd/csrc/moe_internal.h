@@ -206,9 +206,10 @@ inline int host_row_tile_bound(int rows, int G, int BM) { return rows / BM + G; 
 // Arguments are validated by the C-ABI layer before these are called.
 // ---------------------------------------------------------------------------
 
+size_t route_ws_bytes(int T, int d, int E);
 hipError_t launch_route(const void *x, const void *w_router, int dt, const float *bias,
                         int T, int d, int E, int k, unsigned flags, float *logits,
-                        int32_t *topk_idx, float *topk_w, hipStream_t s);
+                        int32_t *topk_idx, float *topk_w, float *ws, hipStream_t s);
 
 size_t permute_ws_bytes(int T, int k, int E);
 hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *topk_idx,

@@ -75,7 +75,10 @@ class MoELayer:
         self.offsets = torch.empty((G + 1,), dtype=i32, device=dev)
         self.perm_src = torch.empty((T * k,), dtype=i32, device=dev)
         self.flat_to_row = torch.empty((T * k + ns * T,), dtype=i32, device=dev)
-        ws = api.moe_permute_workspace_size(T, k, E)
+        # route and permute run one after the other on one stream, so they
+        # share one workspace
+        ws = max(api.moe_permute_workspace_size(T, k, E),
+                 api.moe_route_workspace_size(T, self.d, E))
         self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
         if self.fp8:
             self.x_perm = torch.empty((rows, self.d), dtype=torch.uint8, device=dev)
@@ -98,7 +101,7 @@ class MoELayer:
         E, ns = self.E, self.n_shared
         s = [("route", lambda: api.moe_route(x, self.w_router, self.topk_idx, self.topk_w,
                                              logits=self.logits, logit_bias=self.bias,
-                                             flags=self.flags)),
+                                             flags=self.flags, ws=self.ws)),
              ("permute", lambda: api.moe_permute(x, self.topk_idx, E, ns, self.x_perm,
                                                  self.counts, self.offsets, self.perm_src,
                                                  self.flat_to_row, self.ws,

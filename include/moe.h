@@ -102,13 +102,21 @@ int moe_abi_version(void);
  * logit_bias [E] fp32 or NULL.  logits [T][E] fp32: written if non-NULL; with
  * MOE_ROUTE_FROM_LOGITS it is read instead (and must be non-NULL).
  * topk_idx [T][k] int32, topk_w [T][k] fp32 are written.
+ * ws (device, 4-byte aligned) holds the fp32 partial logits of the d-axis
+ * slices; it must hold moe_route_workspace_size(T, d, E) bytes (else
+ * MOE_ERR_WORKSPACE).  With MOE_ROUTE_FROM_LOGITS it is unused (may be NULL,
+ * ws_bytes 0).
  * Requires 1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS, d % 8 == 0.
  * Non-finite logits are a caller error (selection is then unspecified).
  */
 moe_status_t moe_route(const void *x, const void *w_router, moe_dtype_t dt,
                        const float *logit_bias, int T, int d, int E, int k,
                        unsigned flags, float *logits, int32_t *topk_idx,
-                       float *topk_w, moe_stream_t stream);
+                       float *topk_w, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Bytes of device workspace moe_route needs for these sizes (the router's
+ * split-K partial logits: at most a small multiple of T * E * 4). */
+size_t moe_route_workspace_size(int T, int d, int E);
 
 /* Bytes of device workspace moe_permute needs for these sizes. */
 size_t moe_permute_workspace_size(int T, int k, int E);

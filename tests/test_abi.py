@@ -29,7 +29,9 @@ def lib():
         build.build()
     L = C.CDLL(LIB)
     vp, i32, u32, sz = C.c_void_p, C.c_int, C.c_uint, C.c_size_t
-    L.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp]
+    L.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp, sz, vp]
+    L.moe_route_workspace_size.restype = sz
+    L.moe_route_workspace_size.argtypes = [i32, i32, i32]
     L.moe_permute_workspace_size.restype = sz
     L.moe_permute_workspace_size.argtypes = [i32, i32, i32]
     L.moe_permute.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
@@ -52,7 +54,7 @@ NUL = C.c_void_p(0)
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), "libmoe.so does not export %s" % n
 
@@ -60,11 +62,12 @@ def test_every_declared_function_is_exported(lib):
 def test_status_strings_and_version(lib):
     for s in range(5):
         assert lib.moe_status_string(s)
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_route_validation(lib):
-    r = lambda *a: lib.moe_route(*a)  # noqa: E731
+    big = 1 << 40
+    r = lambda *a: lib.moe_route(*a[:-1], P2, big, a[-1])  # noqa: E731  (ample workspace)
     # k > E, k < 1, E > max, d % 8, dtype, null outputs, misaligned x
     assert r(P, P, BF16, NUL, 16, 64, 4, 5, 0, NUL, P, P, NUL) == INVALID
     assert r(P, P, BF16, NUL, 16, 64, 4, 0, 0, NUL, P, P, NUL) == INVALID
@@ -77,6 +80,18 @@ def test_route_validation(lib):
     assert r(NUL, NUL, BF16, NUL, 16, 64, 8, 2, 2, NUL, P, P, NUL) == INVALID  # from-logits, no logits
     assert r(P, P, BF16, NUL, -1, 64, 8, 2, 0, NUL, P, P, NUL) == INVALID
     assert r(P, P, BF16, NUL, 0, 64, 8, 2, 0, NUL, P, P, NUL) == OK  # T == 0: no-op
+
+
+def test_route_workspace(lib):
+    need = lib.moe_route_workspace_size(4096, 7168, 256)
+    assert need >= 4096 * 256 * 4 and need % (4096 * 256 * 4) == 0
+    assert lib.moe_route_workspace_size(-1, 64, 8) == 0
+    args = (P, P, BF16, NUL, 4096, 7168, 256, 8, 0, NUL, P, P)
+    assert lib.moe_route(*args, P2, need - 1, NUL) == WORKSPACE
+    assert lib.moe_route(*args, NUL, 0, NUL) == WORKSPACE
+    assert lib.moe_route(*args, MIS, need, NUL) == INVALID
+    # from-logits needs no workspace; with T == 0 nothing is launched
+    assert lib.moe_route(NUL, NUL, BF16, NUL, 0, 8, 256, 8, 2, P, P, P, NUL, 0, NUL) == OK
 
 
 def test_permute_validation_and_workspace(lib):

@@ -90,6 +90,12 @@ def check_selection(idx, lg_ref, bound, k):
     ("bf16", 96, 7168, 256, 8, False),
     ("bf16", 40, 256, 1000, 4, False),
     ("bf16", 17, 64, 3, 3, False),
+    # column tail inside a K step (1000 = 15 x 64 + 40), expert tiles of
+    # 128 with a ragged last one, several d-slices
+    ("bf16", 130, 1000, 100, 6, True),
+    # 64-expert tiles, three token tiles with a ragged tail, d-slices of
+    # unequal step counts
+    ("bf16", 257, 2056, 48, 4, False),
 ])
 def test_scoring_and_selection(orc, dt, T, d, E, k, bias):
     a = api()
