@@ -19,7 +19,7 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH 
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_ROUTE_RENORM, MOE_ROUTE_FROM_LOGITS = 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTS = ["moe_status_string", "moe_abi_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size",

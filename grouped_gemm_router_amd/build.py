@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_fp8.hip",
+SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_fp8_ring.hip",
            "gemm_simple.hip", "combine.hip", "quant.hip"]
 
 ARCH = "gfx950"

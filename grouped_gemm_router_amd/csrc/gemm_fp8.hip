@@ -18,6 +18,7 @@
 //   * SwiGLU: B-tile rows 0..127 are 128 gate rows (one 128-row scale
 //     block) and rows 128..255 the matching up rows; wave column wn takes
 //     gate rows [64 wn, +64) and up rows [128 + 64 wn, +64);
+//   * activation and output scales are stored group-major, [K/128][rows];
 //   * E4M3 output: each output row's 128 h-columns of the tile are one
 //     1 x 128 quantisation group; absmax over 16 lanes, then over the two
 //     wave columns through LDS; s = absmax / 448; q = RNE(h / s).
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
   }
   // activation scale row handled by this thread (threads < 128)
   const int srow = min(tile.m0 + tid, rows - 1);
-  const float *psa = As + (size_t)srow * KB;
+  const float *psa = As + srow;  // [K/128][rows]
   // weight scales of this wave column: [g][n-block][kb]
   const float *psb;
   const float *psb2 = nullptr;
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
       for (int i = 0; i < A_LOADS; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(pa[i] + k0);
 #pragma unroll
       for (int i = 0; i < B_LOADS; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(pb[i] + k0);
-      if (tid < FBM) rs = psa[kb + 1];
+      if (tid < FBM) rs = psa[(size_t)(kb + 1) * rows];
     }
     const float sb = psb[kb];
     const float sb2 = SWIGLU ? psb2[kb] : sb;
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
             const int n = tile.nt * 128 + wn * 64 + nb * 16 + col;
             static_cast<uint8_t *>(C)[(size_t)m * N + n] = (uint8_t)f32_to_e4m3(h[mi][nb][i] / sc);
           }
-          if (wn == 0 && col == 0) Cs[(size_t)m * NB + tile.nt] = sc;
+          if (wn == 0 && col == 0) Cs[(size_t)tile.nt * rows + m] = sc;
         } else {
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) {
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
           else
             static_cast<uint16_t *>(C)[(size_t)m * N + n] = f32_to_bf16_bits(acc[mi][nb][i]);
         }
-        if (OUT_FP8 && col == 0) Cs[(size_t)m * NB + tile.nt * 2 + wn] = sc;
+        if (OUT_FP8 && col == 0) Cs[(size_t)(tile.nt * 2 + wn) * rows + m] = sc;
       }
   }
 }

@@ -1,0 +1,398 @@
+// gemm_fp8_ring.hip -- FP8 (E4M3) block-scaled grouped GEMM for gfx950,
+// operands streamed through a 4-stage LDS ring of LDS-direct loads.
+//
+// "DeepGEMM walkthrough" §2.3 (C ~ (A_q / scale_A)(B_q / scale_B); the
+// stored scales here are the dequantisation multipliers, the reciprocal of
+// the page's scale), §5.1 (scales per token group and per weight block woven
+// into the GEMM, fp32 accumulation), §4.3 (one launch over ragged groups),
+// §5.2 (multi-buffered loads), §5.3 (masked tails).
+//   C[r][n] = sum_kb sA[r][kb] * sB[g][n/128][kb] * (sum_{k in kb} Aq Bq)
+//
+// Design (CDNA4, 64-wide waves, 8 waves in a 2 x 4 grid):
+//   * a K step is 64 fp8 columns = 64 bytes per tile row, the same row size
+//     as the bf16 kernel's 32-column step, so the LDS ring, the 16-byte
+//     piece swizzle and the load issue are the same: tile rows move
+//     HBM/L2 -> LDS with global_load_lds_dwordx4, three steps ahead, each step
+//     waiting only for its own stage and meeting the other waves at a plain
+//     s_barrier;
+//   * one v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit E8M0 block
+//     scales) per 32 x 32 block and step; its result is the exact-scale
+//     partial sum of 64 products, folded into the fp32 accumulator with the
+//     fp32 factor sA * sB of its 128-column scale block (two steps share a
+//     block): the promotion to fp32 happens every 64 columns;
+//   * the weight tile is the MFMA's row operand and the token tile its column
+//     operand, so a lane holds one token: the fold needs one sA per lane and
+//     one sB per wave column (a scalar load), not one per accumulator row;
+//   * activation scales are stored group-major, [K/128][rows], so one
+//     block's scales for the tile rows are one contiguous run; they travel
+//     with every even step (the first of a 128-column block): one 4-byte
+//     LDS-direct load per wave (32 rows, each fetched by two lanes) into one
+//     of two LDS slots, read once per block.  Exactly one of any two
+//     consecutive steps carries it, so every step still waits for the same
+//     count;
+//   * tile heights 64 / 128 / 256 rows are chosen per tile from its row count,
+//     as in the bf16 kernel (a group's last tile shrinks to what it holds);
+//   * SwiGLU: the weight tile holds 128 gate rows then the 128 matching up
+//     rows; wave column wn takes gate rows [32 wn, +32) and up rows
+//     [128 + 32 wn, +32), so silu(gate) * up pairs in registers; E4M3 output
+//     quantises each row's 128 h columns of the tile as one 1 x 128 group
+//     (absmax over the lane pair, then over the four wave columns in LDS).
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr int BM_MAX = 256, BN = 256, BK = 64;  // BK: fp8 columns (= bytes) per step
+constexpr int PIECES = BK / 16;                 // 16-byte pieces per tile row (4)
+constexpr int SLOTS_MAX = BM_MAX * PIECES;      // 16-byte slots per A stage (16 KB at most)
+constexpr int SLOTS_B = BN * PIECES;            // 16-byte slots per B stage (16 KB)
+constexpr int NW = 8, NWN = 4;                  // waves, wave columns (2 wave rows)
+constexpr int NB = 2;                           // 32-row weight blocks per wave
+constexpr int NTH = NW * 64;
+constexpr int SROWS = NW * 64;                  // activation-scale slot (32 rows per wave, x2)
+
+__device__ __forceinline__ int swz(int row, int p) { return p ^ ((row ^ (row >> 2)) & 3); }
+
+// weight-tile row of wave column wn, 32-row block nb
+template <bool SWIGLU>
+__device__ __forceinline__ int b_row(int wn, int nb) {
+  return SWIGLU ? nb * 128 + wn * 32 : wn * 64 + nb * 32;
+}
+
+// s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// workgroup barrier without __syncthreads()'s release fence, which would
+// drain every LDS-direct load still in flight
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int SZ>
+__device__ __forceinline__ void dma_to_lds(const void *g, void *l) {
+  if constexpr (SZ == 16)
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 4, 0, 0);
+}
+
+// the 32 bytes (64 K columns split in two lane halves) of row r
+__device__ __forceinline__ i32x8 frag(const u32x4 *t, int r, int fh) {
+  const u32x4 lo = t[r * PIECES + swz(r, 2 * fh)];
+  const u32x4 hi = t[r * PIECES + swz(r, 2 * fh + 1)];
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+struct Ring {
+  u32x4 *a[4];
+  u32x4 *b[4];
+  float *sa[2];  // activation scales of a 128-column block, slot = block % 2
+  float *amax;  // [NWN][BM_MAX]
+};
+
+template <int BM, bool SWIGLU, bool OUT_FP8>
+__device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__restrict__ Aq,
+                                         const float *__restrict__ As,
+                                         const uint8_t *__restrict__ Bq,
+                                         const float *__restrict__ Bs,
+                                         const uint8_t *__restrict__ B2q,
+                                         const float *__restrict__ B2s, void *__restrict__ C,
+                                         float *__restrict__ Cs, int rows, int N, int K,
+                                         const Ring &ring) {
+  constexpr int MI = BM / 64;            // 32-token blocks per wave
+  constexpr int SLOTS_A = BM * PIECES;
+  constexpr bool A_DW = SLOTS_A < NW * 64;  // 64-row tile: 4-byte loads for A
+  constexpr int IA = A_DW ? (SLOTS_A * 4) / NW / 64 : SLOTS_A / NW / 64;
+  constexpr int IB = SLOTS_B / NW / 64;
+  constexpr int OPS = IA + IB;            // operand loads per wave and stage
+  static_assert(IA >= 1 && IB >= 1, "tile too small for the wave count");
+
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  const int wm = wv / NWN, wn = wv % NWN;
+  const int KB = K / 128, NBK = N / 128;  // scale blocks along K and N
+
+  // LDS-direct sources (see the bf16 kernel for the slot layout): a
+  // wave-uniform base (SGPRs) plus a 32-bit per-lane byte offset, which keeps
+  // the addresses to one VGPR each
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const int gu = __builtin_amdgcn_readfirstlane(tile.g);
+  const int ntu = __builtin_amdgcn_readfirstlane(tile.nt);
+  uint32_t ga[IA];
+  uint32_t gb[IB];
+#pragma unroll
+  for (int i = 0; i < IA; ++i) {
+    int r, off;
+    if (A_DW) {
+      const int q = (wv * IA + i) * 64 + lane;
+      const int sl = q / 4;
+      r = sl / PIECES;
+      off = swz(r, sl % PIECES) * 16 + (q % 4) * 4;
+    } else {
+      const int sl = wv * (SLOTS_A / NW) + i * 64 + lane;
+      r = sl / PIECES;
+      off = swz(r, sl % PIECES) * 16;
+    }
+    const int m = min(tile.m0 + r, rows - 1);
+    ga[i] = (uint32_t)m * (uint32_t)K + off;
+  }
+  // the B tile of wave wv comes from one matrix: SwiGLU waves 0-3 fill the
+  // 128 gate rows, waves 4-7 the 128 up rows
+  const uint8_t *bbase = ((SWIGLU && wvu >= NW / 2) ? B2q : Bq) + (size_t)gu * N * K;
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int sl = wv * (SLOTS_B / NW) + i * 64 + lane;
+    const int r = sl / PIECES;
+    const int p = swz(r, sl % PIECES);
+    const int n = SWIGLU ? ntu * 128 + (r & 127)
+                         : min(ntu * 256 + r, N - 1);  // N % 256 == 128: half tile
+    gb[i] = (uint32_t)n * (uint32_t)K + p * 16;
+  }
+  // activation scales [K/128][rows]: wave wv loads tile rows [32 wv, +32),
+  // each by lanes l and l + 32 (the second copy lands in an unused half);
+  // rows past the tile read a clamped row and are never used
+  const uint32_t gs = (uint32_t)min(tile.m0 + wv * 32 + (lane & 31), rows - 1) * 4u;
+  const int dma_a = A_DW ? wv * IA * 16 : wv * (SLOTS_A / NW);
+  constexpr int STEP_A = A_DW ? 16 : 64;
+  const int dma_b = wv * (SLOTS_B / NW);
+#define MOE_ISSUE(st, kt, SC, SLOT)                                                        \
+  _Pragma("unroll") for (int i = 0; i < IA; ++i)                                          \
+    dma_to_lds<A_DW ? 4 : 16>(Aq + (ga[i] + (kt) * BK), ring.a[st] + dma_a + i * STEP_A); \
+  _Pragma("unroll") for (int i = 0; i < IB; ++i)                                          \
+    dma_to_lds<16>(bbase + (gb[i] + (kt) * BK), ring.b[st] + dma_b + i * 64);             \
+  if (SC)                                                                                 \
+    dma_to_lds<4>(reinterpret_cast<const uint8_t *>(As + (size_t)((kt) / 2) * rows) + gs,  \
+                  ring.sa[SLOT] + wv * 64);
+
+  // weight scales of this wave's two 32-row blocks: [g][n-block][kb]; the
+  // indices are wave-uniform, so these are scalar loads
+  const int wnu = wvu % NWN;
+  const float *sb0, *sb1;
+  if (SWIGLU) {
+    sb0 = Bs + ((size_t)gu * NBK + ntu) * KB;
+    sb1 = B2s + ((size_t)gu * NBK + ntu) * KB;
+  } else {
+    sb0 = Bs + ((size_t)gu * NBK + min(ntu * 2 + wnu / 2, NBK - 1)) * KB;
+    sb1 = sb0;
+  }
+
+  f32x16 acc[MI][NB];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+  const int fr = lane & 31, fh = lane >> 5;
+  const int KT = K / BK;  // a multiple of 4
+
+  // stage t carries the scales of block t/2 iff t is even, into slot
+  // (t/2) % 2; with 4 steps per loop trip (kt % 4 == 0) both are fixed per
+  // unrolled step
+  MOE_ISSUE(0, 0, true, 0);
+  MOE_ISSUE(1, 1, false, 0);
+  MOE_ISSUE(2, 2, true, 1);
+  float sa[MI];  // this lane's token scales for the current block
+
+  // Step s: wait for stage s (stages s+1 and s+2 -- 2 OPS + 1 loads -- may
+  // still be in flight), barrier (stage s visible; every wave is past its
+  // reads of stage s-1, whose buffer takes step s+3, and of the scale slot
+  // that step s+3 refills), issue step s+3 (the last three steps re-load the
+  // final step into buffers nobody reads, so the wait count never changes),
+  // then fragments, MFMAs and the fold.
+#define MOE_STEP(st, s)                                                                     \
+  {                                                                                         \
+    wait_vmcnt<2 * OPS + 1>();                                                              \
+    stage_barrier();                                                                        \
+    MOE_ISSUE(((st) + 3) & 3, min((s) + 3, KT - 1), ((st) & 1) == 1, (st) == 1 ? 0 : 1);    \
+    const float s0 = sb0[(s) >> 1], s1 = sb1[(s) >> 1];                                     \
+    i32x8 w[NB];                                                                            \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                       \
+      w[nb] = frag(ring.b[st], b_row<SWIGLU>(wn, nb) + fr, fh);                             \
+    _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) {                                     \
+      const int r = wm * (MI * 32) + mi * 32 + fr;                                          \
+      const i32x8 x = frag(ring.a[st], r, fh);                                              \
+      if (((st) & 1) == 0) sa[mi] = ring.sa[(st) >> 1][(r >> 5) * 64 + (r & 31)];           \
+      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                   \
+        const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                   \
+            w[nb], x, f32x16{}, 0, 0, 0, 127, 0, 127);                                      \
+        const float c = sa[mi] * (nb == 0 ? s0 : s1);                                       \
+        _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2)                                   \
+          acc[mi][nb][r2] = fmaf(p[r2], c, acc[mi][nb][r2]);                                \
+      }                                                                                     \
+    }                                                                                       \
+  }
+
+  for (int kt = 0; kt < KT; kt += 4) {
+    MOE_STEP(0, kt)
+    MOE_STEP(1, kt + 1)
+    MOE_STEP(2, kt + 2)
+    MOE_STEP(3, kt + 3)
+  }
+  wait_vmcnt<0>();  // no LDS-direct load may still be landing when the tile ends
+#undef MOE_STEP
+#undef MOE_ISSUE
+
+  // epilogue.  32x32 accumulator layout: lane holds column (token) lane%32;
+  // register r holds row (weight row) 8*(r/4) + 4*(lane/32) + r%4, so each
+  // lane holds four runs of four consecutive output columns.
+  if (SWIGLU) {
+    // h for this lane's tokens: columns nt*128 + 32 wn + 8 j + 4 fh + i
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int ml = wm * (MI * 32) + mi * 32 + fr;
+      const int m = tile.m0 + ml;
+      float h[16];
+      float mx = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float g = acc[mi][0][r], u = acc[mi][1][r];
+        h[r] = g / (1.0f + expf(-g)) * u;
+        mx = fmaxf(mx, fabsf(h[r]));
+      }
+      if (OUT_FP8) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        if (fh == 0) ring.amax[wn * BM_MAX + ml] = mx;
+      } else if (m < tile.mend) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = tile.nt * 128 + wn * 32 + 8 * j + 4 * fh;
+          const uint32_t lo = f32_to_bf16_bits(h[4 * j]) | ((uint32_t)f32_to_bf16_bits(h[4 * j + 1]) << 16);
+          const uint32_t hi = f32_to_bf16_bits(h[4 * j + 2]) | ((uint32_t)f32_to_bf16_bits(h[4 * j + 3]) << 16);
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(C) + (size_t)m * N + n) = uint2{lo, hi};
+        }
+      }
+      if (OUT_FP8) {
+        // every wave reaches this barrier the same number of times (MI is
+        // uniform); the four wave columns' maxima of row ml are then visible
+        __syncthreads();
+        const float amax = fmaxf(fmaxf(ring.amax[ml], ring.amax[BM_MAX + ml]),
+                                 fmaxf(ring.amax[2 * BM_MAX + ml], ring.amax[3 * BM_MAX + ml]));
+        const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+        if (m < tile.mend) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = tile.nt * 128 + wn * 32 + 8 * j + 4 * fh;
+            const uint32_t q = f32_to_e4m3(h[4 * j] / sc) | (f32_to_e4m3(h[4 * j + 1] / sc) << 8) |
+                               (f32_to_e4m3(h[4 * j + 2] / sc) << 16) |
+                               (f32_to_e4m3(h[4 * j + 3] / sc) << 24);
+            *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(C) + (size_t)m * N + n) = q;
+          }
+          if (wn == 0 && fh == 0) Cs[(size_t)tile.nt * rows + m] = sc;
+        }
+        __syncthreads();  // the amax slots are rewritten for the next mi
+      }
+    }
+  } else {
+    // columns nt*256 + 64 wn + 32 nb + 8 j + 4 fh + i; quantisation group
+    // (E4M3 output) = wave columns {0,1} and {2,3}
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int ml = wm * (MI * 32) + mi * 32 + fr;
+      const int m = tile.m0 + ml;
+      const int nbase = tile.nt * 256 + wn * 64;
+      const bool live = nbase < N && m < tile.mend;
+      float sc = 1.0f;
+      if (OUT_FP8) {
+        float mx = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc[mi][nb][r]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        if (fh == 0) ring.amax[wn * BM_MAX + ml] = mx;
+        __syncthreads();
+        const int w0 = wn & ~1;
+        const float amax = fmaxf(ring.amax[w0 * BM_MAX + ml], ring.amax[(w0 + 1) * BM_MAX + ml]);
+        sc = amax > 0.f ? amax / 448.0f : 1.0f;
+        __syncthreads();
+      }
+      if (!live) continue;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = nbase + nb * 32 + 8 * j + 4 * fh;
+          const float v[4] = {acc[mi][nb][4 * j], acc[mi][nb][4 * j + 1],
+                              acc[mi][nb][4 * j + 2], acc[mi][nb][4 * j + 3]};
+          if (OUT_FP8) {
+            const uint32_t q = f32_to_e4m3(v[0] / sc) | (f32_to_e4m3(v[1] / sc) << 8) |
+                               (f32_to_e4m3(v[2] / sc) << 16) | (f32_to_e4m3(v[3] / sc) << 24);
+            *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(C) + (size_t)m * N + n) = q;
+          } else {
+            const uint32_t lo = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+            const uint32_t hi = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(C) + (size_t)m * N + n) = uint2{lo, hi};
+          }
+        }
+      if (OUT_FP8 && wn % 2 == 0 && fh == 0) Cs[(size_t)(tile.nt * 2 + wn / 2) * rows + m] = sc;
+    }
+  }
+}
+
+template <bool SWIGLU, bool OUT_FP8>
+__global__ __launch_bounds__(NTH, 1) void gemm_fp8_ring_kernel(
+    const uint8_t *__restrict__ Aq, const float *__restrict__ As, const uint8_t *__restrict__ Bq,
+    const float *__restrict__ Bs, const uint8_t *__restrict__ B2q,
+    const float *__restrict__ B2s, void *__restrict__ C, float *__restrict__ Cs,
+    const int32_t *__restrict__ offsets, int G, int rows, int N, int K, int nt_count) {
+  __shared__ u32x4 sA0[SLOTS_MAX], sA1[SLOTS_MAX], sA2[SLOTS_MAX], sA3[SLOTS_MAX];
+  __shared__ u32x4 sB0[SLOTS_B], sB1[SLOTS_B], sB2[SLOTS_B], sB3[SLOTS_B];
+  __shared__ float sS0[SROWS], sS1[SROWS];
+  __shared__ float s_amax[OUT_FP8 ? NWN * BM_MAX : 1];
+  __shared__ int s_cum[MOE_MAX_GROUPS + 1];
+  __shared__ int s_tmp[NW];
+
+  sched_build<NTH>(offsets, G, rows, BM_MAX, s_cum, s_tmp);
+  const int total = s_cum[G] * nt_count;
+  const int L = xcd_remap(blockIdx.x, total);
+  if (L < 0) return;
+  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM_MAX, nt_count, 8);
+  const Ring ring{{sA0, sA1, sA2, sA3}, {sB0, sB1, sB2, sB3}, {sS0, sS1}, s_amax};
+  const int h = tile.mend - tile.m0;  // wave-uniform
+  if (h > 128)
+    run_tile<256, SWIGLU, OUT_FP8>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+  else if (h > 64)
+    run_tile<128, SWIGLU, OUT_FP8>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+  else
+    run_tile<64, SWIGLU, OUT_FP8>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+}
+
+}  // namespace
+
+bool gemm_fp8_ring_supports(int rows, int N, int K) {
+  // per-lane source offsets are 32-bit: rows x K bytes of A and N x K bytes
+  // of one group's weights must stay below 4 GiB
+  return K > 0 && K % (4 * BK) == 0 && N % 128 == 0 && (long long)rows * K < (1ll << 32) &&
+         (long long)N * K < (1ll << 32);
+}
+
+hipError_t launch_gemm_fp8_ring(const uint8_t *Aq, const float *As, const uint8_t *Bq,
+                                const float *Bs, const uint8_t *B2q, const float *B2s, void *C,
+                                int c_dt, float *C_scale, const int32_t *offsets, int G,
+                                int rows, int N, int K, int epi, hipStream_t s) {
+  const bool swiglu = epi == MOE_EPI_SWIGLU;
+  const int nt = swiglu ? N / 128 : (N + 255) / 256;
+  const long long bound = (long long)host_row_tile_bound(rows, G, BM_MAX) * nt;
+  const dim3 grid((unsigned)((bound + 7) / 8 * 8)), block(NTH);
+  const bool f8 = c_dt == MOE_E4M3;
+  if (swiglu) {
+    if (f8)
+      hipLaunchKernelGGL((gemm_fp8_ring_kernel<true, true>), grid, block, 0, s, Aq, As, Bq, Bs,
+                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, nt);
+    else
+      hipLaunchKernelGGL((gemm_fp8_ring_kernel<true, false>), grid, block, 0, s, Aq, As, Bq, Bs,
+                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, nt);
+  } else {
+    if (f8)
+      hipLaunchKernelGGL((gemm_fp8_ring_kernel<false, true>), grid, block, 0, s, Aq, As, Bq, Bs,
+                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, nt);
+    else
+      hipLaunchKernelGGL((gemm_fp8_ring_kernel<false, false>), grid, block, 0, s, Aq, As, Bq, Bs,
+                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, nt);
+  }
+  return hipGetLastError();
+}

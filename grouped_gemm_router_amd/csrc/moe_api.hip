@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -141,6 +141,10 @@ moe_status_t moe_grouped_gemm_fp8(const uint8_t *A_q, const float *A_scale, cons
   if (c_dt == MOE_E4M3 ? !aligned4(C_scale) : C_scale != nullptr) return MOE_ERR_INVALID;
   if ((long long)G * N * K >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
+  if (gemm_fp8_ring_supports(rows, N, K))
+    return launched(launch_gemm_fp8_ring(A_q, A_scale, B_q, B_scale, B2_q, B2_scale, C, c_dt,
+                                         C_scale, offsets, G, rows, N, K, epi,
+                                         as_stream(stream)));
   return launched(launch_gemm_fp8(A_q, A_scale, B_q, B_scale, B2_q, B2_scale, C, c_dt, C_scale,
                                   offsets, G, rows, N, K, epi, as_stream(stream)));
 }

@@ -226,6 +226,11 @@ hipError_t launch_gemm_simple(const void *A, const void *B, const void *B2, int 
                               void *C, int c_dt, const int32_t *offsets, int G, int rows,
                               int N, int K, int epi, hipStream_t s);
 
+bool gemm_fp8_ring_supports(int rows, int N, int K);
+hipError_t launch_gemm_fp8_ring(const uint8_t *Aq, const float *As, const uint8_t *Bq,
+                                const float *Bs, const uint8_t *B2q, const float *B2s, void *C,
+                                int c_dt, float *C_scale, const int32_t *offsets, int G,
+                                int rows, int N, int K, int epi, hipStream_t s);
 hipError_t launch_gemm_fp8(const uint8_t *Aq, const float *As, const uint8_t *Bq,
                            const float *Bs, const uint8_t *B2q, const float *B2s, void *C,
                            int c_dt, float *C_scale, const int32_t *offsets, int G, int rows,

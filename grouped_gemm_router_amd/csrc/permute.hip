@@ -123,6 +123,8 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
   const int nent = (t1 - t0) * k;
   // shared-expert rows follow the routed rows: row = offsets[E] + s*T + t
   const size_t shared_base = (size_t)offsets[E];
+  // scales are stored group-major, [d/128][rows], rows = T*k + n_shared*T
+  const size_t srows = (size_t)T * (k + n_shared);
   for (int i = threadIdx.x; i < (t1 - t0) * n_shared; i += blockDim.x) {
     const int s = i / (t1 - t0), t = t0 + i % (t1 - t0);
     flat_to_row[(size_t)T * k + (size_t)s * T + t] = (int32_t)(shared_base + (size_t)s * T + t);
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
             row = shared_base + (size_t)(j - k) * T + t;
           }
           *reinterpret_cast<uint2 *>(dst + row * d + gi * 128 + lane16 * 8) = q;
-          if (lane16 == 0) x_scale[row * gpr + gi] = sc;
+          if (lane16 == 0) x_scale[(size_t)gi * srows + row] = sc;
         }
       }
     }

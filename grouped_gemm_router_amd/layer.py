@@ -82,9 +82,10 @@ class MoELayer:
         self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
         if self.fp8:
             self.x_perm = torch.empty((rows, self.d), dtype=torch.uint8, device=dev)
-            self.x_scale = torch.empty((rows, self.d // 128), dtype=f32, device=dev)
+            # scales group-major, [columns/128][rows]
+            self.x_scale = torch.empty((self.d // 128, rows), dtype=f32, device=dev)
             self.h = torch.empty((rows, self.dff), dtype=torch.uint8, device=dev)
-            self.h_scale = torch.empty((rows, self.dff // 128), dtype=f32, device=dev)
+            self.h_scale = torch.empty((self.dff // 128, rows), dtype=f32, device=dev)
             self.y = torch.empty((rows, self.d), dtype=torch.bfloat16, device=dev)
         else:
             self.x_perm = torch.empty((rows, self.d), dtype=self.act_dtype, device=dev)

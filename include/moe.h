@@ -142,8 +142,10 @@ size_t moe_permute_workspace_size(int T, int k, int E);
  * BF16) quantises every row in 1 x 128 groups ("DeepGEMM walkthrough" §2.3:
  * per-token, per-group scales): s = absmax / 448 (1 if the group is all
  * zero), q = E4M3 round-to-nearest-even of (x / s) with IEEE fp32 division,
- * saturating at +-448; x_perm_scale [rows][d/128] receives s (d % 128 == 0
- * required).  Otherwise x_perm_scale must be NULL.
+ * saturating at +-448; x_perm_scale receives s group-major, [d/128][rows]
+ * (scale of row r, group c at c * rows + r; rows = T*k + n_shared*T, so one
+ * column group's scales are contiguous for the GEMM's K loop); d % 128 == 0
+ * required.  Otherwise x_perm_scale must be NULL.
  * Each token's k experts must be distinct (top-k output always is).  An
  * entry of topk_idx outside [0, E) is dropped: it is counted nowhere, its
  * flat_to_row is -1 and no row is written for it; the rows stay compact
@@ -182,15 +184,16 @@ moe_status_t moe_grouped_gemm(const void *A, const void *B, const void *B2,
  * FP8 block-scaled grouped GEMM ("DeepGEMM walkthrough" §2.3 and §5.1).
  * The stored scales are dequantisation multipliers (the reciprocal of the
  * page's scale_A / scale_B; scale_C = 1):
- *   A[r][k]    ~ A_q[r][k] * A_scale[r][k/128]          A_scale [rows][K/128]
+ *   A[r][k]    ~ A_q[r][k] * A_scale[k/128][r]          A_scale [K/128][rows]
  *   B[g][n][k] ~ B_q[g][n][k] * B_scale[g][n/128][k/128]
  *                                                  B_scale [G][N/128][K/128]
  *   C = A B^T (or the SwiGLU form with B2) computed as
- *       sum_kb A_scale[r][kb] B_scale[g][n/128][kb] * (sum_{k in kb} A_q B_q)
+ *       sum_kb A_scale[kb][r] B_scale[g][n/128][kb] * (sum_{k in kb} A_q B_q)
  *   with fp32 accumulation.
  * c_dt == MOE_BF16 writes bf16.  c_dt == MOE_E4M3 quantises each output row
  * in 1 x 128 groups exactly as moe_permute does and writes C_scale
- * [rows][N/128]; C_scale must be NULL otherwise.
+ * [N/128][rows] (group-major, like A_scale, so it feeds the next GEMM);
+ * C_scale must be NULL otherwise.
  * Requires N % 128 == 0 and K % 128 == 0.
  */
 moe_status_t moe_grouped_gemm_fp8(const uint8_t *A_q, const float *A_scale,

@@ -62,7 +62,7 @@ def test_every_declared_function_is_exported(lib):
 def test_status_strings_and_version(lib):
     for s in range(5):
         assert lib.moe_status_string(s)
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 def test_route_validation(lib):

@@ -135,14 +135,30 @@ def to_dev(*ts):
     return [None if t is None else t.to(DEV) for t in ts]
 
 
-@pytest.mark.parametrize("sizes", [[0, 1, 127, 128, 129, 300], [64], [5, 0, 200]])
+def dev_operands(Aq, As, Bq, Bs, B2q, B2s):
+    """Device copies; activation scales go group-major, [K/128][rows]."""
+    dAq, dBq, dBs, dB2q, dB2s = to_dev(Aq, Bq, Bs, B2q, B2s)
+    return dAq, As.t().contiguous().to(DEV), dBq, dBs, dB2q, dB2s
+
+
+def host_scales(Cs):
+    """Output scales [N/128][rows] from the device, as [rows][N/128]."""
+    return Cs.t().cpu().numpy()
+
+
+# K % 256 == 0 runs the LDS-ring kernel (tile heights 64 / 128 / 256 picked
+# per tile: the sizes cross every switch point), other K the general one;
+# N = 384 leaves half a 256-column tile in the plain GEMM.
+@pytest.mark.parametrize("sizes", [[0, 1, 127, 128, 129, 300], [64], [5, 0, 200],
+                                   [64, 65, 256, 257, 320, 384, 385]])
 @pytest.mark.parametrize("N,K,swiglu", [(256, 128, False), (384, 256, False), (128, 384, True),
-                                        (256, 128, True)])
+                                        (256, 128, True), (384, 512, False), (256, 1024, True),
+                                        (512, 768, False)])
 def test_fp8_gemm_bf16_out(orc, sizes, N, K, swiglu):
     offs, Aq, As, Bq, Bs, B2q, B2s = make_fp8(sizes, N, K, 70 + N + K, swiglu)
     a = api()
     rows = int(offs[-1])
-    dAq, dAs, dBq, dBs, dB2q, dB2s = to_dev(Aq, As, Bq, Bs, B2q, B2s)
+    dAq, dAs, dBq, dBs, dB2q, dB2s = dev_operands(Aq, As, Bq, Bs, B2q, B2s)
     C = torch.full((rows, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     a.moe_grouped_gemm_fp8(dAq, dAs, dBq, dBs, C, torch.from_numpy(offs).to(DEV), B2_q=dB2q,
                            B2_scale=dB2s, epi=a.MOE_EPI_SWIGLU if swiglu else a.MOE_EPI_NONE)
@@ -154,21 +170,21 @@ def test_fp8_gemm_bf16_out(orc, sizes, N, K, swiglu):
     assert_within(C.float().cpu().numpy(), ref, bound)
 
 
-@pytest.mark.parametrize("sizes", [[0, 3, 129, 256], [40]])
-@pytest.mark.parametrize("N,K", [(256, 256), (128, 128)])
+@pytest.mark.parametrize("sizes", [[0, 3, 129, 256], [40], [70, 300]])
+@pytest.mark.parametrize("N,K", [(256, 256), (128, 128), (384, 512)])
 def test_fp8_gemm_e4m3_out_swiglu(orc, sizes, N, K):
     offs, Aq, As, Bq, Bs, B2q, B2s = make_fp8(sizes, N, K, 90 + N, True)
     a = api()
     rows = int(offs[-1])
-    dAq, dAs, dBq, dBs, dB2q, dB2s = to_dev(Aq, As, Bq, Bs, B2q, B2s)
+    dAq, dAs, dBq, dBs, dB2q, dB2s = dev_operands(Aq, As, Bq, Bs, B2q, B2s)
     C = torch.zeros((rows, N), dtype=torch.uint8, device=DEV)
-    Cs = torch.zeros((rows, N // 128), dtype=torch.float32, device=DEV)
+    Cs = torch.zeros((N // 128, rows), dtype=torch.float32, device=DEV)
     a.moe_grouped_gemm_fp8(dAq, dAs, dBq, dBs, C, torch.from_numpy(offs).to(DEV), B2_q=dB2q,
                            B2_scale=dB2s, C_scale=Cs, epi=a.MOE_EPI_SWIGLU)
     torch.cuda.synchronize()
     h, hb = fp8_ref_and_bound(orc, Aq.numpy(), As.numpy(), Bq.numpy(), Bs.numpy(), B2q.numpy(),
                               B2s.numpy(), offs, np.arange(rows), True, 0.0)
-    check_e4m3_output(orc, C.cpu().numpy(), Cs.cpu().numpy(), h, hb)
+    check_e4m3_output(orc, C.cpu().numpy(), host_scales(Cs), h, hb)
 
 
 def check_e4m3_output(orc, gq, gs, h, hb):
@@ -184,15 +200,41 @@ def check_e4m3_output(orc, gq, gs, h, hb):
     assert_within(deq, h, bound, "dequantised E4M3 output")
 
 
-def test_fp8_gemm_e4m3_out_plain(orc):
-    offs, Aq, As, Bq, Bs, _, _ = make_fp8([100, 0, 60], 256, 256, 3, False)
+@pytest.mark.parametrize("sizes,N,K", [([100, 0, 60], 256, 256), ([300, 20], 384, 512),
+                                       ([7], 256, 128)])
+def test_fp8_gemm_e4m3_out_plain(orc, sizes, N, K):
+    offs, Aq, As, Bq, Bs, _, _ = make_fp8(sizes, N, K, 3, False)
     a = api()
     rows = int(offs[-1])
-    dAq, dAs, dBq, dBs = to_dev(Aq, As, Bq, Bs)
-    C = torch.zeros((rows, 256), dtype=torch.uint8, device=DEV)
-    Cs = torch.zeros((rows, 2), dtype=torch.float32, device=DEV)
+    dAq, dAs, dBq, dBs, _, _ = dev_operands(Aq, As, Bq, Bs, None, None)
+    C = torch.zeros((rows, N), dtype=torch.uint8, device=DEV)
+    Cs = torch.zeros((N // 128, rows), dtype=torch.float32, device=DEV)
     a.moe_grouped_gemm_fp8(dAq, dAs, dBq, dBs, C, torch.from_numpy(offs).to(DEV), C_scale=Cs)
     torch.cuda.synchronize()
     c, cb = fp8_ref_and_bound(orc, Aq.numpy(), As.numpy(), Bq.numpy(), Bs.numpy(), None, None,
                               offs, np.arange(rows), False, 0.0)
-    check_e4m3_output(orc, C.cpu().numpy(), Cs.cpu().numpy(), c, cb)
+    check_e4m3_output(orc, C.cpu().numpy(), host_scales(Cs), c, cb)
+
+
+@pytest.mark.parametrize("N,K,swiglu", [(128, 7168, True), (512, 2048, False)])
+def test_fp8_deepseek_shaped_groups_sampled(orc, N, K, swiglu):
+    """257 groups of ~128 rows (256 routed experts at T=4096, k=8, and a
+    4096-row shared group) at the DeepSeek K of gate/up and down, N cut to
+    keep the weights small; sampled rows of every group."""
+    from gpu_util import sample_rows
+    rng = np.random.default_rng(12)
+    sizes = np.concatenate([rng.integers(98, 166, 256), [4096]])
+    offs, Aq, As, Bq, Bs, B2q, B2s = make_fp8(sizes, N, K, 80 + K, swiglu)
+    a = api()
+    rows = int(offs[-1])
+    dAq, dAs, dBq, dBs, dB2q, dB2s = dev_operands(Aq, As, Bq, Bs, B2q, B2s)
+    C = torch.full((rows, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    a.moe_grouped_gemm_fp8(dAq, dAs, dBq, dBs, C, torch.from_numpy(offs).to(DEV), B2_q=dB2q,
+                           B2_scale=dB2s, epi=a.MOE_EPI_SWIGLU if swiglu else a.MOE_EPI_NONE)
+    torch.cuda.synchronize()
+    sel = sample_rows(offs, per_group=2, seed=2)
+    ref, bound = fp8_ref_and_bound(orc, Aq.numpy(), As.numpy(), Bq.numpy(), Bs.numpy(),
+                                   None if B2q is None else B2q.numpy(),
+                                   None if B2s is None else B2s.numpy(), offs, sel, swiglu,
+                                   2.0 ** -8)
+    assert_within(C.float().cpu().numpy()[sel], ref, bound)

@@ -23,7 +23,7 @@ def run_permute(x, idx, E, ns, fp8=False):
     rows = T * k + ns * T
     out_dtype = torch.uint8 if fp8 else x.dtype
     x_perm = torch.full((rows, d), 0, dtype=out_dtype, device=DEV)
-    scale = torch.zeros((rows, d // 128), dtype=torch.float32, device=DEV) if fp8 else None
+    scale = torch.zeros((d // 128, rows), dtype=torch.float32, device=DEV) if fp8 else None
     counts = torch.empty((E,), dtype=torch.int32, device=DEV)
     offsets = torch.empty((E + ns + 1,), dtype=torch.int32, device=DEV)
     perm_src = torch.empty((T * k,), dtype=torch.int32, device=DEV)
@@ -33,6 +33,8 @@ def run_permute(x, idx, E, ns, fp8=False):
     a.moe_permute(x, idx, E, ns, x_perm, counts, offsets, perm_src, f2r, ws,
                   x_perm_scale=scale)
     torch.cuda.synchronize()
+    # scales come back group-major [d/128][rows]; hand them out row-major
+    scale = scale.t().contiguous() if fp8 else None
     return x_perm, scale, counts, offsets, perm_src, f2r
 
 
