@@ -13,7 +13,6 @@ recorded on the launch stream around every call of every timed step.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -26,8 +25,7 @@ METRIC = "grouped-GEMM TFLOP/s (% MFMA peak) + MoE-layer tokens/s per config"
 PEAK = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}  # dense MFMA TFLOP/s, MI355X
 HBM_PEAK_GBS = 8000.0
 STEP_NAMES = ["route", "permute", "gemm_gate_up", "gemm_down", "combine"]
-KERNEL_SOURCES = {"gemm_gate_up": ["gemm_bf16.hip", "gemm_fp8.hip", "moe_internal.h"],
-                  "gemm_down": ["gemm_bf16.hip", "gemm_fp8.hip", "moe_internal.h"]}
+
 
 
 def parse():
@@ -42,14 +40,6 @@ def parse():
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
-
-
-def source_hash(names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "grouped_gemm_router_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def step_bytes_flops(cfg, counts):
@@ -67,20 +57,23 @@ def step_bytes_flops(cfg, counts):
     wsc = (active * 2 * (dff // 128) * (d // 128) * 4) if cfg.dtype == "fp8" else 0
     out["gemm_gate_up"] = (rows * d * act_es + active * 2 * dff * d * w_es + wsc
                            + rows * dff * act_es, 2.0 * rows * d * 2 * dff)
+    y_es = 2 if cfg.dtype == "fp8" else 4  # Y is fp32 except in the FP8 layer
     out["gemm_down"] = (rows * dff * act_es + active * d * dff * w_es + wsc // 2
-                        + rows * d * es, 2.0 * rows * dff * d)
-    out["combine"] = (rows * d * es + T * d * es + T * k * 8, 0.0)
+                        + rows * d * y_es, 2.0 * rows * dff * d)
+    out["combine"] = (rows * d * y_es + T * d * es + T * k * 8, 0.0)
     return out
 
 
 def load_traffic(kernel, cfg_name):
-    """Counter-measured HBM bytes for a kernel, if taken on the current source."""
+    """Counter-measured HBM bytes per launch of a kernel (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy), if taken on the current source."""
+    from grouped_gemm_router_amd.profiling import source_hash
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, cfg_name))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+    if rec.get("source_hash") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
