@@ -30,8 +30,8 @@
 //     each wave's columns cover matching gate and up rows, so the epilogue
 //     pairs silu(gate) * up in registers;
 //   * the tile scheduler reads the device offsets array (no host round trip
-//     of expert sizes), and the XCD-aware remap keeps tiles that share
-//     weight columns / activation rows on one XCD (one L2);
+//     of expert sizes); tiles are taken in an order that keeps all XCDs on
+//     one expert at a time (see tile_of_workgroup);
 //   * ragged tails: A rows past the group end are loaded (clamped to the
 //     buffer) and multiplied but never stored.
 #include "moe_internal.h"
@@ -298,9 +298,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
 
   sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_tmp);
   const int total = s_cum[G] * nt_count;
-  const int L = xcd_remap(blockIdx.x, total);
+  const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM_MAX, nt_count, 8);
+  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM_MAX, nt_count, kTileChunk);
   const int h = tile.mend - tile.m0;  // wave-uniform
   if (h > 128)
     run_tile<256, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, sA0, sA1, sA2, sA3, sB0,

@@ -57,9 +57,9 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
 
   sched_build<FNTH>(offsets, G, rows, FBM, s_cum, s_tmp);
   const int total = s_cum[G] * nt_count;
-  const int L = xcd_remap(blockIdx.x, total);
+  const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, FBM, nt_count, 8);
+  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, FBM, nt_count, kTileChunk);
 
   const int tid = threadIdx.x;
   const int lane = lane_id(), wv = tid / kWave;

@@ -348,9 +348,9 @@ __global__ __launch_bounds__(NTH, 1) void gemm_fp8_ring_kernel(
 
   sched_build<NTH>(offsets, G, rows, BM_MAX, s_cum, s_tmp);
   const int total = s_cum[G] * nt_count;
-  const int L = xcd_remap(blockIdx.x, total);
+  const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM_MAX, nt_count, 8);
+  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM_MAX, nt_count, kTileChunk);
   const Ring ring{{sA0, sA1, sA2, sA3}, {sB0, sB1, sB2, sB3}, {sS0, sS1}, s_amax};
   const int h = tile.mend - tile.m0;  // wave-uniform
   if (h > 128)

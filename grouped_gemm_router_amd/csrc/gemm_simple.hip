@@ -36,9 +36,9 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(
 
   sched_build<256>(offsets, G, rows, SBM, s_cum, s_tmp);
   const int total = s_cum[G] * nt_count;
-  const int L = xcd_remap(blockIdx.x, total);
+  const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, SBM, nt_count, 8);
+  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, SBM, nt_count, kTileChunk);
   const int n0 = tile.nt * SBN;
   const size_t boff = (size_t)tile.g * N * K;
 
