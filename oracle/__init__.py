@@ -78,6 +78,10 @@ def _declare(L):
     L.orc_counts_offsets.argtypes = [vp, i64, i32, i32, i32, vp, vp]
     L.orc_permutation.restype = None
     L.orc_permutation.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    L.orc_capacity_permutation.restype = C.c_int64
+    L.orc_capacity_permutation.argtypes = [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]
+    L.orc_router_stats.restype = None
+    L.orc_router_stats.argtypes = [vp, i64, i32, vp, i32, C.c_double, vp, vp, vp]
     L.orc_permute_rows.restype = None
     L.orc_permute_rows.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, vp]
     L.orc_gemm_rows.restype = None
@@ -189,6 +193,35 @@ def permutation(idx: np.ndarray, E: int, offsets: np.ndarray):
     f2r = np.empty(T * k, dtype=np.int32)
     lib().orc_permutation(_p(idx), T, k, E, _p(offsets), _p(perm_src), _p(f2r))
     return perm_src, f2r
+
+
+def capacity_permutation(idx: np.ndarray, E: int, capacity: int, n_shared: int = 0):
+    """(counts, offsets, perm_src [kept rows], flat_to_row [T*k + n_shared*T],
+    overflow [dropped]) with each expert capped at `capacity` rows."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + n_shared + 1, dtype=np.int32)
+    perm_src = np.full(T * k, -1, dtype=np.int32)
+    f2r = np.empty(T * k + n_shared * T, dtype=np.int32)
+    overflow = np.full(T * k, -1, dtype=np.int32)
+    n = lib().orc_capacity_permutation(_p(idx), T, k, E, n_shared, int(capacity), _p(counts),
+                                       _p(offsets), _p(perm_src), _p(f2r), _p(overflow))
+    if n < 0:
+        raise ValueError("expert index out of range")
+    return counts, offsets, perm_src[: offsets[E]], f2r, overflow[:n]
+
+
+def router_stats(logits32: np.ndarray, counts: np.ndarray, k: int, alpha: float):
+    """(f [E], P [E], aux, max_over_mean, entropy) in fp64."""
+    lg = _c(logits32, np.float32)
+    T, E = lg.shape
+    counts = _c(counts, np.int32)
+    f = np.empty(E, dtype=np.float64)
+    P = np.empty(E, dtype=np.float64)
+    summ = np.empty(3, dtype=np.float64)
+    lib().orc_router_stats(_p(lg), T, E, _p(counts), k, float(alpha), _p(f), _p(P), _p(summ))
+    return f, P, float(summ[0]), float(summ[1]), float(summ[2])
 
 
 def permute_rows(x: np.ndarray, k: int, perm_src: np.ndarray, rows: np.ndarray):

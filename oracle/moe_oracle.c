@@ -263,6 +263,120 @@ void orc_permutation(const int32_t *idx, int64_t T, int k, int E,
 }
 
 /*
+ * Capacity-limited permutation ("Dense GEMM to TP MoE" §5.1: at inference a
+ * capacity factor caps how many tokens each expert takes and the excess
+ * goes down a fallback path; "DeepSeek MoE evolution" §3.2 on the cap as a
+ * bound on the tokens one expert takes in one forward pass).  Reading: the
+ * cap is an integer number of rows per expert; an expert keeps its first
+ * `capacity` routed entries in flat order f = t*k + j and drops the rest.
+ *   counts[e]       = routed entries of expert e (before the cap)
+ *   offsets         = exclusive prefix of min(counts[e], capacity), then
+ *                     n_shared groups of T rows
+ *   perm_src, flat_to_row as in orc_permutation for kept entries;
+ *   flat_to_row[f]  = -1 for a dropped entry;
+ *   flat_to_row[T*k + s*T + t] = offsets[E] + s*T + t (shared rows)
+ *   overflow        = dropped flat indices, expert by expert, each
+ *                     expert's in ascending f, starting at the exclusive
+ *                     prefix of max(counts[e] - capacity, 0)
+ *   returns the number of dropped entries (-1 for an index outside [0, E)).
+ * Pinned by: numpy stable argsort grouped by expert and sliced at the cap;
+ * capacity >= max count reproduces orc_permutation.
+ */
+int64_t orc_capacity_permutation(const int32_t *idx, int64_t T, int k, int E, int n_shared,
+                                 int64_t capacity, int32_t *counts, int32_t *offsets,
+                                 int32_t *perm_src, int32_t *flat_to_row, int32_t *overflow) {
+  if (E <= 0 || capacity < 0) return -1;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t f = 0; f < T * k; ++f) {
+    if (idx[f] < 0 || idx[f] >= E) return -1;
+    counts[idx[f]] += 1;
+  }
+  int64_t *ov_start = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+  int64_t *seen = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+  int64_t n_over = 0;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) {
+    int64_t kept = counts[e] < capacity ? counts[e] : capacity;
+    offsets[e + 1] = offsets[e] + (int32_t)kept;
+    ov_start[e] = n_over;
+    n_over += counts[e] - kept;
+  }
+  for (int s = 0; s < n_shared; ++s) offsets[E + s + 1] = offsets[E + s] + (int32_t)T;
+  for (int64_t f = 0; f < T * k; ++f) {
+    int e = idx[f];
+    int64_t r = seen[e]++;
+    if (r < capacity) {
+      int32_t row = offsets[e] + (int32_t)r;
+      perm_src[row] = (int32_t)f;
+      flat_to_row[f] = row;
+    } else {
+      flat_to_row[f] = -1;
+      overflow[ov_start[e] + (r - capacity)] = (int32_t)f;
+    }
+  }
+  for (int s = 0; s < n_shared; ++s)
+    for (int64_t t = 0; t < T; ++t)
+      flat_to_row[T * k + s * T + t] = offsets[E] + (int32_t)(s * T + t);
+  free(ov_start);
+  free(seen);
+  return n_over;
+}
+
+/*
+ * Router statistics for load balancing, forward only.
+ *   p[t][e] = softmax over all E of the binary32 logits (fp64, max-subtracted,
+ *             as in orc_topk)
+ *   P[e]    = (1/T) sum_t p[t][e]       mean gate probability
+ *   f[e]    = counts[e] / (T*k)         share of the routed entries
+ *   aux     = alpha * E * sum_e f[e] P[e]
+ *             ("DeepGEMM walkthrough" §2.2; reading: f is the share of the
+ *             T*k routed entries, so sum f = 1 and a uniform router gives
+ *             aux = alpha whatever E and k are)
+ *   max_over_mean = max_e counts[e] / (sum_e counts[e] / E)
+ *             ("Dense GEMM to TP MoE" §5.1: above 3 is a severe imbalance)
+ *   entropy = -sum_e q[e] log2(q[e] + 1e-8), q = counts / sum counts
+ *             ("DeepSeek MoE evolution" §2.3, in bits)
+ * summary = {aux, max_over_mean, entropy}.
+ * Pinned by: closed forms (equal logits -> P = 1/E; uniform counts ->
+ * max/mean 1, entropy log2 E; one expert -> entropy 0, max/mean E) and scipy
+ * softmax + numpy on random inputs.
+ */
+void orc_router_stats(const float *logits, int64_t T, int E, const int32_t *counts, int k,
+                      double alpha, double *f, double *P, double *summary) {
+  for (int e = 0; e < E; ++e) P[e] = 0.0;
+  double *p = (double *)malloc(sizeof(double) * (size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    const float *l = logits + t * E;
+    double mx = l[0];
+    for (int e = 1; e < E; ++e)
+      if (l[e] > mx) mx = l[e];
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) {
+      p[e] = exp((double)l[e] - mx);
+      z += p[e];
+    }
+    for (int e = 0; e < E; ++e) P[e] += p[e] / z;
+  }
+  free(p);
+  double total = 0.0, cmax = 0.0;
+  for (int e = 0; e < E; ++e) {
+    P[e] /= (double)T;
+    f[e] = (double)counts[e] / ((double)T * (double)k);
+    total += counts[e];
+    if (counts[e] > cmax) cmax = counts[e];
+  }
+  double dot = 0.0, ent = 0.0;
+  for (int e = 0; e < E; ++e) {
+    dot += f[e] * P[e];
+    double q = total > 0 ? counts[e] / total : 0.0;
+    ent -= q * log2(q + 1e-8);
+  }
+  summary[0] = alpha * E * dot;
+  summary[1] = total > 0 ? cmax / (total / E) : 0.0;
+  summary[2] = ent;
+}
+
+/*
  * Gathers the permuted activation rows x_perm[r] for the rows listed in
  * row_list: row r < T*k copies x[perm_src[r] / k]; a shared-expert row
  * r = T*k + s*T + t copies x[t].  Rows are copied byte for byte.
