@@ -78,6 +78,67 @@ def load_traffic(kernel, cfg_name):
     return rec.get("bytes_per_launch")
 
 
+def timed(fn, reps, stream):
+    """Average ms of fn over reps launches, HIP events on the launch stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def extras(cfg, layer, x, reps, stream):
+    """The routing variants outside the layer step, timed on their own:
+    the router statistics of this routing decision, and the permutation with
+    a capacity factor of 1.0 (ceil(T k / E) rows per expert)."""
+    import torch
+    from grouped_gemm_router_amd import api
+    T, E, k, d = cfg.T, cfg.E, cfg.k, cfg.d
+    dev = x.device
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    api.moe_route(x, layer.w_router, idx, w, logits=lg, logit_bias=layer.bias)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    f = torch.empty((E,), dtype=torch.float32, device=dev)
+    P = torch.empty_like(f)
+    summ = torch.empty((3,), dtype=torch.float32, device=dev)
+    sws = torch.empty((max(api.moe_router_stats_workspace_size(T, E), 4),), dtype=torch.uint8,
+                      device=dev)
+    out = {}
+    # permutation under a capacity factor of 1.0
+    cap = -(-T * k // E)
+    ov = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    nov = torch.empty((1,), dtype=torch.int32, device=dev)
+    run = lambda: api.moe_permute_capped(x, idx, E, layer.n_shared, cap, layer.x_perm, counts,  # noqa: E731
+                                         layer.offsets, layer.perm_src, layer.flat_to_row,
+                                         layer.ws, overflow=ov, n_overflow=nov,
+                                         x_perm_scale=layer.x_scale)
+    ms = timed(run, reps, stream)
+    kept = int(layer.offsets[E].item())
+    es = 4 if cfg.dtype == "f32" else 2
+    oes = 1 if cfg.dtype == "fp8" else es
+    by = T * d * es + (kept + layer.n_shared * T) * d * oes + T * k * 4 * 4
+    out["permute_capped_cf1"] = {"ms": round(ms, 5), "capacity": cap,
+                                 "dropped": int(nov.item()), "GB/s": round(by / ms / 1e6, 1),
+                                 "hbm_frac": round(by / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    # router statistics (reads the logits and the counts)
+    run = lambda: api.moe_router_stats(lg, counts, k, 0.01, f, P, summ, ws=sws)  # noqa: E731
+    ms = timed(run, reps, stream)
+    by = T * E * 4 + E * 4 * 3 + 12
+    s = summ.cpu().tolist()
+    out["router_stats"] = {"ms": round(ms, 5), "GB/s": round(by / ms / 1e6, 1),
+                           "hbm_frac": round(by / ms / 1e6 / HBM_PEAK_GBS, 4),
+                           "aux_loss_alpha_0.01": round(s[0], 6),
+                           "max_over_mean": round(s[1], 4), "entropy_bits": round(s[2], 4)}
+    return out
+
+
 def cpu_baseline(cfg, layer, x, wr, bias, weights, target_s):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -214,6 +275,8 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4), "traffic": traffic}
 
+    extra = extras(cfg, layer, x, K, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, layer, x, wr, bias, weights, args.cpu_seconds)
@@ -237,6 +300,7 @@ def main():
         "grouped_gemm_tflops": round(gemm_tflops, 2),
         "grouped_gemm_frac_mfma_peak": round(gemm_tflops / peak, 4),
         "kernels": kernels,
+        "extras": extra,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -19,10 +19,11 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH 
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_ROUTE_RENORM, MOE_ROUTE_FROM_LOGITS = 1, 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTS = ["moe_status_string", "moe_abi_version", "moe_route_workspace_size", "moe_route",
-           "moe_permute_workspace_size",
+           "moe_permute_workspace_size", "moe_permute_capped", "moe_router_stats_workspace_size",
+           "moe_router_stats",
            "moe_permute", "moe_grouped_gemm", "moe_grouped_gemm_fp8", "moe_combine",
            "moe_quantize_fp8"]
 
@@ -52,6 +53,13 @@ def _load():
     lib.moe_permute.restype = i32
     lib.moe_permute.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                 vp, vp, sz, vp]
+    lib.moe_permute_capped.restype = i32
+    lib.moe_permute_capped.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, i32, vp, vp, vp,
+                                       vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_router_stats_workspace_size.restype = sz
+    lib.moe_router_stats_workspace_size.argtypes = [i32, i32]
+    lib.moe_router_stats.restype = i32
+    lib.moe_router_stats.argtypes = [vp, vp, i32, i32, i32, C.c_float, vp, vp, vp, vp, sz, vp]
     lib.moe_grouped_gemm.restype = i32
     lib.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, vp]
     lib.moe_grouped_gemm_fp8.restype = i32
@@ -155,6 +163,41 @@ def moe_permute(x, topk_idx, E, n_shared, x_perm, counts, offsets, perm_src, fla
                                           _ptr(counts), _ptr(offsets), _ptr(perm_src),
                                           _ptr(flat_to_row), _ptr(ws), ws_bytes,
                                           _stream(stream)))
+
+
+def moe_permute_capped(x, topk_idx, E, n_shared, capacity, x_perm, counts, offsets, perm_src,
+                       flat_to_row, ws, *, overflow=None, n_overflow=None, x_perm_scale=None,
+                       stream=None):
+    """moe_permute with each expert capped at `capacity` rows; dropped
+    entries get flat_to_row -1 and are listed in `overflow` (expert by
+    expert), their number in n_overflow[0]."""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_permute_capped",
+           lib.moe_permute_capped(_ptr(x), _dt(x), T, d, _ptr(topk_idx), k, E, n_shared,
+                                  int(capacity), _dt(x_perm), _ptr(x_perm), _ptr(x_perm_scale),
+                                  _ptr(counts), _ptr(offsets), _ptr(perm_src),
+                                  _ptr(flat_to_row), _ptr(overflow), _ptr(n_overflow),
+                                  _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_router_stats_workspace_size(T: int, E: int) -> int:
+    return int(lib.moe_router_stats_workspace_size(T, E))
+
+
+def moe_router_stats(logits, counts, k, alpha, f, P, summary, *, ws=None, stream=None):
+    """Load-balance statistics: f [E], P [E], summary [3] = (aux loss,
+    max/mean count, entropy in bits).  ws: moe_router_stats_workspace_size
+    bytes; when None, one is allocated here for this call."""
+    T, E = logits.shape
+    if ws is None:
+        ws = torch.empty(max(moe_router_stats_workspace_size(T, E), 4), dtype=torch.uint8,
+                         device=logits.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("moe_router_stats",
+           lib.moe_router_stats(_ptr(logits), _ptr(counts), T, E, k, float(alpha), _ptr(f),
+                                _ptr(P), _ptr(summary), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_grouped_gemm(A, B, C_out, offsets, *, B2=None, epi=MOE_EPI_NONE, stream=None):

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 
 SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_fp8_ring.hip",
-           "gemm_simple.hip", "combine.hip", "quant.hip"]
+           "gemm_simple.hip", "combine.hip", "quant.hip", "router_stats.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -73,12 +73,16 @@ size_t moe_permute_workspace_size(int T, int k, int E) {
   return permute_ws_bytes(T, k, E);
 }
 
-moe_status_t moe_permute(const void *x, moe_dtype_t x_dt, int T, int d, const int32_t *topk_idx,
-                         int k, int E, int n_shared, moe_dtype_t out_dt, void *x_perm,
-                         float *x_perm_scale, int32_t *counts, int32_t *offsets,
-                         int32_t *perm_src, int32_t *flat_to_row, void *ws, size_t ws_bytes,
-                         moe_stream_t stream) {
-  if (T < 0 || d < 8 || E < 1 || k < 1 || k > E || n_shared < 0) return MOE_ERR_INVALID;
+namespace {
+
+moe_status_t permute_checked(const void *x, moe_dtype_t x_dt, int T, int d,
+                             const int32_t *topk_idx, int k, int E, int n_shared, int capacity,
+                             moe_dtype_t out_dt, void *x_perm, float *x_perm_scale,
+                             int32_t *counts, int32_t *offsets, int32_t *perm_src,
+                             int32_t *flat_to_row, int32_t *overflow, int32_t *n_overflow,
+                             void *ws, size_t ws_bytes, moe_stream_t stream) {
+  if (T < 0 || d < 8 || E < 1 || k < 1 || k > E || n_shared < 0 || capacity < 0)
+    return MOE_ERR_INVALID;
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || n_shared > 8) return MOE_ERR_UNSUPPORTED;
   if (!is_act(x_dt)) return MOE_ERR_UNSUPPORTED;
   if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;
@@ -91,15 +95,61 @@ moe_status_t moe_permute(const void *x, moe_dtype_t x_dt, int T, int d, const in
     if (x_perm_scale) return MOE_ERR_INVALID;
   }
   if (!aligned16(x) || !aligned16(x_perm) || !aligned4(topk_idx) || !aligned4(counts) ||
-      !aligned4(offsets) || !aligned4(perm_src) || !aligned4(flat_to_row))
+      !aligned4(offsets) || !aligned4(perm_src) || !aligned4(flat_to_row) ||
+      !opt_aligned4(overflow) || !opt_aligned4(n_overflow))
     return MOE_ERR_INVALID;
   const size_t need = permute_ws_bytes(T, k, E);
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (need > 0 && !aligned4(ws)) return MOE_ERR_INVALID;
   if (T == 0) return MOE_OK;
-  return launched(launch_permute(x, x_dt, T, d, topk_idx, k, E, n_shared, out_dt, x_perm,
-                                 x_perm_scale, counts, offsets, perm_src, flat_to_row, ws,
-                                 as_stream(stream)));
+  return launched(launch_permute(x, x_dt, T, d, topk_idx, k, E, n_shared, capacity, out_dt,
+                                 x_perm, x_perm_scale, counts, offsets, perm_src, flat_to_row,
+                                 overflow, n_overflow, ws, as_stream(stream)));
+}
+
+}  // namespace
+
+moe_status_t moe_permute(const void *x, moe_dtype_t x_dt, int T, int d, const int32_t *topk_idx,
+                         int k, int E, int n_shared, moe_dtype_t out_dt, void *x_perm,
+                         float *x_perm_scale, int32_t *counts, int32_t *offsets,
+                         int32_t *perm_src, int32_t *flat_to_row, void *ws, size_t ws_bytes,
+                         moe_stream_t stream) {
+  return permute_checked(x, x_dt, T, d, topk_idx, k, E, n_shared, INT32_MAX, out_dt, x_perm,
+                         x_perm_scale, counts, offsets, perm_src, flat_to_row, nullptr, nullptr,
+                         ws, ws_bytes, stream);
+}
+
+moe_status_t moe_permute_capped(const void *x, moe_dtype_t x_dt, int T, int d,
+                                const int32_t *topk_idx, int k, int E, int n_shared,
+                                int capacity, moe_dtype_t out_dt, void *x_perm,
+                                float *x_perm_scale, int32_t *counts, int32_t *offsets,
+                                int32_t *perm_src, int32_t *flat_to_row, int32_t *overflow,
+                                int32_t *n_overflow, void *ws, size_t ws_bytes,
+                                moe_stream_t stream) {
+  return permute_checked(x, x_dt, T, d, topk_idx, k, E, n_shared, capacity, out_dt, x_perm,
+                         x_perm_scale, counts, offsets, perm_src, flat_to_row, overflow,
+                         n_overflow, ws, ws_bytes, stream);
+}
+
+size_t moe_router_stats_workspace_size(int T, int E) {
+  if (T < 0 || E < 1) return 0;
+  return router_stats_ws_bytes(T, E);
+}
+
+moe_status_t moe_router_stats(const float *logits, const int32_t *counts, int T, int E, int k,
+                              float alpha, float *f, float *P, float *summary, void *ws,
+                              size_t ws_bytes, moe_stream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (!aligned4(logits) || !aligned4(counts) || !aligned4(f) || !aligned4(P) ||
+      !aligned4(summary))
+    return MOE_ERR_INVALID;
+  const size_t need = router_stats_ws_bytes(T, E);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (need > 0 && !aligned4(ws)) return MOE_ERR_INVALID;
+  if (T == 0) return MOE_OK;
+  return launched(launch_router_stats(logits, counts, T, E, k, alpha, f, P, summary,
+                                      static_cast<float *>(ws), as_stream(stream)));
 }
 
 moe_status_t moe_grouped_gemm(const void *A, const void *B, const void *B2, moe_dtype_t ab_dt,

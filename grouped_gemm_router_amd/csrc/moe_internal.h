@@ -208,15 +208,23 @@ inline int host_row_tile_bound(int rows, int G, int BM) { return rows / BM + G; 
 // ---------------------------------------------------------------------------
 
 size_t route_ws_bytes(int T, int d, int E);
+
+size_t router_stats_ws_bytes(int T, int E);
+hipError_t launch_router_stats(const float *logits, const int32_t *counts, int T, int E, int k,
+                               float alpha, float *f, float *P, float *summary, float *ws,
+                               hipStream_t s);
 hipError_t launch_route(const void *x, const void *w_router, int dt, const float *bias,
                         int T, int d, int E, int k, unsigned flags, float *logits,
                         int32_t *topk_idx, float *topk_w, float *ws, hipStream_t s);
 
 size_t permute_ws_bytes(int T, int k, int E);
+// capacity: rows kept per expert (INT_MAX: drop-less); overflow and
+// n_overflow may be null
 hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *topk_idx,
-                          int k, int E, int n_shared, int out_dt, void *x_perm,
+                          int k, int E, int n_shared, int capacity, int out_dt, void *x_perm,
                           float *x_perm_scale, int32_t *counts, int32_t *offsets,
-                          int32_t *perm_src, int32_t *flat_to_row, void *ws, hipStream_t s);
+                          int32_t *perm_src, int32_t *flat_to_row, int32_t *overflow,
+                          int32_t *n_overflow, void *ws, hipStream_t s);
 
 hipError_t launch_gemm_bf16_mfma(const void *A, const void *B, const void *B2, void *C,
                                  int c_dt, const int32_t *offsets, int G, int rows, int N,

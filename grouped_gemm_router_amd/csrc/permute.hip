@@ -14,8 +14,13 @@
 //               the block's count per expert is popcount(bitmap).
 //               Ranks are parked in flat_to_row, counts in the workspace.
 //   2. scan     one workgroup: per expert, exclusive prefix over blocks
-//               (in place), then the exclusive prefix over experts ->
-//               offsets.
+//               (in place), then the exclusive prefix over experts of the
+//               kept counts -> offsets (and of the dropped counts -> where
+//               each expert's dropped entries start in the overflow list).
+//               With a capacity ("Dense GEMM to TP MoE" §5.1: cap the
+//               tokens per expert, excess to a fallback path) an expert
+//               keeps its first `capacity` entries in flat order; the rest
+//               get flat_to_row = -1 and are listed in `overflow`.
 //   3. scatter  row = offsets[e] + block prefix + rank -> perm_src /
 //               flat_to_row; then the
 //               row copy: every source row is read once and stored to its k
@@ -70,12 +75,40 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t *__restric
 // 16 loads are independent, so they are in flight together) and leaves the
 // exclusive prefix over blocks in place; the exclusive prefix over experts
 // becomes offsets.  The scatter adds the two.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_shared, int nblk,
-                                                         int32_t *__restrict__ blk,
-                                                         int32_t *__restrict__ counts,
-                                                         int32_t *__restrict__ offsets) {
-  __shared__ int s_wave[16];
+// Exclusive prefix over the 1024 threads of v (fixed combination order);
+// every thread gets its own prefix, and *total receives the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int *s_wave, int *total) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) s_wave[wv] = incl;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wv) base += s_wave[w];
+    all += s_wave[w];
+  }
+  __syncthreads();  // s_wave is reused by the next scan
+  *total = all;
+  return base + incl - v;
+}
+
+// Each expert keeps at most `cap` rows (cap = INT_MAX: drop-less).
+// offsets = exclusive prefix of the kept counts; ovf_start = exclusive
+// prefix of the dropped counts (where each expert's dropped entries start
+// in the overflow list); *n_overflow (if given) = all dropped entries.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_shared, int nblk,
+                                                         int cap, int32_t *__restrict__ blk,
+                                                         int32_t *__restrict__ counts,
+                                                         int32_t *__restrict__ offsets,
+                                                         int32_t *__restrict__ ovf_start,
+                                                         int32_t *__restrict__ n_overflow) {
+  __shared__ int s_wave[16];
+  const int tid = threadIdx.x;
   int total = 0;
   if (tid < E) {
     for (int b0 = 0; b0 < nblk; b0 += 16) {
@@ -90,23 +123,18 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_sha
     }
     counts[tid] = total;
   }
-  // exclusive prefix over experts (wave scan + wave totals)
-  int incl = total;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
+  const int kept = min(total, cap);
+  int routed, dropped;
+  const int excl = block_excl_scan(kept, s_wave, &routed);
+  const int oexcl = block_excl_scan(total - kept, s_wave, &dropped);
+  if (tid < E) {
+    offsets[tid] = excl;
+    ovf_start[tid] = oexcl;
   }
-  if (lane == kWave - 1) s_wave[wv] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wv; ++w) base += s_wave[w];
-  const int excl = base + incl - total;
-  if (tid < E) offsets[tid] = excl;
-  if (tid == E - 1) {
-    const int routed = excl + total;
+  if (tid == 0) {
     offsets[E] = routed;
     for (int s = 0; s < n_shared; ++s) offsets[E + s + 1] = routed + (s + 1) * T;
+    if (n_overflow) *n_overflow = dropped;
   }
 }
 
@@ -116,7 +144,8 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
     const void *__restrict__ xv, int T, int d, const int32_t *__restrict__ idx, int k, int E,
     int n_shared, int tpb, const int32_t *__restrict__ blk_base,
     const int32_t *__restrict__ offsets, int32_t *__restrict__ perm_src,
-    int32_t *__restrict__ flat_to_row, void *__restrict__ x_perm, float *__restrict__ x_scale) {
+    int32_t *__restrict__ flat_to_row, void *__restrict__ x_perm, float *__restrict__ x_scale,
+    int cap, const int32_t *__restrict__ ovf_start, int32_t *__restrict__ overflow) {
   extern __shared__ int s_row[];  // [tpb * k]
   const int t0 = blockIdx.x * tpb;
   const int t1 = min(t0 + tpb, T);
@@ -135,8 +164,13 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
     int row = -1;
     if (e >= 0 && e < E) {
       const int t = (int)(f / k);
-      row = offsets[e] + blk_base[(size_t)(t / kBlk) * E + e] + flat_to_row[f];
-      perm_src[row] = (int32_t)f;
+      const int r = blk_base[(size_t)(t / kBlk) * E + e] + flat_to_row[f];  // rank in expert
+      if (r < cap) {
+        row = offsets[e] + r;
+        perm_src[row] = (int32_t)f;
+      } else if (overflow) {
+        overflow[ovf_start[e] + (r - cap)] = (int32_t)f;
+      }
     }
     flat_to_row[f] = row;
     s_row[i] = row;
@@ -226,47 +260,43 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
 
 size_t permute_ws_bytes(int T, int k, int E) {
   (void)k;
+  if (T <= 0) return 0;
   const size_t nblk = ((size_t)T + kBlk - 1) / kBlk;
-  return nblk * (size_t)E * sizeof(int32_t);
+  return (nblk + 1) * (size_t)E * sizeof(int32_t);  // block counts, then overflow starts
 }
 
 hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *topk_idx, int k,
-                          int E, int n_shared, int out_dt, void *x_perm, float *x_perm_scale,
-                          int32_t *counts, int32_t *offsets, int32_t *perm_src,
-                          int32_t *flat_to_row, void *ws, hipStream_t s) {
+                          int E, int n_shared, int capacity, int out_dt, void *x_perm,
+                          float *x_perm_scale, int32_t *counts, int32_t *offsets,
+                          int32_t *perm_src, int32_t *flat_to_row, int32_t *overflow,
+                          int32_t *n_overflow, void *ws, hipStream_t s) {
   const int nblk = (T + kBlk - 1) / kBlk;
   int32_t *blk = static_cast<int32_t *>(ws);
+  int32_t *ovf_start = blk + (size_t)nblk * E;
   hipLaunchKernelGGL(perm_rank_kernel, dim3((nblk + 3) / 4), dim3(256),
                      sizeof(unsigned long long) * 4 * (size_t)E, s, topk_idx, T, k, E, nblk, blk,
                      flat_to_row);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, T, E, n_shared, nblk, blk,
-                     counts, offsets);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, T, E, n_shared, nblk, capacity,
+                     blk, counts, offsets, ovf_start, n_overflow);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int tpb = T >= 4096 ? 16 : (T >= 1024 ? 4 : 1);
   const dim3 grid((T + tpb - 1) / tpb), block(256);
   const size_t lds = sizeof(int) * (size_t)tpb * k;
   const bool quant = out_dt == MOE_E4M3;
+#define MOE_SCATTER(ES, Q)                                                                  \
+  hipLaunchKernelGGL((perm_scatter_kernel<ES, Q>), grid, block, lds, s, x, T, d, topk_idx, k, E, \
+                     n_shared, tpb, blk, offsets, perm_src, flat_to_row, x_perm, x_perm_scale,  \
+                     capacity, ovf_start, overflow)
   if (x_dt == MOE_BF16) {
-    if (quant)
-      hipLaunchKernelGGL((perm_scatter_kernel<2, true>), grid, block, lds, s, x, T, d, topk_idx,
-                         k, E, n_shared, tpb, blk, offsets, perm_src, flat_to_row, x_perm,
-                         x_perm_scale);
-    else
-      hipLaunchKernelGGL((perm_scatter_kernel<2, false>), grid, block, lds, s, x, T, d, topk_idx,
-                         k, E, n_shared, tpb, blk, offsets, perm_src, flat_to_row, x_perm,
-                         x_perm_scale);
+    if (quant) MOE_SCATTER(2, true);
+    else MOE_SCATTER(2, false);
   } else {
-    if (quant)
-      hipLaunchKernelGGL((perm_scatter_kernel<4, true>), grid, block, lds, s, x, T, d, topk_idx,
-                         k, E, n_shared, tpb, blk, offsets, perm_src, flat_to_row, x_perm,
-                         x_perm_scale);
-    else
-      hipLaunchKernelGGL((perm_scatter_kernel<4, false>), grid, block, lds, s, x, T, d, topk_idx,
-                         k, E, n_shared, tpb, blk, offsets, perm_src, flat_to_row, x_perm,
-                         x_perm_scale);
+    if (quant) MOE_SCATTER(4, true);
+    else MOE_SCATTER(4, false);
   }
+#undef MOE_SCATTER
   return hipGetLastError();
 }

@@ -27,7 +27,7 @@ class MoELayer:
     """
 
     def __init__(self, w_router, w_gate, w_up, w_down, k, *, n_shared=0, bias=None, fp8=False,
-                 renorm=False, keep_logits=True):
+                 renorm=False, keep_logits=True, capacity_factor=None):
         self.E, self.d = w_router.shape
         self.G, self.dff, d2 = w_gate.shape
         assert d2 == self.d and self.G == self.E + n_shared
@@ -37,6 +37,9 @@ class MoELayer:
         self.bias = None if bias is None else bias.to(torch.float32).contiguous()
         self.flags = api.MOE_ROUTE_RENORM if renorm else 0
         self.keep_logits = keep_logits
+        # capacity factor cf: each expert keeps at most ceil(cf * T * k / E)
+        # routed rows (1.0 = a perfectly even share); None = drop-less
+        self.capacity_factor = capacity_factor
         self.act_dtype = w_router.dtype
         self.device = w_router.device
         if fp8:
@@ -57,6 +60,12 @@ class MoELayer:
                              s.view(G * R // 128, Cn // 128), block_rows=128, block_cols=128)
         return q, s
 
+    def capacity(self, T: int):
+        """Rows per expert under the capacity factor (None when drop-less)."""
+        if self.capacity_factor is None:
+            return None
+        return int(-(-self.capacity_factor * T * self.k // self.E))
+
     @property
     def out_dtype(self):
         return torch.bfloat16 if self.fp8 else self.act_dtype
@@ -75,6 +84,9 @@ class MoELayer:
         self.offsets = torch.empty((G + 1,), dtype=i32, device=dev)
         self.perm_src = torch.empty((T * k,), dtype=i32, device=dev)
         self.flat_to_row = torch.empty((T * k + ns * T,), dtype=i32, device=dev)
+        if self.capacity_factor is not None:
+            self.overflow = torch.empty((T * k,), dtype=i32, device=dev)
+            self.n_overflow = torch.empty((1,), dtype=i32, device=dev)
         # route and permute run one after the other on one stream, so they
         # share one workspace
         ws = max(api.moe_permute_workspace_size(T, k, E),
@@ -103,10 +115,7 @@ class MoELayer:
         s = [("route", lambda: api.moe_route(x, self.w_router, self.topk_idx, self.topk_w,
                                              logits=self.logits, logit_bias=self.bias,
                                              flags=self.flags, ws=self.ws)),
-             ("permute", lambda: api.moe_permute(x, self.topk_idx, E, ns, self.x_perm,
-                                                 self.counts, self.offsets, self.perm_src,
-                                                 self.flat_to_row, self.ws,
-                                                 x_perm_scale=self.x_scale))]
+             ("permute", self._permute_fn(x))]
         if self.fp8:
             s.append(("gemm_gate_up", lambda: api.moe_grouped_gemm_fp8(
                 self.x_perm, self.x_scale, self.wg_q, self.wg_s, self.h, self.offsets,
@@ -123,6 +132,39 @@ class MoELayer:
         s.append(("combine", lambda: api.moe_combine(self.y, self.flat_to_row, self.topk_w, out,
                                                      n_shared=ns)))
         return s
+
+    def _permute_fn(self, x):
+        E, ns = self.E, self.n_shared
+        cap = self.capacity(x.shape[0])
+        if cap is None:
+            return lambda: api.moe_permute(x, self.topk_idx, E, ns, self.x_perm, self.counts,
+                                           self.offsets, self.perm_src, self.flat_to_row, self.ws,
+                                           x_perm_scale=self.x_scale)
+        return lambda: api.moe_permute_capped(x, self.topk_idx, E, ns, cap, self.x_perm,
+                                              self.counts, self.offsets, self.perm_src,
+                                              self.flat_to_row, self.ws, overflow=self.overflow,
+                                              n_overflow=self.n_overflow,
+                                              x_perm_scale=self.x_scale)
+
+    def router_stats(self, alpha: float = 0.01):
+        """Load-balance statistics of the last forward (needs keep_logits):
+        f [E], P [E] and summary [3] = (aux loss, max/mean, entropy bits),
+        as device tensors, enqueued on the current stream."""
+        if self.logits is None:
+            raise RuntimeError("router_stats needs the logits: build the layer with "
+                               "keep_logits=True")
+        T = self.logits.shape[0]
+        f = torch.empty((self.E,), dtype=torch.float32, device=self.device)
+        P = torch.empty_like(f)
+        summary = torch.empty((3,), dtype=torch.float32, device=self.device)
+        if getattr(self, "_stats_ws", None) is None or self._stats_ws_T != T:
+            self._stats_ws = torch.empty((max(api.moe_router_stats_workspace_size(T, self.E), 4),),
+                                         dtype=torch.uint8, device=self.device)
+            self._stats_ws_T = T
+        api.moe_router_stats(self.logits, self.counts, self.k, alpha, f, P, summary,
+                             ws=self._stats_ws)
+        return {"f": f, "P": P, "aux_loss": summary[0], "max_over_mean": summary[1],
+                "entropy_bits": summary[2]}
 
     def forward(self, x, out=None):
         T, d = x.shape

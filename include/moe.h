@@ -161,6 +161,55 @@ moe_status_t moe_permute(const void *x, moe_dtype_t x_dt, int T, int d,
                          moe_stream_t stream);
 
 /*
+ * moe_permute with a per-expert capacity ("Dense GEMM to TP MoE" §5.1: at
+ * inference a capacity factor caps the tokens each expert takes and the
+ * excess goes to a fallback path; "DeepSeek MoE evolution" §3.2).
+ * Expert e keeps its first `capacity` routed entries in flat order
+ * f = t*k + j (the ones a stable sort puts first) and drops the rest:
+ *   counts[e]     = routed entries of expert e (before the cap)
+ *   offsets       = exclusive prefix of min(counts[e], capacity), then the
+ *                   n_shared groups of T rows (rows stay compact)
+ *   flat_to_row[f] = -1 for a dropped entry (moe_combine skips it, so the
+ *                   token gets only its kept experts and the shared ones)
+ *   overflow      = the dropped flat indices, expert by expert (ascending f
+ *                   within an expert), [T*k] capacity, or NULL
+ *   *n_overflow   = number of dropped entries, or NULL
+ * Everything else as moe_permute (same workspace).  capacity >= 0; a
+ * capacity of at least T gives exactly moe_permute's result.
+ */
+moe_status_t moe_permute_capped(const void *x, moe_dtype_t x_dt, int T, int d,
+                                const int32_t *topk_idx, int k, int E, int n_shared,
+                                int capacity, moe_dtype_t out_dt, void *x_perm,
+                                float *x_perm_scale, int32_t *counts, int32_t *offsets,
+                                int32_t *perm_src, int32_t *flat_to_row, int32_t *overflow,
+                                int32_t *n_overflow, void *ws, size_t ws_bytes,
+                                moe_stream_t stream);
+
+/* Bytes of device workspace moe_router_stats needs ((T/64 rounded up) x E
+ * floats). */
+size_t moe_router_stats_workspace_size(int T, int E);
+
+/*
+ * Load-balance statistics of one routing decision, forward only.
+ *   P[e] = (1/T) sum_t softmax(logits[t][.])[e]   mean gate probability [E]
+ *   f[e] = counts[e] / (T*k)                      share of routed entries [E]
+ *   summary[0] = alpha * E * sum_e f[e] P[e]       aux load-balance loss
+ *                ("DeepGEMM walkthrough" §2.2)
+ *   summary[1] = max_e counts[e] / mean_e counts[e]
+ *                ("Dense GEMM to TP MoE" §5.1: above 3 is severe)
+ *   summary[2] = -sum_e q[e] log2(q[e] + 1e-8), q = counts / sum counts
+ *                (routing entropy in bits, "DeepSeek MoE evolution" §2.3)
+ * logits [T][E] fp32 (moe_route's output), counts [E] int32 (moe_permute's),
+ * all fp32 outputs on the device.  Softmax as in moe_route (max-subtracted
+ * fp32); sums in a fixed order (deterministic).  Counts are exact up to
+ * 2^24 in the fp32 arithmetic.  ws must hold
+ * moe_router_stats_workspace_size(T, E) bytes (else MOE_ERR_WORKSPACE).
+ */
+moe_status_t moe_router_stats(const float *logits, const int32_t *counts, int T, int E,
+                              int k, float alpha, float *f, float *P, float *summary,
+                              void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
  * Grouped GEMM over ragged groups in one launch ("DeepGEMM walkthrough"
  * §4.3; "Dense GEMM to TP MoE" §2.1, §2.3).  Group g owns rows
  * offsets[g] .. offsets[g+1]-1 of A (device array, read by the kernel's own

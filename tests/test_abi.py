@@ -41,6 +41,11 @@ def lib():
                                        i32, i32, vp]
     L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp]
     L.moe_quantize_fp8.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.moe_permute_capped.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, i32, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_router_stats_workspace_size.restype = sz
+    L.moe_router_stats_workspace_size.argtypes = [i32, i32]
+    L.moe_router_stats.argtypes = [vp, vp, i32, i32, i32, C.c_float, vp, vp, vp, vp, sz, vp]
     L.moe_status_string.restype = C.c_char_p
     L.moe_status_string.argtypes = [i32]
     return L
@@ -54,7 +59,7 @@ NUL = C.c_void_p(0)
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), "libmoe.so does not export %s" % n
 
@@ -62,7 +67,7 @@ def test_every_declared_function_is_exported(lib):
 def test_status_strings_and_version(lib):
     for s in range(5):
         assert lib.moe_status_string(s)
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def test_route_validation(lib):
@@ -159,3 +164,24 @@ def test_combine_and_quant_validation(lib):
     assert q(256, 200, 1, 128, F32) == UNSUPPORTED
     assert q(256, 256, 128, 128, E4M3) == UNSUPPORTED
     assert q(0, 256, 128, 128, F32) == OK
+
+
+def test_permute_capped_validation(lib):
+    need = lib.moe_permute_workspace_size(1000, 2, 8)
+    c = lambda cap, ov, wsb: lib.moe_permute_capped(  # noqa: E731
+        P, BF16, 1000, 64, P, 2, 8, 0, cap, BF16, P, NUL, P, P, P, P, ov, NUL, P2, wsb, NUL)
+    assert c(-1, NUL, need) == INVALID          # negative capacity
+    assert c(10, MIS, need) == INVALID          # misaligned overflow list
+    assert c(10, NUL, need - 1) == WORKSPACE
+    assert lib.moe_permute_capped(P, BF16, 0, 64, P, 2, 8, 0, 5, BF16, P, NUL, P, P, P, P, NUL,
+                                  NUL, NUL, 0, NUL) == OK   # T == 0
+
+
+def test_router_stats_validation(lib):
+    need = lib.moe_router_stats_workspace_size(4096, 256)
+    assert need == 64 * 256 * 4
+    s = lambda T, E, k, wsb: lib.moe_router_stats(P, P, T, E, k, 0.01, P, P, P, P2, wsb, NUL)  # noqa: E731
+    assert s(4096, 256, 0, need) == INVALID     # k < 1
+    assert s(4096, 2000, 8, 1 << 30) == UNSUPPORTED
+    assert s(4096, 256, 8, need - 1) == WORKSPACE
+    assert lib.moe_router_stats(P, P, 0, 256, 8, 0.01, P, P, P, NUL, 0, NUL) == OK

@@ -25,14 +25,14 @@ from test_gpu_route import check_selection
 pytestmark = pytest.mark.gpu
 
 
-def build_layer(cfg, renorm=False):
+def build_layer(cfg, renorm=False, capacity_factor=None):
     from grouped_gemm_router_amd.layer import MoELayer
     x = synth.gen_x(cfg, DEV)
     wr = synth.gen_router(cfg, DEV)
     bias = synth.gen_bias(cfg, DEV)
     wg, wu, wd = synth.gen_experts(cfg, DEV)
     layer = MoELayer(wr, wg, wu, wd, cfg.k, n_shared=cfg.n_shared, bias=bias,
-                     fp8=cfg.dtype == "fp8", renorm=renorm)
+                     fp8=cfg.dtype == "fp8", renorm=renorm, capacity_factor=capacity_factor)
     return layer, x, wr, bias, (wg, wu, wd)
 
 
@@ -127,3 +127,51 @@ def test_layer_is_deterministic():
     o1 = layer(x).clone()
     o2 = layer(x).clone()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("cfg_name,cf", [("skew_bf16", 0.5), ("skew_bf16", 1.25),
+                                         ("deepseek_bf16", 1.0)])
+def test_layer_with_capacity_factor(orc, cfg_name, cf):
+    """Each expert keeps ceil(cf T k / E) rows (first in flat order); a
+    dropped (token, expert) pair contributes nothing.  The oracle output is
+    the token loop with the dropped pairs' weights set to zero, the drop
+    pattern taken from the oracle's capacity permutation of the selection
+    (whose flat_to_row must equal the GPU's exactly)."""
+    base = synth.CONFIGS[cfg_name]
+    if cfg_name == "skew_bf16":
+        cfg = synth.scaled(base, name="cap", T=512, d=512, dff=1024)
+    else:
+        cfg = synth.scaled(base, name="cap_ds", T=300, d=512, dff=256, E=64, k=6)
+    layer, x, wr, bias, weights = build_layer(cfg, capacity_factor=cf)
+    out = layer(x)
+    torch.cuda.synchronize()
+    cap = layer.capacity(cfg.T)
+    gidx = layer.topk_idx.cpu().numpy()
+    tokens = np.arange(cfg.T)
+    ref_all, ridx, rw, lg, _ = oracle_layer_for(orc, cfg, x, wr, bias, weights, tokens)
+    same = (gidx == ridx).all(axis=1)
+    assert same.mean() >= 0.9
+    _, _, _, f2r, ov = orc.capacity_permutation(gidx, cfg.E, cap, cfg.n_shared)
+    kept = (f2r[: cfg.T * cfg.k] >= 0).reshape(cfg.T, cfg.k)
+    n_drop = int(layer.n_overflow.cpu()[0])
+    assert n_drop == len(ov)
+    if cf < 1.0:
+        assert n_drop > 0
+    np.testing.assert_array_equal(layer.flat_to_row.cpu().numpy(), f2r)
+    # oracle layer with the dropped pairs zero-weighted
+    wg, wu, wd = weights
+    G = cfg.G
+    need = set(np.unique(gidx).tolist()) | set(range(cfg.E, G))
+    lists = {n: [None] * G for n in ("g", "u", "d")}
+    for g in sorted(need):
+        lists["g"][g], lists["u"][g], lists["d"][g] = np_of(wg[g]), np_of(wu[g]), np_of(wd[g])
+    L = orc.Layer(np_of(x), cfg.E, cfg.k, cfg.n_shared, lists["g"], lists["u"], lists["d"])
+    ref = L.tokens(gidx, np.where(kept, rw, 0.0), tokens)
+    got = out.float().cpu().numpy()
+    # Dropping zeroes terms, it does not change the arithmetic of the kept
+    # ones: the error scale is that of the drop-less layer, so the bf16 bar
+    # (2e-2 x RMS) is taken on the drop-less reference output (the capped
+    # output's own RMS shrinks with every dropped pair).
+    scale = rms(L.tokens(gidx, rw, tokens)[same])
+    err = np.abs(got[same] - ref[same]).max()
+    assert err <= 2e-2 * scale, "capped layer: max err %.3e vs 2e-2 x RMS %.3e" % (err, scale)

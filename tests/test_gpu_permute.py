@@ -139,3 +139,79 @@ def test_permute_is_deterministic():
     for u, v in zip(r1, r2):
         if u is not None:
             assert torch.equal(u, v)
+
+
+def run_permute_capped(x, idx, E, ns, cap, fp8=False):
+    a = api()
+    T, d = x.shape
+    k = idx.shape[1]
+    rows = T * k + ns * T
+    x_perm = torch.full((rows, d), 0, dtype=torch.uint8 if fp8 else x.dtype, device=DEV)
+    scale = torch.zeros((d // 128, rows), dtype=torch.float32, device=DEV) if fp8 else None
+    counts = torch.empty((E,), dtype=torch.int32, device=DEV)
+    offsets = torch.empty((E + ns + 1,), dtype=torch.int32, device=DEV)
+    perm_src = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    f2r = torch.empty((T * k + ns * T,), dtype=torch.int32, device=DEV)
+    overflow = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    n_over = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty((max(a.moe_permute_workspace_size(T, k, E), 16),), dtype=torch.uint8,
+                     device=DEV)
+    a.moe_permute_capped(x, idx, E, ns, cap, x_perm, counts, offsets, perm_src, f2r, ws,
+                         overflow=overflow, n_overflow=n_over, x_perm_scale=scale)
+    torch.cuda.synchronize()
+    if fp8:
+        scale = scale.t().contiguous()
+    return x_perm, scale, counts, offsets, perm_src, f2r, overflow, n_over
+
+
+CAPPED = [  # T, E, k, ns, d, kind, capacity
+    (300, 8, 2, 0, 128, "skew", 40),
+    (300, 8, 2, 1, 128, None, 75),
+    (4096, 8, 2, 0, 64, "skew", 1024),        # capacity factor 1.0 at T*k/E = 1024
+    (1000, 256, 8, 1, 128, None, 20),
+    (777, 16, 16, 0, 64, None, 0),            # everything routed is dropped
+    (130, 32, 2, 2, 64, "empty", 5),
+    (200, 8, 2, 0, 64, None, 200),            # cap >= T: the drop-less result
+]
+
+
+@pytest.mark.parametrize("T,E,k,ns,d,kind,cap", CAPPED)
+def test_permute_capped_bit_exact(orc, T, E, k, ns, d, kind, cap):
+    x = synth.randn((T, d), 1.0, 61 + T, DEV, torch.bfloat16)
+    idx_cpu = synth.random_selection(T, E, k, s=71 + T + E, weights=weights_for(kind, E))
+    x_perm, _, counts, offsets, perm_src, f2r, overflow, n_over = run_permute_capped(
+        x, idx_cpu.to(DEV), E, ns, cap)
+    rc, ro, rp, rf, rov = orc.capacity_permutation(idx_cpu.numpy(), E, cap, ns)
+    np.testing.assert_array_equal(counts.cpu().numpy(), rc)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), ro)
+    n_kept = int(ro[E])
+    ps = perm_src.cpu().numpy()
+    np.testing.assert_array_equal(ps[:n_kept], rp)
+    assert (ps[n_kept:] == -7).all()              # nothing written past the kept rows
+    np.testing.assert_array_equal(f2r.cpu().numpy(), rf)
+    assert int(n_over.cpu()[0]) == len(rov)
+    ov = overflow.cpu().numpy()
+    np.testing.assert_array_equal(ov[:len(rov)], rov)
+    assert (ov[len(rov):] == -7).all()
+    # kept rows and shared rows hold their tokens, bit for bit
+    src = np.concatenate([rp // k, np.tile(np.arange(T), ns)])
+    xp = np_of(x_perm)
+    np.testing.assert_array_equal(xp[: n_kept + ns * T], np_of(x)[src])
+    if cap >= T:
+        # the drop-less entry point gives the same rows
+        dp, _, _, doff, dps, df2r = run_permute(x, idx_cpu.to(DEV), E, ns)
+        np.testing.assert_array_equal(doff.cpu().numpy(), ro)
+        np.testing.assert_array_equal(np_of(dp), xp)
+
+
+def test_permute_capped_fp8_rows(orc):
+    T, E, k, ns, d, cap = 500, 16, 4, 1, 256, 60
+    x = synth.randn((T, d), 2.0, 81, DEV, torch.bfloat16)
+    idx_cpu = synth.random_selection(T, E, k, s=82, weights=weights_for("skew", E))
+    x_perm, scale, *_ = run_permute_capped(x, idx_cpu.to(DEV), E, ns, cap, fp8=True)
+    _, ro, rp, _, _ = orc.capacity_permutation(idx_cpu.numpy(), E, cap, ns)
+    qref, sref = orc.quant_blocks(x.float().cpu().numpy(), 1, 128)
+    src = np.concatenate([rp // k, np.tile(np.arange(T), ns)])
+    n = int(ro[E]) + ns * T
+    np.testing.assert_array_equal(x_perm.cpu().numpy()[:n], qref[src])
+    np.testing.assert_array_equal(scale.cpu().numpy()[:n], sref[src])
