@@ -6,9 +6,10 @@
 // expert is added with weight one.
 //
 // One workgroup per token.  Each thread owns 8 consecutive columns (one
-// 16-byte bf16 piece, two for fp32): it issues all k + n_shared row loads,
-// then accumulates in fp32 in ascending j with fused multiply-adds, then the
-// shared rows, and stores once.  HBM traffic is one read of every used Y row
+// 16-byte bf16 piece, two for fp32): it issues the row loads of four terms
+// at a time, accumulates in fp32 in ascending j with fused multiply-adds
+// (the shared rows last, weight one), and stores once.  HBM traffic is one
+// read of every used Y row
 // and one write of out.
 #include "moe_internal.h"
 
@@ -63,18 +64,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ Y
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < nterm; ++j) {
-      const int row = s_row[j];
-      if (row < 0 || row >= nrows) continue;  // dropped entry (or bad index)
-      float v[8];
-      load8<YSIZE>(Y, (size_t)row * d + (size_t)p * 8, v);
-      if (j < k) {
-        const float w = s_w[j];
+    // terms in groups of 4: the group's row loads are all issued before the
+    // first one is used; accumulation stays in ascending j
+    for (int j0 = 0; j0 < nterm; j0 += 4) {
+      float v[4][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
-      } else {
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + q;
+        const int row = j < nterm ? s_row[j] : -1;
+        if (row >= 0 && row < nrows) {  // else: dropped entry (or bad index)
+          load8<YSIZE>(Y, (size_t)row * d + (size_t)p * 8, v[q]);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+          for (int i = 0; i < 8; ++i) v[q][i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + q;
+        if (j >= nterm) break;
+        const int row = s_row[j];
+        if (row < 0 || row >= nrows) continue;
+        if (j < k) {
+          const float w = s_w[j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[q][i], acc[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += v[q][i];
+        }
       }
     }
     if (OSIZE == 2) {

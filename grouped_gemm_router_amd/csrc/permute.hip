@@ -282,7 +282,7 @@ hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *
                      blk, counts, offsets, ovf_start, n_overflow);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int tpb = T >= 4096 ? 16 : (T >= 1024 ? 4 : 1);
+  const int tpb = T >= 1024 ? 4 : 1;  // tokens per scatter workgroup
   const dim3 grid((T + tpb - 1) / tpb), block(256);
   const size_t lds = sizeof(int) * (size_t)tpb * k;
   const bool quant = out_dt == MOE_E4M3;
