@@ -9,8 +9,7 @@
 // 16-byte bf16 piece, two for fp32): it issues the row loads of four terms
 // at a time, accumulates in fp32 in ascending j with fused multiply-adds
 // (the shared rows last, weight one), and stores once.  HBM traffic is one
-// read of every used Y row
-// and one write of out.
+// read of every used Y row and one write of out.
 #include "moe_internal.h"
 
 namespace {
