@@ -19,12 +19,13 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH 
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_ROUTE_RENORM, MOE_ROUTE_FROM_LOGITS = 1, 2
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTS = ["moe_status_string", "moe_abi_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute_capped", "moe_router_stats_workspace_size",
            "moe_router_stats",
-           "moe_permute", "moe_grouped_gemm", "moe_grouped_gemm_fp8", "moe_combine",
+           "moe_permute", "moe_grouped_gemm_workspace_size", "moe_grouped_gemm",
+           "moe_grouped_gemm_fp8", "moe_combine",
            "moe_quantize_fp8"]
 
 
@@ -60,8 +61,11 @@ def _load():
     lib.moe_router_stats_workspace_size.argtypes = [i32, i32]
     lib.moe_router_stats.restype = i32
     lib.moe_router_stats.argtypes = [vp, vp, i32, i32, i32, C.c_float, vp, vp, vp, vp, sz, vp]
+    lib.moe_grouped_gemm_workspace_size.restype = sz
+    lib.moe_grouped_gemm_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.moe_grouped_gemm.restype = i32
-    lib.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, vp]
+    lib.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, vp, sz,
+                                     vp]
     lib.moe_grouped_gemm_fp8.restype = i32
     lib.moe_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
                                          i32, i32, vp]
@@ -200,17 +204,28 @@ def moe_router_stats(logits, counts, k, alpha, f, P, summary, *, ws=None, stream
                                 _ptr(P), _ptr(summary), _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def moe_grouped_gemm(A, B, C_out, offsets, *, B2=None, epi=MOE_EPI_NONE, stream=None):
-    """C[r] = A[r] B[g]^T for rows r of group g (offsets on the device)."""
+def moe_grouped_gemm_workspace_size(G: int, rows: int, N: int, K: int, dtype, epi: int) -> int:
+    """Bytes of the tail-split workspace moe_grouped_gemm may use on the
+    current device (0: this shape never splits)."""
+    dt = dtype if isinstance(dtype, int) else _dt(torch.empty(0, dtype=dtype))
+    return int(lib.moe_grouped_gemm_workspace_size(G, rows, N, K, dt, epi))
+
+
+def moe_grouped_gemm(A, B, C_out, offsets, *, B2=None, epi=MOE_EPI_NONE, ws=None, stream=None):
+    """C[r] = A[r] B[g]^T for rows r of group g (offsets on the device).
+    ws: moe_grouped_gemm_workspace_size bytes of device scratch that lets the
+    last, partial round of tiles be cut along K; None runs without it."""
     rows, K = A.shape
     G, N, K2 = B.shape
     if K2 != K:
         raise ValueError("A is [rows][%d] but B is [G][N][%d]" % (K, K2))
     if offsets.numel() != G + 1:
         raise ValueError("offsets must have G + 1 = %d entries" % (G + 1))
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_grouped_gemm", lib.moe_grouped_gemm(_ptr(A), _ptr(B), _ptr(B2), _dt(A),
                                                     _ptr(C_out), _dt(C_out), _ptr(offsets), G,
-                                                    rows, N, K, epi, _stream(stream)))
+                                                    rows, N, K, epi, _ptr(ws), ws_bytes,
+                                                    _stream(stream)))
 
 
 def moe_grouped_gemm_fp8(A_q, A_scale, B_q, B_scale, C_out, offsets, *, B2_q=None,

@@ -33,7 +33,12 @@
 //     of expert sizes); tiles are taken in an order that keeps all XCDs on
 //     one expert at a time (see tile_of_workgroup);
 //   * ragged tails: A rows past the group end are loaded (clamped to the
-//     buffer) and multiplied but never stored.
+//     buffer) and multiplied but never stored;
+//   * the last, partial round of tiles (fewer tiles than half the CUs) is
+//     cut along K into S slices when a workspace is given: each slice writes
+//     an fp32 partial tile to the workspace and a second small kernel adds the
+//     S partials in slice order (deterministic) and applies the epilogue, so
+//     the chip is not three-quarters idle for the last tile's duration.
 #include "moe_internal.h"
 
 namespace {
@@ -123,13 +128,40 @@ __device__ __forceinline__ void interleave_mfma_ds_read() {
   __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
 }
 
+// Split of the tail: workspace layout and plan.  The workspace holds a
+// header (n_split, S), the position of every split tile, then the fp32
+// partial tiles [split tile][slice][BM_MAX][BN] (B-tile column order).
+constexpr int kSplitMax = 8;         // slices per tile at most
+constexpr int kSplitMinSteps = 32;   // K steps per slice at least (K/S >= 1024)
+constexpr size_t kPartialFloats = (size_t)BM_MAX * BN;
+
+__host__ __device__ inline size_t split_desc_offset() { return 64; }
+__host__ __device__ inline size_t split_partial_offset(int cus) {
+  return (split_desc_offset() + 16 * (size_t)cus + 255) / 256 * 256;
+}
+
+// Slices per tail tile: 1 (no split) unless the last round holds at most
+// half as many tiles as there are CUs; then the largest S <= kSplitMax with
+// S * rem <= cus, KT a multiple of 4 S (the ring's 4-stage unroll) and at
+// least kSplitMinSteps steps per slice.
+__host__ __device__ inline int split_slices(int total, int cus, int KT) {
+  const int rem = total % cus;
+  if (rem == 0 || 2 * rem > cus) return 1;
+  int S = kSplitMax;
+  while (S > 1 && (S * rem > cus || KT % (4 * S) != 0 || KT / S < kSplitMinSteps)) S >>= 1;
+  return S;
+}
+
 // One output tile of height BM (rows [tile.m0, tile.mend), at most BM of
-// them) over the whole K range, through the 4-stage LDS ring.
+// them) over K steps [kbeg/BK, kbeg/BK + KT), through the 4-stage LDS ring.
+// part == nullptr: the epilogue writes C; otherwise the raw fp32 accumulator
+// goes to part[(m - m0) * BN + B-tile row] (a K-slice of a split tile).
 template <int BM, bool SWIGLU, bool OUT_F32, int NW>
 __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__restrict__ A,
                                          const uint16_t *__restrict__ B,
                                          const uint16_t *__restrict__ B2, void *__restrict__ C,
-                                         int rows, int N, int K, u32x4 *sA0, u32x4 *sA1,
+                                         int rows, int N, int K, int kbeg, int KT,
+                                         float *__restrict__ part, u32x4 *sA0, u32x4 *sA1,
                                          u32x4 *sA2, u32x4 *sA3, u32x4 *sB0, u32x4 *sB1,
                                          u32x4 *sB2, u32x4 *sB3) {
   constexpr int NWN = NW / 2;                 // wave columns (2 wave rows)
@@ -155,7 +187,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
   // wave wv fills dwords [(wv*IA + i)*64, +64), dword q belonging to slot q/4.
   const uint16_t *ga[IA];
   const uint16_t *gb[IB];
-  const size_t goff = (size_t)tile.g * N * K;
+  const size_t goff = (size_t)tile.g * N * K + kbeg;
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
     int r, off;
@@ -170,7 +202,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
       off = swz(r, sl % PIECES) * 8;
     }
     const int m = min(tile.m0 + r, rows - 1);
-    ga[i] = A + (size_t)m * K + off;
+    ga[i] = A + (size_t)m * K + kbeg + off;
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
@@ -201,7 +233,6 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
   const int fr = lane & 31, fh = lane >> 5;
-  const int KT = K / BK;  // a multiple of 4
 
   MOE_ISSUE(sA0, sB0, 0);
   MOE_ISSUE(sA1, sB1, BK);
@@ -241,6 +272,19 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
   // epilogue.  32x32 accumulator layout: lane holds column lane%32, and
   // register r holds row 8*(r/4) + 4*(lane/32) + r%4.
   const int col = lane & 31, rbase = 4 * (lane >> 5);
+  if (SWIGLU && part != nullptr) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int mt = wm * (MI * 32) + mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
+          if (tile.m0 + mt < tile.mend)
+            part[(size_t)mt * BN + b_row<SWIGLU, NWN>(wn, nb) + col] = acc[mi][nb][r];
+        }
+    return;
+  }
   if (SWIGLU) {
     constexpr int HB = NB / 2;
 #pragma unroll
@@ -269,12 +313,14 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
         for (int r = 0; r < 16; ++r) {
           const int m = tile.m0 + wm * (MI * 32) + mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
           if (m < tile.mend) {
-            const int n = tile.nt * 256 + wn * (256 / NWN) + nb * 32 + col;
+            const int nn = wn * (256 / NWN) + nb * 32 + col;  // column in the tile
             const float v = acc[mi][nb][r];
-            if (OUT_F32)
-              static_cast<float *>(C)[(size_t)m * N + n] = v;
+            if (part != nullptr)
+              part[(size_t)(m - tile.m0) * BN + nn] = v;
+            else if (OUT_F32)
+              static_cast<float *>(C)[(size_t)m * N + tile.nt * 256 + nn] = v;
             else
-              static_cast<uint16_t *>(C)[(size_t)m * N + n] = f32_to_bf16_bits(v);
+              static_cast<uint16_t *>(C)[(size_t)m * N + tile.nt * 256 + nn] = f32_to_bf16_bits(v);
           }
         }
   }
@@ -285,12 +331,13 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
 // {64, 128, 256} that holds its rows, chosen here from the device offsets,
 // so a group of 40 rows (or the 40-row tail of a 1064-row group) costs a
 // quarter of the matrix-core work and 5/8 of the operand traffic of a full
-// tile.
+// tile.  With a workspace, the last n_split tiles (the partial last round)
+// are taken by S workgroups each, one K-slice apiece.
 template <bool SWIGLU, bool OUT_F32, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const uint16_t *__restrict__ B2, void *__restrict__ C, const int32_t *__restrict__ offsets,
-    int G, int rows, int N, int K, int nt_count) {
+    int G, int rows, int N, int K, int nt_count, char *__restrict__ ws, int cus) {
   __shared__ u32x4 sA0[SLOTS_MAX], sA1[SLOTS_MAX], sA2[SLOTS_MAX], sA3[SLOTS_MAX];
   __shared__ u32x4 sB0[SLOTS_B], sB1[SLOTS_B], sB2[SLOTS_B], sB3[SLOTS_B];
   __shared__ int s_cum[MOE_MAX_GROUPS + 1];
@@ -298,30 +345,106 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
 
   sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_tmp);
   const int total = s_cum[G] * nt_count;
-  const int L = tile_of_workgroup((int)blockIdx.x, total);
-  if (L < 0) return;
+  const int KT = K / BK;  // a multiple of 4
+  const int S = ws != nullptr ? split_slices(total, cus, KT) : 1;
+  const int n_split = S > 1 ? total % cus : 0;
+  const int full_end = total - n_split;
+  const int w = (int)blockIdx.x;
+  if (ws != nullptr && w == 0 && threadIdx.x == 0) {
+    int *hdr = reinterpret_cast<int *>(ws);
+    hdr[0] = n_split;
+    hdr[1] = S;
+  }
+  int L = tile_of_workgroup(w, full_end), kbeg = 0, kt = KT, j = -1, slice = 0;
+  float *part = nullptr;
+  if (L < 0) {  // a K-slice of a split tile, or nothing
+    j = (w - full_end) / S;
+    slice = (w - full_end) - j * S;
+    if (j >= n_split) return;
+    L = full_end + j;
+    kt = KT / S;
+    kbeg = slice * kt * BK;
+    part = reinterpret_cast<float *>(ws + split_partial_offset(cus)) +
+           (size_t)(j * S + slice) * kPartialFloats;
+  }
   const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM_MAX, nt_count, kTileChunk);
+  if (part != nullptr && slice == 0 && threadIdx.x == 0)
+    reinterpret_cast<int4 *>(ws + split_desc_offset())[j] = make_int4(tile.m0, tile.mend, tile.nt, 0);
   const int h = tile.mend - tile.m0;  // wave-uniform
   if (h > 128)
-    run_tile<256, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, sA0, sA1, sA2, sA3, sB0,
-                                       sB1, sB2, sB3);
+    run_tile<256, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, kbeg, kt, part, sA0, sA1,
+                                       sA2, sA3, sB0, sB1, sB2, sB3);
   else if (h > 64)
-    run_tile<128, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, sA0, sA1, sA2, sA3, sB0,
-                                       sB1, sB2, sB3);
+    run_tile<128, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, kbeg, kt, part, sA0, sA1,
+                                       sA2, sA3, sB0, sB1, sB2, sB3);
   else
-    run_tile<64, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, sA0, sA1, sA2, sA3, sB0,
-                                      sB1, sB2, sB3);
+    run_tile<64, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, kbeg, kt, part, sA0, sA1,
+                                      sA2, sA3, sB0, sB1, sB2, sB3);
+}
+
+// Sum of the S partial tiles of each split tile, in slice order, then the
+// epilogue.  Workgroup (j, rb) takes rows [16 rb, 16 rb + 16) of split tile
+// j; a thread handles 4 consecutive B-tile columns (16 bytes per partial).
+constexpr int kReduceRows = 16;
+
+template <bool SWIGLU, bool OUT_F32>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const char *__restrict__ ws,
+                                                           void *__restrict__ C, int N, int cus) {
+  const int *hdr = reinterpret_cast<const int *>(ws);
+  const int n_split = hdr[0], S = hdr[1];
+  constexpr int RB = BM_MAX / kReduceRows;
+  const int j = blockIdx.x / RB, r0 = (blockIdx.x % RB) * kReduceRows;
+  if (j >= n_split) return;
+  const int4 d = reinterpret_cast<const int4 *>(ws + split_desc_offset())[j];
+  const int h = d.y - d.x;
+  if (r0 >= h) return;
+  const float *P = reinterpret_cast<const float *>(ws + split_partial_offset(cus)) +
+                   (size_t)j * S * kPartialFloats;
+  constexpr int C4 = SWIGLU ? BN / 8 : BN / 4;  // 4-column groups per output row
+  for (int idx = threadIdx.x; idx < kReduceRows * C4; idx += 256) {
+    const int r = r0 + idx / C4, c = (idx % C4) * 4;
+    if (r >= h) break;  // idx / C4 only grows
+    const float *p0 = P + (size_t)r * BN + c;
+    float4 g = *reinterpret_cast<const float4 *>(p0);
+    float4 u = SWIGLU ? *reinterpret_cast<const float4 *>(p0 + BN / 2) : float4{};
+    for (int q = 1; q < S; ++q) {
+      const float4 a = *reinterpret_cast<const float4 *>(p0 + q * kPartialFloats);
+      g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+      if (SWIGLU) {
+        const float4 b = *reinterpret_cast<const float4 *>(p0 + q * kPartialFloats + BN / 2);
+        u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+      }
+    }
+    float v[4] = {g.x, g.y, g.z, g.w};
+    if (SWIGLU) {
+      const float uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = v[i] / (1.0f + expf(-v[i])) * uu[i];
+    }
+    const size_t o = (size_t)(d.x + r) * N + (size_t)d.z * (SWIGLU ? BN / 2 : BN) + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (OUT_F32) static_cast<float *>(C)[o + i] = v[i];
+      else static_cast<uint16_t *>(C)[o + i] = f32_to_bf16_bits(v[i]);
+    }
+  }
 }
 
 template <bool SWIGLU, bool OUT_F32, int NW>
 void launch_t(const void *A, const void *B, const void *B2, void *C, const int32_t *offsets,
-              int G, int rows, int N, int K, hipStream_t s) {
+              int G, int rows, int N, int K, char *ws, int cus, hipStream_t s) {
   const int nt = SWIGLU ? N / 128 : N / 256;
-  const long long bound = (long long)host_row_tile_bound(rows, G, BM_MAX) * nt;
+  // slices of split tiles add at most cus - 1 workgroups past the tile count
+  const long long bound = (long long)host_row_tile_bound(rows, G, BM_MAX) * nt + (ws ? cus : 0);
   hipLaunchKernelGGL((gemm_bf16_kernel<SWIGLU, OUT_F32, NW>), dim3((unsigned)((bound + 7) / 8 * 8)),
                      dim3(NW * 64), 0, s, static_cast<const uint16_t *>(A),
                      static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(B2), C,
-                     offsets, G, rows, N, K, nt);
+                     offsets, G, rows, N, K, nt, ws, cus);
+  if (ws == nullptr) return;
+  // at most cus / 2 tiles are split (S >= 2)
+  hipLaunchKernelGGL((split_reduce_kernel<SWIGLU, OUT_F32>),
+                     dim3((unsigned)(cus / 2 * (BM_MAX / kReduceRows))), dim3(256), 0, s, ws, C,
+                     N, cus);
 }
 
 }  // namespace
@@ -331,16 +454,29 @@ bool gemm_bf16_mfma_supports(int N, int K, int epi) {
   return epi == MOE_EPI_SWIGLU ? (N % 128 == 0) : (N % 256 == 0);
 }
 
+size_t gemm_bf16_split_ws_bytes(int G, int rows, int N, int K, int epi, int cus) {
+  if (!gemm_bf16_mfma_supports(N, K, epi) || cus < 2) return 0;
+  const int KT = K / BK;
+  int smax = kSplitMax;
+  while (smax > 1 && (KT % (4 * smax) != 0 || KT / smax < kSplitMinSteps)) smax >>= 1;
+  if (smax < 2) return 0;
+  const int nt = epi == MOE_EPI_SWIGLU ? N / 128 : N / 256;
+  const long long tiles = (long long)host_row_tile_bound(rows, G, BM_MAX) * nt;
+  const long long slices = tiles * smax < cus ? tiles * smax : cus;  // n_split * S <= both
+  return split_partial_offset(cus) + (size_t)slices * kPartialFloats * sizeof(float);
+}
+
 hipError_t launch_gemm_bf16_mfma(const void *A, const void *B, const void *B2, void *C, int c_dt,
                                  const int32_t *offsets, int G, int rows, int N, int K, int epi,
-                                 hipStream_t s) {
+                                 void *ws, int cus, hipStream_t s) {
+  char *w = static_cast<char *>(ws);
   // wave counts measured on the Mixtral shapes: 8 for gate/up, 4 for down
   if (epi == MOE_EPI_SWIGLU) {
-    if (c_dt == MOE_F32) launch_t<true, true, 8>(A, B, B2, C, offsets, G, rows, N, K, s);
-    else launch_t<true, false, 8>(A, B, B2, C, offsets, G, rows, N, K, s);
+    if (c_dt == MOE_F32) launch_t<true, true, 8>(A, B, B2, C, offsets, G, rows, N, K, w, cus, s);
+    else launch_t<true, false, 8>(A, B, B2, C, offsets, G, rows, N, K, w, cus, s);
   } else {
-    if (c_dt == MOE_F32) launch_t<false, true, 4>(A, B, B2, C, offsets, G, rows, N, K, s);
-    else launch_t<false, false, 4>(A, B, B2, C, offsets, G, rows, N, K, s);
+    if (c_dt == MOE_F32) launch_t<false, true, 4>(A, B, B2, C, offsets, G, rows, N, K, w, cus, s);
+    else launch_t<false, false, 4>(A, B, B2, C, offsets, G, rows, N, K, w, cus, s);
   }
   return hipGetLastError();
 }

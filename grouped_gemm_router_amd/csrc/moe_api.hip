@@ -5,11 +5,13 @@
 // allocates, frees, synchronises or reads device memory.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -20,6 +22,25 @@ bool is_act(moe_dtype_t d) { return d == MOE_F32 || d == MOE_BF16; }
 moe_status_t launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
 hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Compute units of the current device (0 if it cannot be queried), cached
+// per device: a host attribute, no device access.
+int current_device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (cached) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 }  // namespace
 
@@ -152,9 +173,17 @@ moe_status_t moe_router_stats(const float *logits, const int32_t *counts, int T,
                                       static_cast<float *>(ws), as_stream(stream)));
 }
 
+size_t moe_grouped_gemm_workspace_size(int G, int rows, int N, int K, moe_dtype_t ab_dt,
+                                       moe_epilogue_t epi) {
+  if (G < 1 || G > MOE_MAX_GROUPS || rows < 0 || N < 1 || K < 1) return 0;
+  if (ab_dt != MOE_BF16 || (epi != MOE_EPI_NONE && epi != MOE_EPI_SWIGLU)) return 0;
+  return gemm_bf16_split_ws_bytes(G, rows, N, K, epi, current_device_cus());
+}
+
 moe_status_t moe_grouped_gemm(const void *A, const void *B, const void *B2, moe_dtype_t ab_dt,
                               void *C, moe_dtype_t c_dt, const int32_t *offsets, int G, int rows,
-                              int N, int K, moe_epilogue_t epi, moe_stream_t stream) {
+                              int N, int K, moe_epilogue_t epi, void *ws, size_t ws_bytes,
+                              moe_stream_t stream) {
   if (G < 1 || rows < 0 || N < 1 || K < 1) return MOE_ERR_INVALID;
   if (G > MOE_MAX_GROUPS) return MOE_ERR_UNSUPPORTED;
   if (epi != MOE_EPI_NONE && epi != MOE_EPI_SWIGLU) return MOE_ERR_INVALID;
@@ -163,10 +192,24 @@ moe_status_t moe_grouped_gemm(const void *A, const void *B, const void *B2, moe_
   if (!aligned16(A) || !aligned16(B) || !aligned4(C) || !aligned4(offsets)) return MOE_ERR_INVALID;
   if (epi == MOE_EPI_SWIGLU ? !aligned16(B2) : B2 != nullptr) return MOE_ERR_INVALID;
   if ((long long)G * N * K >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  if (ws == nullptr && ws_bytes != 0) return MOE_ERR_INVALID;
+  const bool mfma = ab_dt == MOE_BF16 && gemm_bf16_mfma_supports(N, K, epi);
+  void *split_ws = nullptr;
+  int cus = 0;
+  if (ws != nullptr && mfma) {
+    cus = current_device_cus();
+    const size_t need = gemm_bf16_split_ws_bytes(G, rows, N, K, epi, cus);
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (need > 0) {
+      if (!aligned16(ws)) return MOE_ERR_INVALID;
+      split_ws = ws;
+    }
+  }
   if (rows == 0) return MOE_OK;
   const hipStream_t s = as_stream(stream);
-  if (ab_dt == MOE_BF16 && gemm_bf16_mfma_supports(N, K, epi))
-    return launched(launch_gemm_bf16_mfma(A, B, B2, C, c_dt, offsets, G, rows, N, K, epi, s));
+  if (mfma)
+    return launched(launch_gemm_bf16_mfma(A, B, B2, C, c_dt, offsets, G, rows, N, K, epi,
+                                          split_ws, cus, s));
   return launched(launch_gemm_simple(A, B, B2, ab_dt, C, c_dt, offsets, G, rows, N, K, epi, s));
 }
 

@@ -226,10 +226,13 @@ hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *
                           int32_t *perm_src, int32_t *flat_to_row, int32_t *overflow,
                           int32_t *n_overflow, void *ws, hipStream_t s);
 
+// ws: the tail-split workspace of gemm_bf16_split_ws_bytes bytes, or null
+// (no split); cus: compute units of the device the launch runs on
 hipError_t launch_gemm_bf16_mfma(const void *A, const void *B, const void *B2, void *C,
                                  int c_dt, const int32_t *offsets, int G, int rows, int N,
-                                 int K, int epi, hipStream_t s);
+                                 int K, int epi, void *ws, int cus, hipStream_t s);
 bool gemm_bf16_mfma_supports(int N, int K, int epi);
+size_t gemm_bf16_split_ws_bytes(int G, int rows, int N, int K, int epi, int cus);
 
 hipError_t launch_gemm_simple(const void *A, const void *B, const void *B2, int ab_dt,
                               void *C, int c_dt, const int32_t *offsets, int G, int rows,

@@ -87,10 +87,16 @@ class MoELayer:
         if self.capacity_factor is not None:
             self.overflow = torch.empty((T * k,), dtype=i32, device=dev)
             self.n_overflow = torch.empty((1,), dtype=i32, device=dev)
-        # route and permute run one after the other on one stream, so they
-        # share one workspace
+        # route, permute and the two GEMMs run one after the other on one
+        # stream, so they share one workspace
         ws = max(api.moe_permute_workspace_size(T, k, E),
                  api.moe_route_workspace_size(T, self.d, E))
+        if not self.fp8:
+            ws = max(ws,
+                     api.moe_grouped_gemm_workspace_size(G, rows, self.dff, self.d,
+                                                         self.act_dtype, api.MOE_EPI_SWIGLU),
+                     api.moe_grouped_gemm_workspace_size(G, rows, self.d, self.dff,
+                                                         self.act_dtype, api.MOE_EPI_NONE))
         self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
         if self.fp8:
             self.x_perm = torch.empty((rows, self.d), dtype=torch.uint8, device=dev)
@@ -126,9 +132,9 @@ class MoELayer:
         else:
             s.append(("gemm_gate_up", lambda: api.moe_grouped_gemm(
                 self.x_perm, self.w_gate, self.h, self.offsets, B2=self.w_up,
-                epi=api.MOE_EPI_SWIGLU)))
+                epi=api.MOE_EPI_SWIGLU, ws=self.ws)))
             s.append(("gemm_down", lambda: api.moe_grouped_gemm(
-                self.h, self.w_down, self.y, self.offsets)))
+                self.h, self.w_down, self.y, self.offsets, ws=self.ws)))
         s.append(("combine", lambda: api.moe_combine(self.y, self.flat_to_row, self.topk_w, out,
                                                      n_shared=ns)))
         return s

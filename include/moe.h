@@ -223,11 +223,28 @@ moe_status_t moe_router_stats(const float *logits, const int32_t *counts, int T,
  * group are not written.  offsets values are clamped to [0, rows], so a bad
  * offsets array gives wrong results but no out-of-bounds access.
  * Requires K % 8 == 0, 1 <= G <= MOE_MAX_GROUPS.
+ *
+ * ws (device, 16-byte aligned, caller-owned scratch) lets the bf16 path cut
+ * the last, partial round of output tiles along K over the idle compute
+ * units; the K-slices are added in a fixed order by a second kernel, so the
+ * result is deterministic for a given device and offsets (it may differ in
+ * the last bits from the ws == NULL result).  ws == NULL with ws_bytes == 0
+ * runs without the split.  Otherwise ws_bytes must be at least
+ * moe_grouped_gemm_workspace_size(G, rows, N, K, ab_dt, epi) (else
+ * MOE_ERR_WORKSPACE); a size of 0 means the shape never splits and ws is
+ * not touched.  Calls that share one ws must be ordered (same stream).
  */
 moe_status_t moe_grouped_gemm(const void *A, const void *B, const void *B2,
                               moe_dtype_t ab_dt, void *C, moe_dtype_t c_dt,
                               const int32_t *offsets, int G, int rows, int N,
-                              int K, moe_epilogue_t epi, moe_stream_t stream);
+                              int K, moe_epilogue_t epi, void *ws,
+                              size_t ws_bytes, moe_stream_t stream);
+
+/* Workspace bytes moe_grouped_gemm may use for this shape on the current
+ * device (it depends on the device's compute-unit count); 0 for shapes and
+ * dtypes that never split, and for invalid arguments. */
+size_t moe_grouped_gemm_workspace_size(int G, int rows, int N, int K,
+                                       moe_dtype_t ab_dt, moe_epilogue_t epi);
 
 /*
  * FP8 block-scaled grouped GEMM ("DeepGEMM walkthrough" §2.3 and §5.1).

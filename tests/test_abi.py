@@ -36,7 +36,10 @@ def lib():
     L.moe_permute_workspace_size.argtypes = [i32, i32, i32]
     L.moe_permute.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                               vp, sz, vp]
-    L.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, vp]
+    L.moe_grouped_gemm_workspace_size.restype = sz
+    L.moe_grouped_gemm_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, vp, sz,
+                                   vp]
     L.moe_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
                                        i32, i32, vp]
     L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp]
@@ -59,7 +62,7 @@ NUL = C.c_void_p(0)
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), "libmoe.so does not export %s" % n
 
@@ -67,7 +70,7 @@ def test_every_declared_function_is_exported(lib):
 def test_status_strings_and_version(lib):
     for s in range(5):
         assert lib.moe_status_string(s)
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
 
 
 def test_route_validation(lib):
@@ -125,7 +128,7 @@ def test_permute_workspace_error_is_reported(lib):
 
 def test_gemm_validation(lib):
     g = lambda A, B, B2, dt, cdt, G, rows, N, K, epi: lib.moe_grouped_gemm(  # noqa: E731
-        A, B, B2, dt, P, cdt, P, G, rows, N, K, epi, NUL)
+        A, B, B2, dt, P, cdt, P, G, rows, N, K, epi, NUL, 0, NUL)
     assert g(P, P, NUL, BF16, BF16, 0, 10, 256, 64, 0) == INVALID        # G < 1
     assert g(P, P, NUL, BF16, BF16, 5000, 10, 256, 64, 0) == UNSUPPORTED  # G > max
     assert g(P, P, NUL, BF16, BF16, 2, 10, 256, 60, 0) == UNSUPPORTED    # K % 8
@@ -135,6 +138,19 @@ def test_gemm_validation(lib):
     assert g(P, P, NUL, BF16, BF16, 2, 10, 256, 64, 7) == INVALID        # bad epilogue
     assert g(MIS, P, NUL, BF16, BF16, 2, 10, 256, 64, 0) == INVALID
     assert g(P, P, NUL, BF16, BF16, 2, 0, 256, 64, 0) == OK              # no rows: no-op
+    # a workspace size without a workspace
+    assert lib.moe_grouped_gemm(P, P, NUL, BF16, P, BF16, P, 2, 10, 256, 64, 0, NUL, 64,
+                                NUL) == INVALID
+
+
+def test_gemm_workspace_size(lib):
+    ws = lib.moe_grouped_gemm_workspace_size
+    assert ws(0, 1024, 4096, 14336, BF16, 0) == 0        # invalid G
+    assert ws(8, -1, 4096, 14336, BF16, 0) == 0          # invalid rows
+    assert ws(8, 1024, 4096, 14336, F32, 0) == 0         # only the bf16 path splits
+    assert ws(8, 1024, 4096, 14336, BF16, 5) == 0        # bad epilogue
+    assert ws(8, 1024, 4096, 200, BF16, 0) == 0          # off the MFMA grid
+    assert ws(8, 1024, 4096, 256, BF16, 0) == 0          # K too short to cut in two
 
 
 def test_gemm_fp8_validation(lib):
