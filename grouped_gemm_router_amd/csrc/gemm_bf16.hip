@@ -3,25 +3,33 @@
 //
 // "DeepGEMM walkthrough" §4.2 (load tiles, multiply on the matrix cores,
 // accumulate in registers, write back), §4.3 (many GEMMs of different M in
-// one launch over an expert-contiguous layout), §5.2 (double -- here
-// quadruple -- buffering so loads overlap the multiplies), §5.3 (rows past a
+// one launch over an expert-contiguous layout), §5.2 (double buffering --
+// here deeper LDS rings -- so loads overlap the multiplies), §5.3 (rows past a
 // group's end are masked); "Dense GEMM to TP MoE" §2.1-2.3 (grouped, not
 // batched: N and K shared, M_i ragged; expert sizes stay on the GPU).
 //
 // Design (CDNA4, 64-wide waves):
-//   * output tile BM x 256 (BM = 256, or 128 when groups average fewer than
-//     ~192 rows, so small experts do not pay for a mostly empty tile), K
-//     step 32, 4 or 8 waves in a 2 x (NW/2) grid; each wave owns
-//     BM/2 x (256/(NW/2)) = MI x NB blocks of v_mfma_f32_32x32x16_bf16;
+//   * output tile BM x 256 (BM = 256, or 128 / 64 for the last, partial
+//     tile of a group), K step 32, 4 or 8 waves in a 2 x (NW/2) grid; each
+//     wave owns BM/2 x (256/(NW/2)) = MI x NB blocks of
+//     v_mfma_f32_32x32x16_bf16;
 //   * operand tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no
-//     staging registers) into a 4-stage LDS ring (4 x 32 KB), issued three
-//     steps ahead; each step waits only for its own stage (vmcnt) and meets
-//     the other waves at a plain s_barrier (no release fence, which would
-//     drain every in-flight load);
-//   * a tile row is 64 B = 4 pieces of 16 B; piece p of row r lives at slot
-//     p ^ ((r ^ (r >> 2)) & 3): the DMA writes whole rows and the MFMA
-//     fragment reads (16 rows x one piece per phase) hit distinct banks
-//     (measured: zero LDS bank conflicts);
+//     staging registers), each step waits only for its own data (vmcnt) and
+//     meets the other waves at a plain s_barrier (no release fence, which
+//     would drain every in-flight load);
+//   * A (activations) runs through a 4-stage ring of 64-byte row pieces
+//     (4 x 16 KB), issued three steps ahead; B (weights) through a ring of
+//     three double stages (3 x 32 KB) of 128-byte row pieces, issued four to
+//     five steps ahead.  Whole 128-byte lines halve the L2 requests for B
+//     (the TCP sends one request per line touched), which is what bounds this
+//     kernel: measured on the Mixtral shapes, all-64-byte rings 1.91 / 1.08
+//     ms (gate/up / down), this mix 1.75 / 0.96 ms, and a 2-stage ring of
+//     128-byte pieces for both operands 2.25 / 1.39 ms (too little in
+//     flight).  The two rings fill the 160 KB of LDS;
+//   * A row = 64 B = 4 pieces, piece p of row r at slot p ^ ((r ^ (r >> 2))
+//     & 3); B row = 128 B = 8 pieces at slot p ^ ((r >> 1) & 7): the DMA
+//     writes whole rows and the MFMA fragment reads (16 rows x one piece per
+//     phase) hit distinct banks;
 //   * fragments are double buffered in registers and the stage barrier sits
 //     in the middle of a stage, so the next stage's first fragments are read
 //     while this stage's second half of MFMAs runs; one LDS read is
@@ -46,11 +54,13 @@ namespace {
 using namespace moe;
 
 constexpr int BM_MAX = 256, BN = 256, BK = 32;
-constexpr int PIECES = BK / 8;             // 16-byte pieces per tile row
+constexpr int PIECES = BK / 8;             // 16-byte pieces per A tile row and stage
 constexpr int SLOTS_MAX = BM_MAX * PIECES; // 16-byte slots per A stage (16 KB at most)
-constexpr int SLOTS_B = BN * PIECES;       // 16-byte slots per B stage (16 KB)
+constexpr int PIECES_B = 2 * PIECES;       // B: 128-byte rows covering two stages
+constexpr int SLOTS_B2 = BN * PIECES_B;    // 16-byte slots per B double stage (32 KB)
 
 __device__ __forceinline__ int swz(int row, int p) { return p ^ ((row ^ (row >> 2)) & 3); }
+__device__ __forceinline__ int swzb(int row, int p) { return p ^ ((row >> 1) & 7); }
 
 // B-tile row of wave column wn (of NWN), 32-row block nb
 template <bool SWIGLU, int NWN>
@@ -94,8 +104,9 @@ struct Frag {
 
 template <bool SWIGLU, int MI, int NB, int NWN>
 __device__ __forceinline__ void read_frag(Frag<MI, NB> &f, const u32x4 *tA, const u32x4 *tB,
-                                          int ks, int wm, int wn, int fr, int fh) {
+                                          int ks, int par, int wm, int wn, int fr, int fh) {
   const int pc = ks * 2 + fh;
+  const int pb = par * PIECES + pc;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
     const int r = wm * (MI * 32) + mi * 32 + fr;
@@ -104,7 +115,7 @@ __device__ __forceinline__ void read_frag(Frag<MI, NB> &f, const u32x4 *tA, cons
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int r = b_row<SWIGLU, NWN>(wn, nb) + fr;
-    f.b[nb] = __builtin_bit_cast(bf16x8, tB[r * PIECES + swz(r, pc)]);
+    f.b[nb] = __builtin_bit_cast(bf16x8, tB[r * PIECES_B + swzb(r, pb)]);
   }
 }
 
@@ -142,8 +153,8 @@ __host__ __device__ inline size_t split_partial_offset(int cus) {
 
 // Slices per tail tile: 1 (no split) unless the last round holds at most
 // half as many tiles as there are CUs; then the largest S <= kSplitMax with
-// S * rem <= cus, KT a multiple of 4 S (the ring's 4-stage unroll) and at
-// least kSplitMinSteps steps per slice.
+// S * rem <= cus, KT a multiple of 4 S (the rings advance 4 steps at a time)
+// and at least kSplitMinSteps steps per slice.
 __host__ __device__ inline int split_slices(int total, int cus, int KT) {
   const int rem = total % cus;
   if (rem == 0 || 2 * rem > cus) return 1;
@@ -153,7 +164,7 @@ __host__ __device__ inline int split_slices(int total, int cus, int KT) {
 }
 
 // One output tile of height BM (rows [tile.m0, tile.mend), at most BM of
-// them) over K steps [kbeg/BK, kbeg/BK + KT), through the 4-stage LDS ring.
+// them) over K steps [kbeg/BK, kbeg/BK + KT), through the A and B LDS rings.
 // part == nullptr: the epilogue writes C; otherwise the raw fp32 accumulator
 // goes to part[(m - m0) * BN + B-tile row] (a K-slice of a split tile).
 template <int BM, bool SWIGLU, bool OUT_F32, int NW>
@@ -163,7 +174,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
                                          int rows, int N, int K, int kbeg, int KT,
                                          float *__restrict__ part, u32x4 *sA0, u32x4 *sA1,
                                          u32x4 *sA2, u32x4 *sA3, u32x4 *sB0, u32x4 *sB1,
-                                         u32x4 *sB2, u32x4 *sB3) {
+                                         u32x4 *sB2) {
   constexpr int NWN = NW / 2;                 // wave columns (2 wave rows)
   constexpr int MI = BM / 64;                 // 32-row blocks per wave
   constexpr int NB = (BN / NWN) / 32;         // 32-column blocks per wave
@@ -172,8 +183,8 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
   // load it 4 bytes per lane instead, so every wave issues the same count
   constexpr bool A_DW = SLOTS_A < NW * 64;
   constexpr int IA = A_DW ? (SLOTS_A * 4) / NW / 64 : SLOTS_A / NW / 64;
-  constexpr int IB = SLOTS_B / NW / 64;       // B DMA instructions per wave per stage
-  constexpr int PER_STAGE = IA + IB;          // vmcnt units per stage
+  constexpr int IB = SLOTS_B2 / NW / 64;      // B DMA instructions per wave per double stage
+  constexpr int PER_STAGE = IA + IB;          // vmcnt units issued between two waits
   constexpr int NM = MI * NB;                 // MFMAs per 16-deep step
   constexpr int NR = MI + NB;                 // fragment reads per 16-deep step
   static_assert(IA >= 1 && IB >= 1, "tile too small for the wave count");
@@ -206,9 +217,9 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
-    const int sl = wv * (SLOTS_B / NW) + i * 64 + lane;
-    const int r = sl / PIECES;
-    const int p = swz(r, sl % PIECES);
+    const int sl = wv * (SLOTS_B2 / NW) + i * 64 + lane;
+    const int r = sl / PIECES_B;
+    const int p = swzb(r, sl % PIECES_B);
     if (SWIGLU) {
       const int n = tile.nt * 128 + (r & 127);
       gb[i] = (r < 128 ? B : B2) + goff + (size_t)n * K + p * 8;
@@ -219,10 +230,11 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
   // LDS destinations of lane 0, in 16-byte units
   const int dma_a = A_DW ? wv * IA * 16 : wv * (SLOTS_A / NW);
   constexpr int STEP_A = A_DW ? 16 : 64;
-  const int dma_b = wv * (SLOTS_B / NW);
-#define MOE_ISSUE(dA, dB, k0)                                                              \
+  const int dma_b = wv * (SLOTS_B2 / NW);
+#define MOE_ISSUE_A(dA, k0)                                                                \
   _Pragma("unroll") for (int i = 0; i < IA; ++i)                                          \
-    dma_to_lds<A_DW ? 4 : 16>(ga[i] + (k0), (dA) + dma_a + i * STEP_A);                  \
+    dma_to_lds<A_DW ? 4 : 16>(ga[i] + (k0), (dA) + dma_a + i * STEP_A);
+#define MOE_ISSUE_B(dB, k0)                                                                \
   _Pragma("unroll") for (int i = 0; i < IB; ++i)                                          \
     __builtin_amdgcn_global_load_lds((const void *)(gb[i] + (k0)),                        \
                                      (lds_void *)((dB) + dma_b + i * 64), 16, 0, 0);
@@ -234,40 +246,70 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
   const int fr = lane & 31, fh = lane >> 5;
 
-  MOE_ISSUE(sA0, sB0, 0);
-  MOE_ISSUE(sA1, sB1, BK);
-  MOE_ISSUE(sA2, sB2, 2 * BK);
-  wait_vmcnt<2 * PER_STAGE>();  // stage 0 landed (stages 1, 2 may be in flight)
+  const int KT2 = KT / 2;  // B double stages
+  MOE_ISSUE_B(sB0, 0);
+  MOE_ISSUE_A(sA0, 0);
+  MOE_ISSUE_A(sA1, BK);
+  MOE_ISSUE_B(sB1, 2 * BK);
+  MOE_ISSUE_A(sA2, 2 * BK);
+  wait_vmcnt<2 * IA + IB>();  // A stage 0 and B stages 0-1 landed
   stage_barrier();
   Frag<MI, NB> f0, f1;
-  read_frag<SWIGLU, MI, NB, NWN>(f0, sA0, sB0, 0, wm, wn, fr, fh);
+  read_frag<SWIGLU, MI, NB, NWN>(f0, sA0, sB0, 0, 0, wm, wn, fr, fh);
 
-  // One stage: second-half fragments of this stage are read under the
-  // first-half MFMAs; then the barrier that makes stage s+1 visible (and
-  // frees buffer s-1 for the load three steps ahead); then the next stage's
-  // first-half fragments are read under the second-half MFMAs.  The last
-  // three stages re-load the final K step into buffers nobody reads, so the
-  // wait count never changes.
-#define MOE_STAGE(tA, tB, nA, nB, dA, dB, s)                                               \
-  read_frag<SWIGLU, MI, NB, NWN>(f1, tA, tB, 1, wm, wn, fr, fh);                             \
+  // One stage s: A from ring slot s % 4, B from double-stage slot (s / 2) % 3
+  // (half `tp`).  The barrier in the middle makes stage s+1 visible and frees
+  // A slot s-1 (refilled with stage s+3) and, on even s, B slot (s/2 + 2) % 3
+  // (refilled with stages s+4, s+5).  Between two waits exactly IA + IB
+  // instructions are issued, so the wait count never changes; past the end
+  // the last K step is re-loaded into slots nobody reads.
+#define MOE_STAGE(tA, tB, tp, nA, nB, np, dA, s, ISSB, dB)                                   \
+  read_frag<SWIGLU, MI, NB, NWN>(f1, tA, tB, 1, tp, wm, wn, fr, fh);                         \
   mfma_frag<MI, NB>(acc, f0);                                                                 \
   interleave_mfma_ds_read<NM, NR>();                                                          \
   wait_vmcnt<PER_STAGE>();                                                                    \
   stage_barrier();                                                                            \
-  MOE_ISSUE(dA, dB, min((s) + 3, KT - 1) * BK);                                               \
-  read_frag<SWIGLU, MI, NB, NWN>(f0, nA, nB, 0, wm, wn, fr, fh);                             \
+  MOE_ISSUE_A(dA, min((s) + 3, KT - 1) * BK);                                                 \
+  if (ISSB) { MOE_ISSUE_B(dB, min((s) / 2 + 2, KT2 - 1) * 2 * BK); }                          \
+  read_frag<SWIGLU, MI, NB, NWN>(f0, nA, nB, 0, np, wm, wn, fr, fh);                         \
   mfma_frag<MI, NB>(acc, f1);                                                                 \
   interleave_mfma_ds_read<NM, NR>();
 
-  for (int kt = 0; kt < KT; kt += 4) {
-    MOE_STAGE(sA0, sB0, sA1, sB1, sA3, sB3, kt)
-    MOE_STAGE(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1)
-    MOE_STAGE(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2)
-    MOE_STAGE(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3)
+#define MOE_STAGES_0_3(kt)                                        \
+  MOE_STAGE(sA0, sB0, 0, sA1, sB0, 1, sA3, (kt), 1, sB2)          \
+  MOE_STAGE(sA1, sB0, 1, sA2, sB1, 0, sA0, (kt) + 1, 0, sB0)      \
+  MOE_STAGE(sA2, sB1, 0, sA3, sB1, 1, sA1, (kt) + 2, 1, sB0)      \
+  MOE_STAGE(sA3, sB1, 1, sA0, sB2, 0, sA2, (kt) + 3, 0, sB0)
+#define MOE_STAGES_4_7(kt)                                        \
+  MOE_STAGE(sA0, sB2, 0, sA1, sB2, 1, sA3, (kt) + 4, 1, sB1)      \
+  MOE_STAGE(sA1, sB2, 1, sA2, sB0, 0, sA0, (kt) + 5, 0, sB1)      \
+  MOE_STAGE(sA2, sB0, 0, sA3, sB0, 1, sA1, (kt) + 6, 1, sB2)      \
+  MOE_STAGE(sA3, sB0, 1, sA0, sB1, 0, sA2, (kt) + 7, 0, sB2)
+#define MOE_STAGES_8_11(kt)                                       \
+  MOE_STAGE(sA0, sB1, 0, sA1, sB1, 1, sA3, (kt) + 8, 1, sB0)      \
+  MOE_STAGE(sA1, sB1, 1, sA2, sB2, 0, sA0, (kt) + 9, 0, sB0)      \
+  MOE_STAGE(sA2, sB2, 0, sA3, sB2, 1, sA1, (kt) + 10, 1, sB1)     \
+  MOE_STAGE(sA3, sB2, 1, sA0, sB0, 0, sA2, (kt) + 11, 0, sB1)
+
+  int kt = 0;
+  for (; kt + 12 <= KT; kt += 12) {
+    MOE_STAGES_0_3(kt)
+    MOE_STAGES_4_7(kt)
+    MOE_STAGES_8_11(kt)
+  }
+  if (kt + 4 <= KT) {  // KT % 12 is 0, 4 or 8
+    MOE_STAGES_0_3(kt)
+    if (kt + 8 <= KT) {
+      MOE_STAGES_4_7(kt)
+    }
   }
   wait_vmcnt<0>();  // no LDS-direct load may still be landing when the tile ends
+#undef MOE_STAGES_0_3
+#undef MOE_STAGES_4_7
+#undef MOE_STAGES_8_11
 #undef MOE_STAGE
-#undef MOE_ISSUE
+#undef MOE_ISSUE_A
+#undef MOE_ISSUE_B
 
   // epilogue.  32x32 accumulator layout: lane holds column lane%32, and
   // register r holds row 8*(r/4) + 4*(lane/32) + r%4.
@@ -338,10 +380,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const uint16_t *__restrict__ B2, void *__restrict__ C, const int32_t *__restrict__ offsets,
     int G, int rows, int N, int K, int nt_count, char *__restrict__ ws, int cus) {
+  // 4 A stages (64 KB) and 3 B double stages (96 KB): all 160 KB of LDS.
+  // The scheduler table lives in the last B slot, which is first loaded
+  // after every wave has passed the prologue barrier.
   __shared__ u32x4 sA0[SLOTS_MAX], sA1[SLOTS_MAX], sA2[SLOTS_MAX], sA3[SLOTS_MAX];
-  __shared__ u32x4 sB0[SLOTS_B], sB1[SLOTS_B], sB2[SLOTS_B], sB3[SLOTS_B];
-  __shared__ int s_cum[MOE_MAX_GROUPS + 1];
-  __shared__ int s_tmp[NW];
+  __shared__ u32x4 sB0[SLOTS_B2], sB1[SLOTS_B2], sB2[SLOTS_B2];
+  static_assert(sizeof(int) * (MOE_MAX_GROUPS + 1 + NW) <= sizeof(u32x4) * SLOTS_B2,
+                "scheduler table must fit in one B slot");
+  int *s_cum = reinterpret_cast<int *>(sB2);
+  int *s_tmp = s_cum + MOE_MAX_GROUPS + 1;
 
   sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_tmp);
   const int total = s_cum[G] * nt_count;
@@ -373,13 +420,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   const int h = tile.mend - tile.m0;  // wave-uniform
   if (h > 128)
     run_tile<256, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, kbeg, kt, part, sA0, sA1,
-                                       sA2, sA3, sB0, sB1, sB2, sB3);
+                                       sA2, sA3, sB0, sB1, sB2);
   else if (h > 64)
     run_tile<128, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, kbeg, kt, part, sA0, sA1,
-                                       sA2, sA3, sB0, sB1, sB2, sB3);
+                                       sA2, sA3, sB0, sB1, sB2);
   else
     run_tile<64, SWIGLU, OUT_F32, NW>(tile, A, B, B2, C, rows, N, K, kbeg, kt, part, sA0, sA1,
-                                      sA2, sA3, sB0, sB1, sB2, sB3);
+                                      sA2, sA3, sB0, sB1, sB2);
 }
 
 // Sum of the S partial tiles of each split tile, in slice order, then the
@@ -480,3 +527,4 @@ hipError_t launch_gemm_bf16_mfma(const void *A, const void *B, const void *B2, v
   }
   return hipGetLastError();
 }
+
