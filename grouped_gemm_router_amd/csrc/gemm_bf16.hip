@@ -314,7 +314,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
   // epilogue.  32x32 accumulator layout: lane holds column lane%32, and
   // register r holds row 8*(r/4) + 4*(lane/32) + r%4.
   const int col = lane & 31, rbase = 4 * (lane >> 5);
-  if (SWIGLU && part != nullptr) {
+  if (part != nullptr) {  // a K-slice of a split tile: raw fp32 partials
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -327,44 +327,59 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
         }
     return;
   }
-  if (SWIGLU) {
-    constexpr int HB = NB / 2;
+  // Output, one 32-row block (mi) of every wave at a time: each wave writes
+  // its values into LDS -- wave row wm into B slot wm, free once every wave
+  // is past the last stage -- as [32 rows][TC columns] of the output type,
+  // then all threads store whole 16-byte row pieces (instead of one 2- or
+  // 4-byte store per accumulator element).  The 16-byte piece index is
+  // XORed with bit 2 of the row, so the two rows one write instruction
+  // touches (4 apart) fall in different banks.
+  constexpr int TC = SWIGLU ? BN / 2 : BN;  // output columns of the tile
+  constexpr int OSZ = OUT_F32 ? 4 : 2;      // bytes per output element
+  constexpr int ROWB = TC * OSZ;            // bytes per staged row
+  constexpr int PPR = ROWB / 16;            // 16-byte pieces per row
+  static_assert(32 * ROWB <= (int)sizeof(u32x4) * SLOTS_B2, "staging block must fit a B slot");
+  __syncthreads();  // every wave is done reading the rings
+  char *const stg_w = reinterpret_cast<char *>(wm == 0 ? sB0 : sB1);
+  const size_t col0 = (size_t)tile.nt * TC;  // first output column of the tile
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < MI; ++mi) {
+    constexpr int NO = SWIGLU ? NB / 2 : NB;  // 32-column output blocks per wave
 #pragma unroll
-      for (int nb = 0; nb < HB; ++nb)
+    for (int nb = 0; nb < NO; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = tile.m0 + wm * (MI * 32) + mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
-          if (m < tile.mend) {
-            const int n = tile.nt * 128 + wn * (128 / NWN) + nb * 32 + col;
-            const float g = acc[mi][nb][r], u = acc[mi][nb + HB][r];
-            const float h = g / (1.0f + expf(-g)) * u;
-            if (OUT_F32)
-              static_cast<float *>(C)[(size_t)m * N + n] = h;
-            else
-              static_cast<uint16_t *>(C)[(size_t)m * N + n] = f32_to_bf16_bits(h);
-          }
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + rbase + (r & 3);
+        const int c = wn * (TC / NWN) + nb * 32 + col;
+        float v;
+        if (SWIGLU) {
+          const float g = acc[mi][nb][r], u = acc[mi][nb + NO][r];
+          // bf16 output: hardware exp2 and reciprocal (each within 1 ulp;
+          // far below the bf16 rounding); fp32 output keeps expf and the
+          // IEEE divide
+          v = OUT_F32 ? g / (1.0f + expf(-g)) * u
+                      : g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * g)) * u;
+        } else {
+          v = acc[mi][nb][r];
         }
-  } else {
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = tile.m0 + wm * (MI * 32) + mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
-          if (m < tile.mend) {
-            const int nn = wn * (256 / NWN) + nb * 32 + col;  // column in the tile
-            const float v = acc[mi][nb][r];
-            if (part != nullptr)
-              part[(size_t)(m - tile.m0) * BN + nn] = v;
-            else if (OUT_F32)
-              static_cast<float *>(C)[(size_t)m * N + tile.nt * 256 + nn] = v;
-            else
-              static_cast<uint16_t *>(C)[(size_t)m * N + tile.nt * 256 + nn] = f32_to_bf16_bits(v);
-          }
-        }
+        const int off = row * ROWB + ((((c * OSZ) >> 4) ^ ((row >> 2) & 1)) << 4) + ((c * OSZ) & 15);
+        if (OUT_F32)
+          *reinterpret_cast<float *>(stg_w + off) = v;
+        else
+          *reinterpret_cast<__bf16 *>(stg_w + off) = (__bf16)v;  // round to nearest even
+      }
+    __syncthreads();
+    for (int q = tid; q < 2 * 32 * PPR; q += NW * 64) {
+      const int wr = q / (32 * PPR), rr = (q / PPR) % 32, pc = q % PPR;
+      const int m = tile.m0 + wr * (MI * 32) + mi * 32 + rr;
+      if (m < tile.mend) {
+        const char *src = reinterpret_cast<const char *>(wr == 0 ? sB0 : sB1) + rr * ROWB +
+                          ((pc ^ ((rr >> 2) & 1)) << 4);
+        *reinterpret_cast<u32x4 *>(static_cast<char *>(C) + ((size_t)m * N + col0) * OSZ + pc * 16) =
+            *reinterpret_cast<const u32x4 *>(src);
+      }
+    }
+    __syncthreads();  // the staging block is rewritten for the next mi
   }
 }
 

@@ -193,7 +193,8 @@ moe_status_t moe_grouped_gemm(const void *A, const void *B, const void *B2, moe_
   if (epi == MOE_EPI_SWIGLU ? !aligned16(B2) : B2 != nullptr) return MOE_ERR_INVALID;
   if ((long long)G * N * K >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
   if (ws == nullptr && ws_bytes != 0) return MOE_ERR_INVALID;
-  const bool mfma = ab_dt == MOE_BF16 && gemm_bf16_mfma_supports(N, K, epi);
+  // the MFMA kernel writes C in 16-byte row pieces
+  const bool mfma = ab_dt == MOE_BF16 && gemm_bf16_mfma_supports(N, K, epi) && aligned16(C);
   void *split_ws = nullptr;
   int cus = 0;
   if (ws != nullptr && mfma) {
