@@ -16,10 +16,12 @@
 //            tiles keep the re-reads of x and w_router from L2 low.  fp32
 //            inputs (small configurations) take a plain per-thread dot
 //            product with one slice.
-//   select   one wave per token: sum of the partials in slice order
-//            (deterministic) plus the bias, export of the logits, wave max,
-//            wave sum of exp, then k rounds of a wave-wide argmax with the key
-//            (logit descending, index ascending).
+//   select   one token per segment of lanes (the next power of two >= E,
+//            at most a wave): sum of the partials in slice order
+//            (deterministic; eight slices' loads in flight at once) plus the
+//            bias, export of the logits, segment max, sum of exp, then k
+//            rounds of a segment-wide argmax with the key (logit descending,
+//            index ascending).
 #include "moe_internal.h"
 
 namespace {
@@ -27,7 +29,6 @@ namespace {
 using namespace moe;
 
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kMaxPerLane = MOE_MAX_EXPERTS / kWave;  // 16
 constexpr int RT = 128;        // tokens per logits tile
 constexpr int RK = 64;         // columns per K step
 constexpr int RP = RK / 8;     // 16-byte pieces per tile row
@@ -156,38 +157,64 @@ __global__ __launch_bounds__(kThreads) void route_logits_f32(const float *__rest
   part[p] = acc;
 }
 
+// One token per segment of W lanes (W = 8 ... 64, so 64 / W tokens per
+// wave when E <= 32); a lane holds NPER = ceil(E / W) experts, e = lane + W i.
+// The S partials of a value are loaded eight slices at a time, all issued
+// before the first is used, and added in slice order.  Segment-wide max,
+// sum of exp and k rounds of argmax use xor shuffles inside the segment.
+template <int W, int NPER>
 __global__ __launch_bounds__(kThreads) void route_select(
     const float *__restrict__ part, int S, const float *__restrict__ bias, int T, int E, int k,
     int renorm, float *__restrict__ logits_out, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w) {
-  const int lane = lane_id(), wv = threadIdx.x / kWave;
-  const int t = blockIdx.x * (kThreads / kWave) + wv;
-  if (t >= T) return;
-  float v[kMaxPerLane];
-  const int nper = (E + kWave - 1) / kWave;
+  constexpr int TPW = kWave / W;  // tokens per wave
+  const int lane = lane_id(), wv = threadIdx.x / kWave, sl_lane = lane % W;
+  const int t = (blockIdx.x * (kThreads / kWave) + wv) * TPW + lane / W;
+  const bool tok = t < T;  // no early return: the shuffles need every lane
+  bool ok[NPER];
+  size_t base[NPER];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + i * kWave;
-    float val = -INFINITY;
-    if (i < nper && e < E) {
-      val = part[(size_t)t * E + e];
-      for (int sl = 1; sl < S; ++sl) val += part[((size_t)sl * T + t) * E + e];
-      if (bias) val += bias[e];
-      if (logits_out) logits_out[(size_t)t * E + e] = val;
+  for (int i = 0; i < NPER; ++i) {
+    const int e = sl_lane + i * W;
+    ok[i] = tok && e < E;
+    base[i] = (size_t)(tok ? t : 0) * E + (e < E ? e : 0);
+  }
+  float v[NPER];
+  constexpr int CH = 8;  // slices loaded per round
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    float q[CH][NPER];
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        q[j][i] = (s0 + j < S && ok[i]) ? part[(size_t)(s0 + j) * T * E + base[i]] : 0.f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if (s0 + j < S) v[i] = (s0 + j == 0) ? q[j][i] : v[i] + q[j][i];
+  }
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = sl_lane + i * W;
+    if (ok[i]) {
+      if (bias) v[i] += bias[e];
+      if (logits_out) logits_out[base[i]] = v[i];
+    } else {
+      v[i] = -INFINITY;
     }
-    v[i] = val;
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) mx = fmaxf(mx, v[i]);
-  mx = wave_max(mx);
+  for (int i = 0; i < NPER; ++i) mx = fmaxf(mx, v[i]);
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
   float z = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + i * kWave;
-    if (i < nper && e < E) z += expf(v[i] - mx);
-  }
-  z = wave_sum(z);
+  for (int i = 0; i < NPER; ++i)
+    if (ok[i]) z += expf(v[i] - mx);
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kWave);
 
   uint32_t taken = 0;
   float my_w = 0.f;
@@ -197,33 +224,59 @@ __global__ __launch_bounds__(kThreads) void route_select(
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + i * kWave;
-      if (i < nper && e < E && !((taken >> i) & 1u)) {
+    for (int i = 0; i < NPER; ++i) {
+      const int e = sl_lane + i * W;
+      if (ok[i] && !((taken >> i) & 1u)) {
         if (v[i] > bv || (v[i] == bv && e < be)) { bv = v[i]; be = e; }
       }
     }
-    // wave-wide argmax on (value desc, index asc)
+    // segment-wide argmax on (value desc, index asc)
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
+    for (int o = W / 2; o > 0; o >>= 1) {
       const float ov = __shfl_xor(bv, o, kWave);
       const int oe = __shfl_xor(be, o, kWave);
       if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
     }
-    if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-    if (lane == j) {
+    if (be != 0x7fffffff && (be % W) == sl_lane) taken |= 1u << (be / W);
+    if (sl_lane == j) {
       my_idx = be;
       my_w = expf(bv - mx) / z;
     }
   }
   if (renorm) {
-    const float s = wave_sum(lane < k ? my_w : 0.f);
-    my_w = my_w / s;
+    float sw = sl_lane < k ? my_w : 0.f;
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) sw += __shfl_xor(sw, o, kWave);
+    my_w = my_w / sw;
   }
-  if (lane < k) {
-    topk_idx[(size_t)t * k + lane] = my_idx;
-    topk_w[(size_t)t * k + lane] = my_w;
+  if (tok && sl_lane < k) {
+    topk_idx[(size_t)t * k + sl_lane] = my_idx;
+    topk_w[(size_t)t * k + sl_lane] = my_w;
   }
+}
+
+template <int W, int NPER>
+void launch_select_t(const float *part, int S, const float *bias, int T, int E, int k, int renorm,
+                     float *logits_out, int32_t *topk_idx, float *topk_w, hipStream_t s) {
+  constexpr int TPB = (kThreads / kWave) * (kWave / W);  // tokens per workgroup
+  hipLaunchKernelGGL((route_select<W, NPER>), dim3((T + TPB - 1) / TPB), dim3(kThreads), 0, s,
+                     part, S, bias, T, E, k, renorm, logits_out, topk_idx, topk_w);
+}
+
+// segment width: the next power of two >= E up to 64, then NPER = E / 64
+void launch_select(const float *part, int S, const float *bias, int T, int E, int k, int renorm,
+                   float *logits_out, int32_t *topk_idx, float *topk_w, hipStream_t s) {
+#define MOE_SEL(W, NP) \
+  launch_select_t<W, NP>(part, S, bias, T, E, k, renorm, logits_out, topk_idx, topk_w, s)
+  if (E <= 8) MOE_SEL(8, 1);
+  else if (E <= 16) MOE_SEL(16, 1);
+  else if (E <= 32) MOE_SEL(32, 1);
+  else if (E <= 64) MOE_SEL(64, 1);
+  else if (E <= 128) MOE_SEL(64, 2);
+  else if (E <= 256) MOE_SEL(64, 4);
+  else if (E <= 512) MOE_SEL(64, 8);
+  else MOE_SEL(64, 16);
+#undef MOE_SEL
 }
 
 }  // namespace
@@ -236,10 +289,9 @@ hipError_t launch_route(const void *x, const void *w_router, int dt, const float
                         int d, int E, int k, unsigned flags, float *logits, int32_t *topk_idx,
                         float *topk_w, float *ws, hipStream_t s) {
   const int renorm = (flags & MOE_ROUTE_RENORM) ? 1 : 0;
-  const dim3 sel_grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
+  const dim3 block(kThreads);
   if (flags & MOE_ROUTE_FROM_LOGITS) {
-    hipLaunchKernelGGL(route_select, sel_grid, block, 0, s, logits, 1, nullptr, T, E, k, renorm,
-                       nullptr, topk_idx, topk_w);
+    launch_select(logits, 1, nullptr, T, E, k, renorm, nullptr, topk_idx, topk_w, s);
     return hipGetLastError();
   }
   int S = 1;
@@ -263,7 +315,6 @@ hipError_t launch_route(const void *x, const void *w_router, int dt, const float
                        0, s, static_cast<const float *>(x), static_cast<const float *>(w_router),
                        T, d, E, ws);
   }
-  hipLaunchKernelGGL(route_select, sel_grid, block, 0, s, ws, S, bias, T, E, k, renorm, logits,
-                     topk_idx, topk_w);
+  launch_select(ws, S, bias, T, E, k, renorm, logits, topk_idx, topk_w, s);
   return hipGetLastError();
 }
