@@ -6,10 +6,11 @@
 // expert is added with weight one.
 //
 // One workgroup per token.  Each thread owns 8 consecutive columns (one
-// 16-byte bf16 piece, two for fp32): it issues the row loads of four terms
-// at a time, accumulates in fp32 in ascending j with fused multiply-adds
-// (the shared rows last, weight one), and stores once.  HBM traffic is one
-// read of every used Y row and one write of out.
+// 16-byte bf16 piece, two for fp32; two such pieces at a time for fp32 Y):
+// it issues the row loads of four terms at a time, accumulates in fp32 in
+// ascending j with fused multiply-adds (the shared rows last, weight one),
+// and stores once.  HBM traffic is one read of every used Y row and one
+// write of out.
 #include "moe_internal.h"
 
 namespace {
@@ -59,52 +60,63 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ Y
   __syncthreads();
   const long long nrows = (long long)T * k + (long long)n_shared * T;
   const int npiece = d / 8;
-  for (int p = threadIdx.x; p < npiece; p += blockDim.x) {
-    float acc[8];
+  // PP column pieces per thread and round (p, p + blockDim.x, ...); terms in
+  // groups of 4; all row loads of a group are issued before the first is
+  // used, and accumulation stays in ascending j.  Two pieces for fp32 Y
+  // (measured faster on the Mixtral shapes), one for bf16 Y (two measured
+  // slower on the DeepSeek FP8 shapes: 0.12 -> 0.14 ms)
+  constexpr int PP = YSIZE == 4 ? 2 : 1;
+  for (int p0 = threadIdx.x; p0 < npiece; p0 += PP * blockDim.x) {
+    float acc[PP][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    // terms in groups of 4: the group's row loads are all issued before the
-    // first one is used; accumulation stays in ascending j
+    for (int h = 0; h < PP; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
     for (int j0 = 0; j0 < nterm; j0 += 4) {
-      float v[4][8];
+      float v[PP][4][8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = j0 + q;
-        const int row = j < nterm ? s_row[j] : -1;
-        if (row >= 0 && row < nrows) {  // else: dropped entry (or bad index)
-          load8<YSIZE>(Y, (size_t)row * d + (size_t)p * 8, v[q]);
-        } else {
+      for (int h = 0; h < PP; ++h)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[q][i] = 0.f;
+        for (int q = 0; q < 4; ++q) {
+          const int j = j0 + q, p = p0 + h * blockDim.x;
+          const int row = j < nterm ? s_row[j] : -1;
+          if (p < npiece && row >= 0 && row < nrows) {  // else: dropped entry (or bad index)
+            load8<YSIZE>(Y, (size_t)row * d + (size_t)p * 8, v[h][q]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[h][q][i] = 0.f;
+          }
         }
-      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int j = j0 + q;
         if (j >= nterm) break;
         const int row = s_row[j];
         if (row < 0 || row >= nrows) continue;
-        if (j < k) {
-          const float w = s_w[j];
+        const float w = j < k ? s_w[j] : 1.0f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[q][i], acc[i]);
-        } else {
+        for (int h = 0; h < PP; ++h)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] += v[q][i];
-        }
+          for (int i = 0; i < 8; ++i)
+            acc[h][i] = j < k ? fmaf(w, v[h][q][i], acc[h][i]) : acc[h][i] + v[h][q][i];
       }
     }
-    if (OSIZE == 2) {
-      uint4 o;
-      o.x = f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
-      o.y = f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
-      o.z = f32_to_bf16_bits(acc[4]) | ((uint32_t)f32_to_bf16_bits(acc[5]) << 16);
-      o.w = f32_to_bf16_bits(acc[6]) | ((uint32_t)f32_to_bf16_bits(acc[7]) << 16);
-      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + (size_t)t * d + (size_t)p * 8) = o;
-    } else {
-      float *o = static_cast<float *>(out) + (size_t)t * d + (size_t)p * 8;
-      *reinterpret_cast<float4 *>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      *reinterpret_cast<float4 *>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+    for (int h = 0; h < PP; ++h) {
+      const int p = p0 + h * blockDim.x;
+      if (p >= npiece) break;
+      if (OSIZE == 2) {
+        uint4 o;
+        o.x = f32_to_bf16_bits(acc[h][0]) | ((uint32_t)f32_to_bf16_bits(acc[h][1]) << 16);
+        o.y = f32_to_bf16_bits(acc[h][2]) | ((uint32_t)f32_to_bf16_bits(acc[h][3]) << 16);
+        o.z = f32_to_bf16_bits(acc[h][4]) | ((uint32_t)f32_to_bf16_bits(acc[h][5]) << 16);
+        o.w = f32_to_bf16_bits(acc[h][6]) | ((uint32_t)f32_to_bf16_bits(acc[h][7]) << 16);
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + (size_t)t * d + (size_t)p * 8) = o;
+      } else {
+        float *o = static_cast<float *>(out) + (size_t)t * d + (size_t)p * 8;
+        *reinterpret_cast<float4 *>(o) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+        *reinterpret_cast<float4 *>(o + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      }
     }
   }
 }

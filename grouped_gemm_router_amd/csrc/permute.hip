@@ -108,19 +108,50 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_sha
                                                          int32_t *__restrict__ ovf_start,
                                                          int32_t *__restrict__ n_overflow) {
   __shared__ int s_wave[16];
+  __shared__ int s_part[1024];  // [r][E]: count of expert e over thread r's blocks
+  __shared__ int s_tot[MOE_MAX_EXPERTS];
   const int tid = threadIdx.x;
-  int total = 0;
-  if (tid < E) {
-    for (int b0 = 0; b0 < nblk; b0 += 16) {
+  // R threads per expert (thread r of expert e takes a contiguous run of
+  // token blocks), so the per-block counts are read with many loads in
+  // flight even when E is small
+  const int R = max(1, min(1024 / E, nblk));
+  const int e = tid % E, r = tid / E;
+  const bool act = r < R && tid < R * E;
+  const int per = (nblk + R - 1) / R;
+  const int b_lo = min(nblk, r * per), b_hi = min(nblk, b_lo + per);
+  int mine = 0;
+  if (act) {
+    for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
       int c[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = (b0 + i < nblk) ? blk[(size_t)(b0 + i) * E + tid] : 0;
+      for (int i = 0; i < 16; ++i) c[i] = (b0 + i < b_hi) ? blk[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mine += c[i];
+    }
+    s_part[r * E + e] = mine;
+  }
+  __syncthreads();
+  if (act) {
+    // exclusive prefix of expert e over the runs before r, then the run's
+    // blocks in order (the counts are re-read from cache)
+    int run = 0;
+    for (int q = 0; q < r; ++q) run += s_part[q * E + e];
+    for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = (b0 + i < b_hi) ? blk[(size_t)(b0 + i) * E + e] : 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (b0 + i < nblk) blk[(size_t)(b0 + i) * E + tid] = total;
-        total += c[i];
+        if (b0 + i < b_hi) blk[(size_t)(b0 + i) * E + e] = run;
+        run += c[i];
       }
     }
+    if (r == R - 1) s_tot[e] = run;
+  }
+  __syncthreads();
+  int total = 0;
+  if (tid < E) {
+    total = s_tot[tid];
     counts[tid] = total;
   }
   const int kept = min(total, cap);
@@ -182,16 +213,32 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
     const int cpr = d * ESIZE / 16;
     const int items = (t1 - t0) * cpr;
     uint4 *dst = static_cast<uint4 *>(x_perm);
-    for (int it = threadIdx.x; it < items; it += blockDim.x) {
-      const int tt = it / cpr, c = it - tt * cpr;
-      const int t = t0 + tt;
-      const uint4 v = reinterpret_cast<const uint4 *>(x + (size_t)t * d * ESIZE)[c];
-      for (int j = 0; j < k; ++j) {
-        const int row = s_row[tt * k + j];
-        if (row >= 0) dst[(size_t)row * cpr + c] = v;
+    // U pieces per thread and round: all loads are issued before the first
+    // store, so each thread keeps U reads in flight
+    constexpr int U = 8;
+    for (int it0 = threadIdx.x; it0 < items; it0 += U * blockDim.x) {
+      uint4 v[U];
+      int tt[U], c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int it = it0 + u * blockDim.x;
+        tt[u] = it < items ? it / cpr : -1;
+        c[u] = it - (it / cpr) * cpr;
+        v[u] = tt[u] >= 0 ? reinterpret_cast<const uint4 *>(x + (size_t)(t0 + tt[u]) * d * ESIZE)[c[u]]
+                          : uint4{0u, 0u, 0u, 0u};
       }
-      for (int s = 0; s < n_shared; ++s)
-        dst[(shared_base + (size_t)s * T + t) * cpr + c] = v;
+      for (int j = 0; j < k; ++j) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int row = tt[u] >= 0 ? s_row[tt[u] * k + j] : -1;
+          if (row >= 0) dst[(size_t)row * cpr + c[u]] = v[u];
+        }
+      }
+      for (int sh = 0; sh < n_shared; ++sh) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (tt[u] >= 0) dst[(shared_base + (size_t)sh * T + t0 + tt[u]) * cpr + c[u]] = v[u];
+      }
     }
   } else {
     // one 1 x 128 group per 16 lanes, 8 elements per lane
@@ -200,56 +247,69 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
     const int lane16 = threadIdx.x & 15;
     uint8_t *dst = static_cast<uint8_t *>(x_perm);
     // every 16-lane group iterates the same number of times, so the
-    // shuffles below always see their whole group
-    for (int base = threadIdx.x >> 4; base < ((items + 15) / 16) * 16; base += blockDim.x >> 4) {
-      const int it = base;
-      const bool ok = it < items;
-      const int tt = ok ? it / gpr : 0, gi = ok ? it - tt * gpr : 0;
-      const int t = t0 + tt;
-      float v[8];
-      const size_t e0 = (size_t)t * d + gi * 128 + lane16 * 8;
-      if (ok) {
-        if (ESIZE == 2) {
-          const uint4 raw = *reinterpret_cast<const uint4 *>(x + e0 * 2);
-          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    // shuffles below always see their whole group; each iteration takes two
+    // groups (stride apart) and issues both loads before using either
+    const int stride = blockDim.x >> 4;
+    const int rounds = (items + 2 * stride - 1) / (2 * stride);
+    for (int rd = 0; rd < rounds; ++rd) {
+      float v[2][8];
+      int its[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
-            v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      for (int h = 0; h < 2; ++h) {
+        const int it = rd * 2 * stride + h * stride + (threadIdx.x >> 4);
+        its[h] = it;
+        if (it < items) {
+          const int tt = it / gpr, gi = it - tt * gpr;
+          const size_t e0 = (size_t)(t0 + tt) * d + gi * 128 + lane16 * 8;
+          if (ESIZE == 2) {
+            const uint4 raw = *reinterpret_cast<const uint4 *>(x + e0 * 2);
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[h][2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+              v[h][2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+            }
+          } else {
+            const float4 a = *reinterpret_cast<const float4 *>(x + e0 * 4);
+            const float4 b2 = *reinterpret_cast<const float4 *>(x + e0 * 4 + 16);
+            v[h][0] = a.x; v[h][1] = a.y; v[h][2] = a.z; v[h][3] = a.w;
+            v[h][4] = b2.x; v[h][5] = b2.y; v[h][6] = b2.z; v[h][7] = b2.w;
           }
         } else {
-          const float4 a = *reinterpret_cast<const float4 *>(x + e0 * 4);
-          const float4 b2 = *reinterpret_cast<const float4 *>(x + e0 * 4 + 16);
-          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-          v[4] = b2.x; v[5] = b2.y; v[6] = b2.z; v[7] = b2.w;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[h][i] = 0.f;
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
       }
-      float amax = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      amax = group_max(amax, 16);
-      const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-      uint32_t lo = 0, hi = 0;
+      for (int h = 0; h < 2; ++h) {
+        const int it = its[h];
+        const bool ok = it < items;
+        const int tt = ok ? it / gpr : 0, gi = ok ? it - tt * gpr : 0;
+        const int t = t0 + tt;
+        float amax = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] / sc) << (8 * i);
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[h][i]));
+        amax = group_max(amax, 16);
+        const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+        uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] / sc) << (8 * i);
-      const uint2 q = make_uint2(lo, hi);
-      if (ok) {
-        for (int j = 0; j < k + n_shared; ++j) {
-          size_t row;
-          if (j < k) {
-            const int r = s_row[tt * k + j];
-            if (r < 0) continue;
-            row = (size_t)r;
-          } else {
-            row = shared_base + (size_t)(j - k) * T + t;
+        for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[h][i] / sc) << (8 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[h][4 + i] / sc) << (8 * i);
+        const uint2 q = make_uint2(lo, hi);
+        if (ok) {
+          for (int j = 0; j < k + n_shared; ++j) {
+            size_t row;
+            if (j < k) {
+              const int r = s_row[tt * k + j];
+              if (r < 0) continue;
+              row = (size_t)r;
+            } else {
+              row = shared_base + (size_t)(j - k) * T + t;
+            }
+            *reinterpret_cast<uint2 *>(dst + row * d + gi * 128 + lane16 * 8) = q;
+            if (lane16 == 0) x_scale[(size_t)gi * srows + row] = sc;
           }
-          *reinterpret_cast<uint2 *>(dst + row * d + gi * 128 + lane16 * 8) = q;
-          if (lane16 == 0) x_scale[(size_t)gi * srows + row] = sc;
         }
       }
     }
