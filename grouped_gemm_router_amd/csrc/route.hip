@@ -4,7 +4,9 @@
 // scoring experts; the same p weights the combine.  "Dense GEMM to TP MoE"
 // §4.2: the router is a linear layer with weight [num_experts][hidden_dim].
 //
-// Two launches:
+// E <= 32 with bf16 inputs: one launch (route_fused_small below; the
+// logits are a few dot products per token, so the partial-logit round trip
+// would dominate).  Otherwise two launches:
 //   logits   a split-K GEMM x [T][d] . w_router[E][d]^T on the matrix cores
 //            (v_mfma_f32_32x32x16_bf16): a workgroup (4 waves) owns 128
 //            tokens x EB experts (EB = 32, 64 or 128) over one slice of the
@@ -255,6 +257,119 @@ __global__ __launch_bounds__(kThreads) void route_select(
   }
 }
 
+// Small E (<= 32, bf16): scoring, softmax and top-k in one launch, no
+// workspace.  A workgroup takes TPW = 64 / EP tokens (EP = E rounded up to
+// 8, 16 or 32) and its four waves split the d axis; a lane accumulates the
+// bf16 dot products (v_dot2c_f32_bf16) of every (token, expert) pair over
+// its 16-byte column chunks, with the token and weight chunks of a step all
+// loaded before use.  A butterfly reduce-scatter over the wave (each value
+// added in exactly one lane, fixed pairing) leaves lane l with value l =
+// token l / EP, expert l % EP; the four waves' values are added in wave
+// order through LDS, and wave 0 finishes like the select kernel with one
+// token per EP-lane segment.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int EP>
+__global__ __launch_bounds__(kThreads) void route_fused_small(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+    const float *__restrict__ bias, int T, int d, int E, int k, int renorm,
+    float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w) {
+  constexpr int TPW = kWave / EP;  // tokens per workgroup
+  __shared__ float s_red[kThreads / kWave][kWave];
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  const int t0 = blockIdx.x * TPW;
+  const int nch = d / 8;  // 16-byte chunks per row
+  const int c_lo = wv * nch / 4, c_hi = (wv + 1) * nch / 4;
+  float a[kWave];  // [t][e] partial dot products
+#pragma unroll
+  for (int i = 0; i < kWave; ++i) a[i] = 0.f;
+  for (int c = c_lo + lane; c < c_hi; c += kWave) {
+    // the 16-byte chunks go through plain arrays of dwords: bit-casting a
+    // subscripted vector element (v[j]) to bf16x2 compiles to element 0
+    // for every j with this toolchain
+    unsigned xs[TPW][4], ws[EP][4];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const u32x4 v = t0 + t < T ? *reinterpret_cast<const u32x4 *>(x + (size_t)(t0 + t) * d + c * 8)
+                                 : u32x4{0u, 0u, 0u, 0u};
+      xs[t][0] = v.x; xs[t][1] = v.y; xs[t][2] = v.z; xs[t][3] = v.w;
+    }
+#pragma unroll
+    for (int e = 0; e < EP; ++e) {
+      const u32x4 v = e < E ? *reinterpret_cast<const u32x4 *>(wr + (size_t)e * d + c * 8)
+                            : u32x4{0u, 0u, 0u, 0u};
+      ws[e][0] = v.x; ws[e][1] = v.y; ws[e][2] = v.z; ws[e][3] = v.w;
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < EP; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          a[t * EP + e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xs[t][j]),
+                                                          __builtin_bit_cast(bf16x2, ws[e][j]),
+                                                          a[t * EP + e], false);
+  }
+  // reduce-scatter: at offset o a lane keeps the half of its values whose
+  // index has bit o equal to its own and adds the partner's copy of them
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const bool hi = (lane & o) != 0;
+#pragma unroll
+    for (int i = 0; i < o; ++i) {
+      const float send = hi ? a[i] : a[o + i];
+      const float keep = hi ? a[o + i] : a[i];
+      a[i] = keep + __shfl_xor(send, o, kWave);
+    }
+  }
+  s_red[wv][lane] = a[0];
+  __syncthreads();
+  if (wv != 0) return;
+  float v = ((s_red[0][lane] + s_red[1][lane]) + s_red[2][lane]) + s_red[3][lane];
+  const int e = lane % EP, t = t0 + lane / EP;
+  const bool ok = t < T && e < E;
+  if (ok) {
+    if (bias) v += bias[e];
+    if (logits_out) logits_out[(size_t)t * E + e] = v;
+  } else {
+    v = -INFINITY;
+  }
+  float mx = v;
+#pragma unroll
+  for (int o = EP / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  float z = ok ? expf(v - mx) : 0.f;
+#pragma unroll
+  for (int o = EP / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kWave);
+  bool taken = false;
+  float my_w = 0.f;
+  int my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = (ok && !taken) ? v : -INFINITY;
+    int be = (ok && !taken) ? e : 0x7fffffff;
+#pragma unroll
+    for (int o = EP / 2; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oe = __shfl_xor(be, o, kWave);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if (be == e) taken = true;
+    if (e == j) {
+      my_idx = be;
+      my_w = expf(bv - mx) / z;
+    }
+  }
+  if (renorm) {
+    float sw = e < k ? my_w : 0.f;
+#pragma unroll
+    for (int o = EP / 2; o > 0; o >>= 1) sw += __shfl_xor(sw, o, kWave);
+    my_w = my_w / sw;
+  }
+  if (t < T && e < k) {
+    topk_idx[(size_t)t * k + e] = my_idx;
+    topk_w[(size_t)t * k + e] = my_w;
+  }
+}
+
 template <int W, int NPER>
 void launch_select_t(const float *part, int S, const float *bias, int T, int E, int k, int renorm,
                      float *logits_out, int32_t *topk_idx, float *topk_w, hipStream_t s) {
@@ -292,6 +407,20 @@ hipError_t launch_route(const void *x, const void *w_router, int dt, const float
   const dim3 block(kThreads);
   if (flags & MOE_ROUTE_FROM_LOGITS) {
     launch_select(logits, 1, nullptr, T, E, k, renorm, nullptr, topk_idx, topk_w, s);
+    return hipGetLastError();
+  }
+  if (dt == MOE_BF16 && E <= 32) {
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    const uint16_t *wb = static_cast<const uint16_t *>(w_router);
+    if (E <= 8)
+      hipLaunchKernelGGL(route_fused_small<8>, dim3((T + 7) / 8), block, 0, s, xb, wb, bias, T, d,
+                         E, k, renorm, logits, topk_idx, topk_w);
+    else if (E <= 16)
+      hipLaunchKernelGGL(route_fused_small<16>, dim3((T + 3) / 4), block, 0, s, xb, wb, bias, T, d,
+                         E, k, renorm, logits, topk_idx, topk_w);
+    else
+      hipLaunchKernelGGL(route_fused_small<32>, dim3((T + 1) / 2), block, 0, s, xb, wb, bias, T, d,
+                         E, k, renorm, logits, topk_idx, topk_w);
     return hipGetLastError();
   }
   int S = 1;

@@ -96,6 +96,13 @@ def check_selection(idx, lg_ref, bound, k):
     # 64-expert tiles, three token tiles with a ragged tail, d-slices of
     # unequal step counts
     ("bf16", 257, 2056, 48, 4, False),
+    # one-launch path for E <= 32: 16-lane segments, 25 column chunks split
+    # unevenly over the four waves, ragged token tail
+    ("bf16", 129, 200, 16, 4, True),
+    # 32-lane segments (E = 30 leaves two idle lanes per token)
+    ("bf16", 65, 512, 30, 5, False),
+    # E < 8 in 8-lane segments, d = 2048 (one chunk per lane and wave)
+    ("bf16", 9, 2048, 5, 2, True),
 ])
 def test_scoring_and_selection(orc, dt, T, d, E, k, bias):
     a = api()
@@ -116,6 +123,11 @@ def test_scoring_and_selection(orc, dt, T, d, E, k, bias):
     dev_max = np.abs(got - lg_ref).max(axis=1)
     bound = bound_el.max(axis=1)
     gi = idx.cpu().numpy()
+    # given the GPU's own fp32 logits, the selection is exact (ties to the
+    # lower index) and the weights are their softmax
+    ridx, rw = orc.topk(logits.cpu().numpy(), k)
+    np.testing.assert_array_equal(gi, ridx)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, atol=1e-6, rtol=1e-5)
     n_ambig = check_selection(gi, lg_ref, dev_max, k)
     assert n_ambig <= max(2, T // 50)
     # weights: softmax of the oracle logits at the GPU's selection
@@ -141,3 +153,26 @@ def test_route_is_deterministic():
         outs.append((lg.cpu(), idx.cpu(), w.cpu()))
     for u, v in zip(*outs):
         assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("T,d,E,k", [(300, 4096, 8, 2), (77, 1024, 32, 6), (1000, 7168, 256, 8)])
+def test_renorm_without_logits_matches_logits_run(orc, T, d, E, k):
+    """Both routing paths (one launch for E <= 32, split-K above): no logits
+    output and renormalised weights give the same experts as a run that
+    exports the logits, and weights that are the oracle's renormalised
+    softmax of those logits."""
+    a = api()
+    x = synth.randn((T, d), 1.0, 31 + T, DEV, torch.bfloat16)
+    wr = synth.randn((E, d), 0.02, 32 + E, DEV, torch.bfloat16)
+    lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    idx1 = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w1 = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    a.moe_route(x, wr, idx1, w1, logits=lg)
+    idx2 = torch.empty_like(idx1)
+    w2 = torch.empty_like(w1)
+    a.moe_route(x, wr, idx2, w2, flags=a.MOE_ROUTE_RENORM)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
+    ridx, rw = orc.topk(lg.cpu().numpy(), k, renorm=True)
+    np.testing.assert_array_equal(idx2.cpu().numpy(), ridx)
+    np.testing.assert_allclose(w2.cpu().numpy(), rw, atol=1e-6, rtol=1e-5)
