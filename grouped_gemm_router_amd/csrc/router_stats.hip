@@ -9,20 +9,21 @@
 // §2.3: entropy -sum q_i log2(q_i + 1e-8) of the count distribution q.
 //
 // Two launches, no atomics (the results are bit-identical run to run):
-//   partial  one workgroup per 64 tokens: the softmax maximum and
+//   partial  one workgroup per 16 tokens: the softmax maximum and
 //            normaliser of each token (as the router takes them; several
 //            tokens per wave when E <= 64), then per expert the sum of
 //            p[t][e] over the block's tokens, split over token slices that
 //            are added in a fixed order, into the workspace [block][E];
-//   final    one workgroup: P_e = (sum over blocks in order) / T, f_e, and
-//            the three scalars through fixed-order block reductions.
+//   final    one workgroup: P_e = (sum over blocks, split over up to 1024/E
+//            threads per expert and recombined in a fixed order) / T, f_e,
+//            and the three scalars through fixed-order block reductions.
 #include "moe_internal.h"
 
 namespace {
 
 using namespace moe;
 
-constexpr int kRB = 64;         // tokens per partial block
+constexpr int kRB = 16;         // tokens per partial block (256 blocks at T = 4096)
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kMaxPerLane = MOE_MAX_EXPERTS / kWave;
 
@@ -144,10 +145,32 @@ __global__ __launch_bounds__(1024) void stats_final_kernel(const float *__restri
                                                            float *__restrict__ P,
                                                            float *__restrict__ summary) {
   __shared__ float s_wave[16];
+  __shared__ float s_part[1024];
+  // R threads per expert: thread (r, e) sums blocks r, r + R, ... in order
+  // (eight loads in flight), then thread r = 0 adds the R sums in r order
+  const int R = max(1, min(1024 / E, nblk));
+  {
+    const int ee = threadIdx.x % E, r = threadIdx.x / E;
+    if (r < R && (int)threadIdx.x < R * E) {
+      float acc = 0.f;
+      for (int b0 = r; b0 < nblk; b0 += 8 * R) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int b = b0 + i * R;
+          v[i] = b < nblk ? part[(size_t)b * E + ee] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += v[i];
+      }
+      s_part[r * E + ee] = acc;
+    }
+  }
+  __syncthreads();
   const int e = threadIdx.x;
   float p = 0.f, fe = 0.f, c = 0.f;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) p += part[(size_t)b * E + e];
+    for (int r = 0; r < R; ++r) p += s_part[r * E + e];
     p /= (float)T;
     c = (float)counts[e];
     fe = c / ((float)T * (float)k);

@@ -195,7 +195,7 @@ def test_permute_capped_validation(lib):
 
 def test_router_stats_validation(lib):
     need = lib.moe_router_stats_workspace_size(4096, 256)
-    assert need == 64 * 256 * 4
+    assert need == (4096 // 16) * 256 * 4   # one fp32 row of E per 16-token block
     s = lambda T, E, k, wsb: lib.moe_router_stats(P, P, T, E, k, 0.01, P, P, P, P2, wsb, NUL)  # noqa: E731
     assert s(4096, 256, 0, need) == INVALID     # k < 1
     assert s(4096, 2000, 8, 1 << 30) == UNSUPPORTED
