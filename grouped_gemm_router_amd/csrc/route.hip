@@ -259,30 +259,29 @@ __global__ __launch_bounds__(kThreads) void route_select(
 
 // Small E (<= 32, bf16): scoring, softmax and top-k in one launch, no
 // workspace.  A workgroup takes TPW = 64 / EP tokens (EP = E rounded up to
-// 8, 16 or 32) and its eight waves split the d axis (a 4096-wide row is one
-// 16-byte chunk per lane, so every load is in flight at once); a lane
-// accumulates the bf16 dot products (v_dot2c_f32_bf16) of every (token,
-// expert) pair over its chunks, the token and weight chunks of a step all
+// 8, 16 or 32) and its four waves split the d axis; a lane accumulates the
+// bf16 dot products (v_dot2c_f32_bf16) of every (token, expert) pair over
+// its 16-byte column chunks, with the token and weight chunks of a step all
 // loaded before use.  A butterfly reduce-scatter over the wave (each value
 // added in exactly one lane, fixed pairing) leaves lane l with value l =
-// token l / EP, expert l % EP; the waves' values are added in wave order
-// through LDS, and wave 0 finishes like the select kernel with one token per
-// EP-lane segment.
+// token l / EP, expert l % EP; the four waves' values are added in wave
+// order through LDS, and wave 0 finishes like the select kernel with one
+// token per EP-lane segment.  Measured on the Mixtral shapes: 13.9 us;
+// eight waves 17.6 us (each wave pays the reduce-scatter); two chunks per
+// step 15.1 us (201 registers, lower occupancy).
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kFusedWaves = 8;
-
 template <int EP>
-__global__ __launch_bounds__(kFusedWaves * kWave) void route_fused_small(
+__global__ __launch_bounds__(kThreads) void route_fused_small(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const float *__restrict__ bias, int T, int d, int E, int k, int renorm,
     float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w) {
   constexpr int TPW = kWave / EP;  // tokens per workgroup
-  __shared__ float s_red[kFusedWaves][kWave];
+  __shared__ float s_red[kThreads / kWave][kWave];
   const int lane = lane_id(), wv = threadIdx.x / kWave;
   const int t0 = blockIdx.x * TPW;
   const int nch = d / 8;  // 16-byte chunks per row
-  const int c_lo = wv * nch / kFusedWaves, c_hi = (wv + 1) * nch / kFusedWaves;
+  const int c_lo = wv * nch / 4, c_hi = (wv + 1) * nch / 4;
   float a[kWave];  // [t][e] partial dot products
 #pragma unroll
   for (int i = 0; i < kWave; ++i) a[i] = 0.f;
@@ -328,9 +327,7 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void route_fused_small(
   s_red[wv][lane] = a[0];
   __syncthreads();
   if (wv != 0) return;
-  float v = s_red[0][lane];
-#pragma unroll
-  for (int w = 1; w < kFusedWaves; ++w) v += s_red[w][lane];  // wave order
+  float v = ((s_red[0][lane] + s_red[1][lane]) + s_red[2][lane]) + s_red[3][lane];
   const int e = lane % EP, t = t0 + lane / EP;
   const bool ok = t < T && e < E;
   if (ok) {
@@ -417,16 +414,15 @@ hipError_t launch_route(const void *x, const void *w_router, int dt, const float
   if (dt == MOE_BF16 && E <= 32) {
     const uint16_t *xb = static_cast<const uint16_t *>(x);
     const uint16_t *wb = static_cast<const uint16_t *>(w_router);
-    const dim3 fb(kFusedWaves * kWave);
     if (E <= 8)
-      hipLaunchKernelGGL(route_fused_small<8>, dim3((T + 7) / 8), fb, 0, s, xb, wb, bias, T, d, E,
-                         k, renorm, logits, topk_idx, topk_w);
+      hipLaunchKernelGGL(route_fused_small<8>, dim3((T + 7) / 8), block, 0, s, xb, wb, bias, T, d,
+                         E, k, renorm, logits, topk_idx, topk_w);
     else if (E <= 16)
-      hipLaunchKernelGGL(route_fused_small<16>, dim3((T + 3) / 4), fb, 0, s, xb, wb, bias, T, d, E,
-                         k, renorm, logits, topk_idx, topk_w);
+      hipLaunchKernelGGL(route_fused_small<16>, dim3((T + 3) / 4), block, 0, s, xb, wb, bias, T, d,
+                         E, k, renorm, logits, topk_idx, topk_w);
     else
-      hipLaunchKernelGGL(route_fused_small<32>, dim3((T + 1) / 2), fb, 0, s, xb, wb, bias, T, d, E,
-                         k, renorm, logits, topk_idx, topk_w);
+      hipLaunchKernelGGL(route_fused_small<32>, dim3((T + 1) / 2), block, 0, s, xb, wb, bias, T, d,
+                         E, k, renorm, logits, topk_idx, topk_w);
     return hipGetLastError();
   }
   int S = 1;
