@@ -60,6 +60,18 @@ __device__ __forceinline__ int b_row(int wn, int nb) {
   return SWIGLU ? nb * 128 + wn * 32 : wn * 64 + nb * 32;
 }
 
+// Output conversions of the epilogues.  silu uses the hardware exp2 and
+// reciprocal (each within 1 ulp), far below the bf16 / E4M3 rounding that
+// follows; E4M3 codes come from e4m3x4 (the per-row scale keeps the values
+// in [-448, 448]); bf16 from the hardware round-to-nearest-even conversion.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * g)) * u;
+}
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
 // s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -186,6 +198,11 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+  // tiles of at most 128 rows have the registers to chain the two MFMAs of
+  // a 128-column scale block and fold once per block (the fold is VALU work
+  // that bounds this kernel); taller tiles fold after every MFMA
+  constexpr bool FOLD2 = BM <= 128;
+  f32x16 pt[FOLD2 ? MI : 1][NB];
   const int fr = lane & 31, fh = lane >> 5;
   const int KT = K / BK;  // a multiple of 4
 
@@ -217,11 +234,16 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
       const i32x8 x = frag(ring.a[st], r, fh);                                              \
       if (((st) & 1) == 0) sa[mi] = ring.sa[(st) >> 1][(r >> 5) * 64 + (r & 31)];           \
       _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                   \
-        const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                   \
-            w[nb], x, f32x16{}, 0, 0, 0, 127, 0, 127);                                      \
-        const float c = sa[mi] * (nb == 0 ? s0 : s1);                                       \
-        _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2)                                   \
-          acc[mi][nb][r2] = fmaf(p[r2], c, acc[mi][nb][r2]);                                \
+        if (FOLD2 && ((st) & 1) == 0) {                                                     \
+          pt[FOLD2 ? mi : 0][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(         \
+              w[nb], x, f32x16{}, 0, 0, 0, 127, 0, 127);                                    \
+        } else {                                                                            \
+          const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                 \
+              w[nb], x, FOLD2 ? pt[FOLD2 ? mi : 0][nb] : f32x16{}, 0, 0, 0, 127, 0, 127);   \
+          const float c = sa[mi] * (nb == 0 ? s0 : s1);                                     \
+          _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2)                                 \
+            acc[mi][nb][r2] = fmaf(p[r2], c, acc[mi][nb][r2]);                              \
+        }                                                                                   \
       }                                                                                     \
     }                                                                                       \
   }
@@ -249,8 +271,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
       float mx = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float g = acc[mi][0][r], u = acc[mi][1][r];
-        h[r] = g / (1.0f + expf(-g)) * u;
+        h[r] = silu_mul(acc[mi][0][r], acc[mi][1][r]);
         mx = fmaxf(mx, fabsf(h[r]));
       }
       if (OUT_FP8) {
@@ -260,9 +281,8 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = tile.nt * 128 + wn * 32 + 8 * j + 4 * fh;
-          const uint32_t lo = f32_to_bf16_bits(h[4 * j]) | ((uint32_t)f32_to_bf16_bits(h[4 * j + 1]) << 16);
-          const uint32_t hi = f32_to_bf16_bits(h[4 * j + 2]) | ((uint32_t)f32_to_bf16_bits(h[4 * j + 3]) << 16);
-          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(C) + (size_t)m * N + n) = uint2{lo, hi};
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(C) + (size_t)m * N + n) =
+              uint2{bf16x2_bits(h[4 * j], h[4 * j + 1]), bf16x2_bits(h[4 * j + 2], h[4 * j + 3])};
         }
       }
       if (OUT_FP8) {
@@ -272,14 +292,13 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
         const float amax = fmaxf(fmaxf(ring.amax[ml], ring.amax[BM_MAX + ml]),
                                  fmaxf(ring.amax[2 * BM_MAX + ml], ring.amax[3 * BM_MAX + ml]));
         const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+        const float inv = 1.0f / sc;
         if (m < tile.mend) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int n = tile.nt * 128 + wn * 32 + 8 * j + 4 * fh;
-            const uint32_t q = f32_to_e4m3(h[4 * j] / sc) | (f32_to_e4m3(h[4 * j + 1] / sc) << 8) |
-                               (f32_to_e4m3(h[4 * j + 2] / sc) << 16) |
-                               (f32_to_e4m3(h[4 * j + 3] / sc) << 24);
-            *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(C) + (size_t)m * N + n) = q;
+            *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(C) + (size_t)m * N + n) =
+                e4m3x4(h[4 * j] * inv, h[4 * j + 1] * inv, h[4 * j + 2] * inv, h[4 * j + 3] * inv);
           }
           if (wn == 0 && fh == 0) Cs[(size_t)tile.nt * rows + m] = sc;
         }
@@ -319,13 +338,12 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
           const float v[4] = {acc[mi][nb][4 * j], acc[mi][nb][4 * j + 1],
                               acc[mi][nb][4 * j + 2], acc[mi][nb][4 * j + 3]};
           if (OUT_FP8) {
-            const uint32_t q = f32_to_e4m3(v[0] / sc) | (f32_to_e4m3(v[1] / sc) << 8) |
-                               (f32_to_e4m3(v[2] / sc) << 16) | (f32_to_e4m3(v[3] / sc) << 24);
-            *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(C) + (size_t)m * N + n) = q;
+            const float inv = 1.0f / sc;
+            *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(C) + (size_t)m * N + n) =
+                e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
           } else {
-            const uint32_t lo = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-            const uint32_t hi = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(C) + (size_t)m * N + n) = uint2{lo, hi};
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(C) + (size_t)m * N + n) =
+                uint2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
           }
         }
       if (OUT_FP8 && wn % 2 == 0 && fh == 0) Cs[(size_t)(tile.nt * 2 + wn / 2) * rows + m] = sc;

@@ -291,12 +291,10 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[h][i]));
         amax = group_max(amax, 16);
         const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[h][i] / sc) << (8 * i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[h][4 + i] / sc) << (8 * i);
-        const uint2 q = make_uint2(lo, hi);
+        // v / sc is at most 448 in magnitude, so the hardware conversion
+        // gives exactly the codes of f32_to_e4m3
+        const uint2 q = make_uint2(e4m3x4(v[h][0] / sc, v[h][1] / sc, v[h][2] / sc, v[h][3] / sc),
+                                   e4m3x4(v[h][4] / sc, v[h][5] / sc, v[h][6] / sc, v[h][7] / sc));
         if (ok) {
           for (int j = 0; j < k + n_shared; ++j) {
             size_t row;

@@ -1,4 +1,7 @@
-"""HBM traffic of one kernel from rocprofv3 counter passes.
+"""Summaries of rocprofv3 runs for profiles/: the HBM traffic of one kernel
+from counter passes, and a per-kernel table of a kernel trace.
+
+HBM traffic.
 
 Two `rocprofv3 --pmc` runs of `bench.py --calib-copy` (one with FETCH_SIZE,
 one with WRITE_SIZE; the counters are KiB per dispatch) give the bytes a
@@ -11,6 +14,15 @@ uses it only while the sources are unchanged.
     python -m grouped_gemm_router_amd.profiling \\
         --fetch <dir>/f_counter_collection.csv --write <dir>/w_counter_collection.csv \\
         --kernel gemm_gate_up --config mixtral_bf16 --out profiles/traffic_gemm_gate_up_mixtral_bf16
+
+Kernel trace.  `--stats <dir>/<cfg>_kernel_stats.csv` (from `rocprofv3
+--kernel-trace --stats`) becomes a markdown table of the layer's kernels
+(calls, average / min / max duration); the kernels that generate the
+synthetic inputs are summed into one line.
+
+    python -m grouped_gemm_router_amd.profiling --stats <dir>/mixtral_bf16_kernel_stats.csv \\
+        --config mixtral_bf16 --command "<the rocprofv3 command>" \\
+        --out profiles/kernel_trace_moe_layer_mixtral_bf16.md
 """
 from __future__ import annotations
 
@@ -93,14 +105,51 @@ def traffic_record(fetch_csv: str, write_csv: str, kernel: str, config: str) -> 
     }
 
 
+# kernels of this library (everything else in a bench trace generates inputs)
+LIBRARY_KERNELS = re.compile(r"route_|perm_|gemm_|split_reduce|combine_|stats_|quantize")
+
+
+def trace_summary(stats_csv: str, config: str, command: str) -> str:
+    """Markdown table of a rocprofv3 kernel_stats.csv."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# Kernel trace: MoE layer step, %s" % config, "",
+             "Command (from /tmp, `$REPO` = repository root, one MI355X):", "",
+             "```", command, "```", "",
+             "| Kernel | Calls | Avg (us) | Min (us) | Max (us) |", "|---|---|---|---|---|"]
+    other_calls, other_ns = 0, 0.0
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+        if not LIBRARY_KERNELS.search(name.split("(")[0]):
+            other_calls += int(r["Calls"])
+            other_ns += float(r["TotalDurationNs"])
+            continue
+        lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (
+            name.split("(")[0], r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    lines += ["", "Input generation and copies outside the layer (torch kernels): %d calls, "
+              "%.1f ms in total." % (other_calls, other_ns / 1e6), ""]
+    return "\n".join(lines)
+
+
 def main() -> None:
     p = argparse.ArgumentParser()
-    p.add_argument("--fetch", required=True, help="counter_collection.csv of the FETCH_SIZE pass")
-    p.add_argument("--write", required=True, help="counter_collection.csv of the WRITE_SIZE pass")
-    p.add_argument("--kernel", required=True, choices=sorted(KERNEL_PATTERNS))
+    p.add_argument("--fetch", help="counter_collection.csv of the FETCH_SIZE pass")
+    p.add_argument("--write", help="counter_collection.csv of the WRITE_SIZE pass")
+    p.add_argument("--kernel", choices=sorted(KERNEL_PATTERNS))
+    p.add_argument("--stats", help="kernel_stats.csv of a kernel trace")
+    p.add_argument("--command", help="the rocprofv3 command of the trace")
     p.add_argument("--config", required=True)
-    p.add_argument("--out", required=True, help="output path without extension (.json + .md)")
+    p.add_argument("--out", required=True,
+                   help="traffic: output path without extension (.json); trace: the .md path")
     a = p.parse_args()
+    if a.stats:
+        text = trace_summary(a.stats, a.config, a.command or "")
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text)
+        return
+    if not (a.fetch and a.write and a.kernel):
+        p.error("traffic needs --fetch, --write and --kernel")
     rec = traffic_record(a.fetch, a.write, a.kernel, a.config)
     with open(a.out + ".json", "w") as f:
         json.dump(rec, f, indent=1)

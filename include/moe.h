@@ -257,7 +257,9 @@ size_t moe_grouped_gemm_workspace_size(int G, int rows, int N, int K,
  *       sum_kb A_scale[kb][r] B_scale[g][n/128][kb] * (sum_{k in kb} A_q B_q)
  *   with fp32 accumulation.
  * c_dt == MOE_BF16 writes bf16.  c_dt == MOE_E4M3 quantises each output row
- * in 1 x 128 groups exactly as moe_permute does and writes C_scale
+ * in 1 x 128 groups with the scale absmax / 448, as moe_permute does (the
+ * values are multiplied by the reciprocal of the scale, so a code can differ
+ * from a division's in the last rounding), and writes C_scale
  * [N/128][rows] (group-major, like A_scale, so it feeds the next GEMM);
  * C_scale must be NULL otherwise.
  * Requires N % 128 == 0 and K % 128 == 0.
