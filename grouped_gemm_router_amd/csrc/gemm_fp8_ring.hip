@@ -108,7 +108,7 @@ struct Ring {
   float *amax;  // [NWN][BM_MAX]
 };
 
-template <int BM, bool SWIGLU, bool OUT_FP8>
+template <int BM, bool SWIGLU, bool OUT_FP8, bool SKIP>
 __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__restrict__ Aq,
                                          const float *__restrict__ As,
                                          const uint8_t *__restrict__ Bq,
@@ -127,6 +127,15 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
 
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
   const int wm = wv / NWN, wn = wv % NWN;
+  // SKIP (a tile with fewer than BM rows): this wave's 32-row blocks that
+  // hold rows of the group; blocks past the group end are neither read nor
+  // multiplied nor folded.  Each SIMD runs one wave of each wave row, so the
+  // work saved in the mostly empty second wave row shortens the tile.
+  int live = MI;
+  if (SKIP) {
+    const int hv = __builtin_amdgcn_readfirstlane(tile.mend - tile.m0 - wm * (MI * 32));
+    live = hv <= 0 ? 0 : min(MI, (hv + 31) / 32);
+  }
   const int KB = K / 128, NBK = N / 128;  // scale blocks along K and N
 
   // LDS-direct sources (see the bf16 kernel for the slot layout): a
@@ -230,6 +239,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
     _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                       \
       w[nb] = frag(ring.b[st], b_row<SWIGLU>(wn, nb) + fr, fh);                             \
     _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) {                                     \
+      if (mi >= live) break;                                                                \
       const int r = wm * (MI * 32) + mi * 32 + fr;                                          \
       const i32x8 x = frag(ring.a[st], r, fh);                                              \
       if (((st) & 1) == 0) sa[mi] = ring.sa[(st) >> 1][(r >> 5) * 64 + (r & 31)];           \
@@ -371,12 +381,14 @@ __global__ __launch_bounds__(NTH, 1) void gemm_fp8_ring_kernel(
   const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM_MAX, nt_count, kTileChunk);
   const Ring ring{{sA0, sA1, sA2, sA3}, {sB0, sB1, sB2, sB3}, {sS0, sS1}, s_amax};
   const int h = tile.mend - tile.m0;  // wave-uniform
-  if (h > 128)
-    run_tile<256, SWIGLU, OUT_FP8>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+  if (h == 256)
+    run_tile<256, SWIGLU, OUT_FP8, false>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+  else if (h > 128)
+    run_tile<256, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
   else if (h > 64)
-    run_tile<128, SWIGLU, OUT_FP8>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+    run_tile<128, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
   else
-    run_tile<64, SWIGLU, OUT_FP8>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+    run_tile<64, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
 }
 
 }  // namespace
