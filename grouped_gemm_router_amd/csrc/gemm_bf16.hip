@@ -415,12 +415,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   // after every wave has passed the prologue barrier.
   __shared__ u32x4 sA0[SLOTS_MAX], sA1[SLOTS_MAX], sA2[SLOTS_MAX], sA3[SLOTS_MAX];
   __shared__ u32x4 sB0[SLOTS_B2], sB1[SLOTS_B2], sB2[SLOTS_B2];
-  static_assert(sizeof(int) * (MOE_MAX_GROUPS + 1 + NW) <= sizeof(u32x4) * SLOTS_B2,
+  static_assert(sizeof(int) * (2 * (MOE_MAX_GROUPS + 1) + NW) <= sizeof(u32x4) * SLOTS_B2,
                 "scheduler table must fit in one B slot");
   int *s_cum = reinterpret_cast<int *>(sB2);
-  int *s_tmp = s_cum + MOE_MAX_GROUPS + 1;
+  int *s_off = s_cum + MOE_MAX_GROUPS + 1;
+  int *s_tmp = s_off + MOE_MAX_GROUPS + 1;
 
-  sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_tmp);
+  sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_tmp, s_off);
   const int total = s_cum[G] * nt_count;
   const int KT = K / BK;  // a multiple of 4
   const int S = ws != nullptr ? split_slices(total, cus, KT) : 1;
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
     part = reinterpret_cast<float *>(ws + split_partial_offset(cus)) +
            (size_t)(j * S + slice) * kPartialFloats;
   }
-  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM_MAX, nt_count, kTileChunk);
+  const Tile tile = sched_tile(L, s_cum, s_off, G, BM_MAX, nt_count, kTileChunk);
   if (part != nullptr && slice == 0 && threadIdx.x == 0)
     reinterpret_cast<int4 *>(ws + split_desc_offset())[j] = make_int4(tile.m0, tile.mend, tile.nt, 0);
   const int h = tile.mend - tile.m0;  // wave-uniform

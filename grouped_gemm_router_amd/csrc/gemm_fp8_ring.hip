@@ -373,12 +373,13 @@ __global__ __launch_bounds__(NTH, 1) void gemm_fp8_ring_kernel(
   __shared__ float s_amax[OUT_FP8 ? NWN * BM_MAX : 1];
   __shared__ int s_cum[MOE_MAX_GROUPS + 1];
   __shared__ int s_tmp[NW];
+  __shared__ int s_off[MOE_MAX_GROUPS + 1];
 
-  sched_build<NTH>(offsets, G, rows, BM_MAX, s_cum, s_tmp);
+  sched_build<NTH>(offsets, G, rows, BM_MAX, s_cum, s_tmp, s_off);
   const int total = s_cum[G] * nt_count;
   const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, G, offsets, rows, BM_MAX, nt_count, kTileChunk);
+  const Tile tile = sched_tile(L, s_cum, s_off, G, BM_MAX, nt_count, kTileChunk);
   const Ring ring{{sA0, sA1, sA2, sA3}, {sB0, sB1, sB2, sB3}, {sS0, sS1}, s_amax};
   const int h = tile.mend - tile.m0;  // wave-uniform
   if (h == 256)

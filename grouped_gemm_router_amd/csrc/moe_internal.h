@@ -108,11 +108,12 @@ struct TileSched {
   int total;  // number of (row tile, column tile) pairs
 };
 
-// Block-wide: fills cum[0..G] (LDS, G+1 ints) from the device offsets array.
-// Must be called by all threads of the block.
+// Block-wide: fills cum[0..G] (LDS, G+1 ints) from the device offsets array,
+// and off[0..G] (LDS) with the offsets clamped to [0, rows], so a tile lookup
+// needs no further global read.  Must be called by all threads of the block.
 template <int NTHREADS>
 __device__ __forceinline__ void sched_build(const int32_t *__restrict__ offsets, int G,
-                                            int rows, int BM, int *cum, int *s_tmp) {
+                                            int rows, int BM, int *cum, int *s_tmp, int *off) {
   // each thread owns a contiguous run of groups
   const int tid = threadIdx.x;
   const int per = (G + NTHREADS - 1) / NTHREADS;
@@ -148,6 +149,8 @@ __device__ __forceinline__ void sched_build(const int32_t *__restrict__ offsets,
       int b = min(max(offsets[g + 1], 0), rows);
       int m = max(b - a, 0);
       run += (m + BM - 1) / BM;
+      off[g] = a;
+      if (g == G - 1) off[G] = b;
     }
   }
   if (tid == NTHREADS - 1) cum[G] = run;
@@ -161,10 +164,9 @@ struct Tile {
   int nt;    // column tile index
 };
 
-// Maps a linear tile id to (group, rows, column tile).  cum is the LDS table
-// from sched_build; nt_count column tiles per row tile.
-__device__ __forceinline__ Tile sched_tile(int L, const int *cum, int G,
-                                           const int32_t *__restrict__ offsets, int rows,
+// Maps a linear tile id to (group, rows, column tile).  cum and off are the
+// LDS tables from sched_build; nt_count column tiles per row tile.
+__device__ __forceinline__ Tile sched_tile(int L, const int *cum, const int *off, int G,
                                            int BM, int nt_count, int chunk) {
   // find g with cum[g] * nt_count <= L < cum[g+1] * nt_count (binary search)
   int lo = 0, hi = G;  // invariant: cum[lo]*nt <= L < cum[hi]*nt
@@ -184,9 +186,8 @@ __device__ __forceinline__ Tile sched_tile(int L, const int *cum, int G,
   int nt = c * chunk + (within - mt * cw);
   Tile t;
   t.g = g;
-  int a = min(max(offsets[g], 0), rows);
-  int b = min(max(offsets[g + 1], 0), rows);
-  int mg = max(b - a, 0);
+  int a = off[g];
+  int mg = max(off[g + 1] - a, 0);
   t.m0 = a + mt * BM;
   t.mend = min(a + mg, t.m0 + BM);
   t.nt = nt;
