@@ -342,6 +342,24 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
         }
     return;
   }
+  if constexpr (OUT_F32 && !SWIGLU) {
+    // fp32 output: every store already writes whole 128-byte row pieces
+    // (32 lanes x 4 bytes), so no staging; measured against the staged
+    // path: DeepSeek-shape down 2.01 -> 1.97 ms, Mixtral-shape 0.94 -> 0.93
+    float *const cb = static_cast<float *>(C) + (size_t)tile.nt * BN + col;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = tile.m0 + wm * (MI * 32) + mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
+        if (m < tile.mend) {
+          float *const rp = cb + (size_t)m * N;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) rp[b_row<SWIGLU, NWN>(wn, nb)] = acc[mi][nb][r];
+        }
+      }
+    return;
+  }
   // Output, one 32-row block (mi) of every wave at a time: each wave writes
   // its values into LDS -- wave row wm into B slot wm, free once every wave
   // is past the last stage -- as [32 rows][TC columns] of the output type,
@@ -415,13 +433,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   // after every wave has passed the prologue barrier.
   __shared__ u32x4 sA0[SLOTS_MAX], sA1[SLOTS_MAX], sA2[SLOTS_MAX], sA3[SLOTS_MAX];
   __shared__ u32x4 sB0[SLOTS_B2], sB1[SLOTS_B2], sB2[SLOTS_B2];
-  static_assert(sizeof(int) * (2 * (MOE_MAX_GROUPS + 1) + NW) <= sizeof(u32x4) * SLOTS_B2,
+  static_assert(sizeof(int) * (3 * (MOE_MAX_GROUPS + 1) + NW) <= sizeof(u32x4) * SLOTS_B2,
                 "scheduler table must fit in one B slot");
   int *s_cum = reinterpret_cast<int *>(sB2);
   int *s_off = s_cum + MOE_MAX_GROUPS + 1;
-  int *s_tmp = s_off + MOE_MAX_GROUPS + 1;
+  int *s_ord = s_off + MOE_MAX_GROUPS + 1;
+  int *s_tmp = s_ord + MOE_MAX_GROUPS;
 
-  sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_tmp, s_off);
+  sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_tmp, s_off, s_ord, SWIGLU);
   const int total = s_cum[G] * nt_count;
   const int KT = K / BK;  // a multiple of 4
   const int S = ws != nullptr ? split_slices(total, cus, KT) : 1;
@@ -445,7 +464,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
     part = reinterpret_cast<float *>(ws + split_partial_offset(cus)) +
            (size_t)(j * S + slice) * kPartialFloats;
   }
-  const Tile tile = sched_tile(L, s_cum, s_off, G, BM_MAX, nt_count, kTileChunk);
+  const Tile tile = sched_tile(L, s_cum, s_ord, s_off, G, BM_MAX, nt_count, kTileChunk);
   if (part != nullptr && slice == 0 && threadIdx.x == 0)
     reinterpret_cast<int4 *>(ws + split_desc_offset())[j] = make_int4(tile.m0, tile.mend, tile.nt, 0);
   const int h = tile.mend - tile.m0;  // wave-uniform

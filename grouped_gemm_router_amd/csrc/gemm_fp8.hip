@@ -55,12 +55,13 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
   __shared__ int s_cum[MOE_MAX_GROUPS + 1];
   __shared__ int s_tmp[4];
   __shared__ int s_off[MOE_MAX_GROUPS + 1];
+  __shared__ int s_ord[MOE_MAX_GROUPS];
 
-  sched_build<FNTH>(offsets, G, rows, FBM, s_cum, s_tmp, s_off);
+  sched_build<FNTH>(offsets, G, rows, FBM, s_cum, s_tmp, s_off, s_ord, SWIGLU);
   const int total = s_cum[G] * nt_count;
   const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, s_off, G, FBM, nt_count, kTileChunk);
+  const Tile tile = sched_tile(L, s_cum, s_ord, s_off, G, FBM, nt_count, kTileChunk);
 
   const int tid = threadIdx.x;
   const int lane = lane_id(), wv = tid / kWave;

@@ -315,6 +315,39 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
         __syncthreads();  // the amax slots are rewritten for the next mi
       }
     }
+  } else if (!OUT_FP8) {
+    // bf16 output, staged per 32-token block: every wave writes its 32
+    // tokens x 64 columns into a [32 tokens][256 columns] block of LDS (wave
+    // row wm in B slot wm, free once every wave is past the last step), then
+    // all threads store whole 16-byte row pieces, where the direct stores
+    // would write 16 bytes into each of 32 rows per instruction.  The 16-byte
+    // piece index is XORed with the token row, so the reads are conflict free.
+    __syncthreads();
+    char *const stg = reinterpret_cast<char *>(wm == 0 ? ring.b[0] : ring.b[1]);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int pc = wn * 8 + nb * 4 + j;  // 16-byte piece of the staged row
+          *reinterpret_cast<uint2 *>(stg + fr * 512 + ((pc ^ fr) << 4) + fh * 8) =
+              uint2{bf16x2_bits(acc[mi][nb][4 * j], acc[mi][nb][4 * j + 1]),
+                    bf16x2_bits(acc[mi][nb][4 * j + 2], acc[mi][nb][4 * j + 3])};
+        }
+      __syncthreads();
+      for (int q = tid; q < 2 * 32 * 32; q += NTH) {
+        const int wr = q >> 10, rr = (q >> 5) & 31, pc = q & 31;
+        const int m = tile.m0 + wr * (MI * 32) + mi * 32 + rr;
+        const int n = tile.nt * 256 + pc * 8;
+        if (m < tile.mend && n < N)
+          *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(C) + (size_t)m * N + n) =
+              *reinterpret_cast<const u32x4 *>(
+                  reinterpret_cast<const char *>(wr == 0 ? ring.b[0] : ring.b[1]) + rr * 512 +
+                  ((pc ^ rr) << 4));
+      }
+      __syncthreads();  // the staging blocks are rewritten for the next mi
+    }
   } else {
     // columns nt*256 + 64 wn + 32 nb + 8 j + 4 fh + i; quantisation group
     // (E4M3 output) = wave columns {0,1} and {2,3}
@@ -374,12 +407,13 @@ __global__ __launch_bounds__(NTH, 1) void gemm_fp8_ring_kernel(
   __shared__ int s_cum[MOE_MAX_GROUPS + 1];
   __shared__ int s_tmp[NW];
   __shared__ int s_off[MOE_MAX_GROUPS + 1];
+  __shared__ int s_ord[MOE_MAX_GROUPS];
 
-  sched_build<NTH>(offsets, G, rows, BM_MAX, s_cum, s_tmp, s_off);
+  sched_build<NTH>(offsets, G, rows, BM_MAX, s_cum, s_tmp, s_off, s_ord, SWIGLU);
   const int total = s_cum[G] * nt_count;
   const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, s_off, G, BM_MAX, nt_count, kTileChunk);
+  const Tile tile = sched_tile(L, s_cum, s_ord, s_off, G, BM_MAX, nt_count, kTileChunk);
   const Ring ring{{sA0, sA1, sA2, sA3}, {sB0, sB1, sB2, sB3}, {sS0, sS1}, s_amax};
   const int h = tile.mend - tile.m0;  // wave-uniform
   if (h == 256)
