@@ -17,19 +17,21 @@
 //     staging registers), each step waits only for its own data (vmcnt) and
 //     meets the other waves at a plain s_barrier (no release fence, which
 //     would drain every in-flight load);
-//   * A (activations) runs through a 4-stage ring of 64-byte row pieces
-//     (4 x 16 KB), issued three steps ahead; B (weights) through a ring of
-//     three double stages (3 x 32 KB) of 128-byte row pieces, issued four to
-//     five steps ahead.  Whole 128-byte lines halve the L2 requests for B
-//     (the TCP sends one request per line touched), which is what bounds this
-//     kernel: measured on the Mixtral shapes, all-64-byte rings 1.91 / 1.08
-//     ms (gate/up / down), this mix 1.75 / 0.96 ms, and a 2-stage ring of
-//     128-byte pieces for both operands 2.25 / 1.39 ms (too little in
-//     flight).  The two rings fill the 160 KB of LDS;
-//   * A row = 64 B = 4 pieces, piece p of row r at slot p ^ ((r ^ (r >> 2))
-//     & 3); B row = 128 B = 8 pieces at slot p ^ ((r >> 1) & 7): the DMA
-//     writes whole rows and the MFMA fragment reads (16 rows x one piece per
-//     phase) hit distinct banks;
+//   * both operands move as whole 128-byte row pieces (two K steps): the
+//     TCP sends one L2 request per line touched, and the request count is
+//     what bounds this kernel.  A (activations) runs through a ring of two
+//     such double stages (2 x 32 KB), each refilled (odd steps) as soon as
+//     its second step has been read, so it lands two steps ahead of use; B
+//     (weights) through three (3 x 32 KB), refilled on even steps, four to
+//     five steps ahead.  Measured (gate/up / down): on the Mixtral shapes
+//     all-64-byte rings 1.91 / 1.08 ms, 64-byte A with 128-byte B 1.75 /
+//     0.96, then 128-byte A 1.67 / 0.91 (DeepSeek shapes 3.40 -> 3.20 /
+//     2.00 -> 1.97); a 2-stage ring for both operands 2.25 / 1.39 (too little
+//     in flight), and 64-deep steps with one barrier each were slower on the
+//     Mixtral shapes.  The two rings fill the 160 KB of LDS;
+//   * a row is 8 pieces of 16 bytes, piece p of row r at slot p ^ ((r >> 1)
+//     & 7): the DMA writes whole rows and the MFMA fragment reads (16 rows x
+//     one piece per phase) hit distinct banks;
 //   * fragments are double buffered in registers and the stage barrier sits
 //     in the middle of a stage, so the next stage's first fragments are read
 //     while this stage's second half of MFMAs runs; one LDS read is
@@ -54,12 +56,11 @@ namespace {
 using namespace moe;
 
 constexpr int BM_MAX = 256, BN = 256, BK = 32;
-constexpr int PIECES = BK / 8;             // 16-byte pieces per A tile row and stage
-constexpr int SLOTS_MAX = BM_MAX * PIECES; // 16-byte slots per A stage (16 KB at most)
-constexpr int PIECES_B = 2 * PIECES;       // B: 128-byte rows covering two stages
+constexpr int PIECES = BK / 8;             // 16-byte pieces per operand row and stage
+constexpr int PIECES_B = 2 * PIECES;       // 128-byte row pieces covering two stages
+constexpr int SLOTS_A2MAX = BM_MAX * PIECES_B; // 16-byte slots per A double stage (32 KB)
 constexpr int SLOTS_B2 = BN * PIECES_B;    // 16-byte slots per B double stage (32 KB)
 
-__device__ __forceinline__ int swz(int row, int p) { return p ^ ((row ^ (row >> 2)) & 3); }
 __device__ __forceinline__ int swzb(int row, int p) { return p ^ ((row >> 1) & 7); }
 
 // B-tile row of wave column wn (of NWN), 32-row block nb
@@ -78,6 +79,13 @@ __device__ __forceinline__ int b_row(int wn, int nb) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's LDS reads are complete too
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
   __builtin_amdgcn_s_waitcnt(imm);
 }
 
@@ -115,7 +123,7 @@ __device__ __forceinline__ void read_frag(Frag<MI, NB> &f, const u32x4 *tA, cons
   for (int mi = 0; mi < MI; ++mi) {
     if (mi >= live) break;
     const int r = wm * (MI * 32) + mi * 32 + fr;
-    f.a[mi] = __builtin_bit_cast(bf16x8, tA[r * PIECES + swz(r, pc)]);
+    f.a[mi] = __builtin_bit_cast(bf16x8, tA[r * PIECES_B + swzb(r, pb)]);
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -183,18 +191,13 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
                                          const uint16_t *__restrict__ B2, void *__restrict__ C,
                                          int rows, int N, int K, int kbeg, int KT,
                                          float *__restrict__ part, u32x4 *sA0, u32x4 *sA1,
-                                         u32x4 *sA2, u32x4 *sA3, u32x4 *sB0, u32x4 *sB1,
-                                         u32x4 *sB2) {
+                                         u32x4 *sB0, u32x4 *sB1, u32x4 *sB2) {
   constexpr int NWN = NW / 2;                 // wave columns (2 wave rows)
   constexpr int MI = BM / 64;                 // 32-row blocks per wave
   constexpr int NB = (BN / NWN) / 32;         // 32-column blocks per wave
-  constexpr int SLOTS_A = BM * PIECES;        // 16-byte slots per A stage
-  // A stage smaller than one 16-byte load per lane (64-row tile, 8 waves):
-  // load it 4 bytes per lane instead, so every wave issues the same count
-  constexpr bool A_DW = SLOTS_A < NW * 64;
-  constexpr int IA = A_DW ? (SLOTS_A * 4) / NW / 64 : SLOTS_A / NW / 64;
+  constexpr int SLOTS_A2 = BM * PIECES_B;     // 16-byte slots per A double stage
+  constexpr int IA = SLOTS_A2 / NW / 64;      // A DMA instructions per wave per double stage
   constexpr int IB = SLOTS_B2 / NW / 64;      // B DMA instructions per wave per double stage
-  constexpr int PER_STAGE = IA + IB;          // vmcnt units issued between two waits
   constexpr int NM = MI * NB;                 // MFMAs per 16-deep step
   constexpr int NR = MI + NB;                 // fragment reads per 16-deep step
   static_assert(IA >= 1 && IB >= 1, "tile too small for the wave count");
@@ -207,28 +210,18 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
     live = hv <= 0 ? 0 : min(MI, (hv + 31) / 32);
   }
 
-  // DMA sources.  16-byte mode: wave wv fills slots [wv*SLOTS/NW, +SLOTS/NW)
-  // of each operand stage, 64 slots per instruction; slot s holds piece
-  // swz(row, s % 4) of row s / 4.  4-byte mode (A only): instruction i of
-  // wave wv fills dwords [(wv*IA + i)*64, +64), dword q belonging to slot q/4.
-  const uint16_t *ga[IA];
+  // DMA sources: wave wv fills slots [wv*SLOTS/NW, +SLOTS/NW) of each
+  // operand double stage, 64 slots per instruction; slot s holds piece
+  // swzb(row, s % 8) of row s / 8.
   const uint16_t *gb[IB];
   const size_t goff = (size_t)tile.g * N * K + kbeg;
+  const uint16_t *ga[IA];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
-    int r, off;
-    if (A_DW) {
-      const int q = (wv * IA + i) * 64 + lane;
-      const int sl = q / 4;
-      r = sl / PIECES;
-      off = swz(r, sl % PIECES) * 8 + (q % 4) * 2;
-    } else {
-      const int sl = wv * (SLOTS_A / NW) + i * 64 + lane;
-      r = sl / PIECES;
-      off = swz(r, sl % PIECES) * 8;
-    }
+    const int sl = wv * (SLOTS_A2 / NW) + i * 64 + lane;
+    const int r = sl / PIECES_B;
     const int m = min(tile.m0 + r, rows - 1);
-    ga[i] = A + (size_t)m * K + kbeg + off;
+    ga[i] = A + (size_t)m * K + kbeg + swzb(r, sl % PIECES_B) * 8;
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
@@ -243,12 +236,12 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
     }
   }
   // LDS destinations of lane 0, in 16-byte units
-  const int dma_a = A_DW ? wv * IA * 16 : wv * (SLOTS_A / NW);
-  constexpr int STEP_A = A_DW ? 16 : 64;
+  const int dma_a = wv * (SLOTS_A2 / NW);
   const int dma_b = wv * (SLOTS_B2 / NW);
 #define MOE_ISSUE_A(dA, k0)                                                                \
   _Pragma("unroll") for (int i = 0; i < IA; ++i)                                          \
-    dma_to_lds<A_DW ? 4 : 16>(ga[i] + (k0), (dA) + dma_a + i * STEP_A);
+    __builtin_amdgcn_global_load_lds((const void *)(ga[i] + (k0)),                        \
+                                     (lds_void *)((dA) + dma_a + i * 64), 16, 0, 0);
 #define MOE_ISSUE_B(dB, k0)                                                                \
   _Pragma("unroll") for (int i = 0; i < IB; ++i)                                          \
     __builtin_amdgcn_global_load_lds((const void *)(gb[i] + (k0)),                        \
@@ -261,50 +254,56 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
   const int fr = lane & 31, fh = lane >> 5;
 
-  const int KT2 = KT / 2;  // B double stages
+  const int KT2 = KT / 2;  // double stages
   MOE_ISSUE_B(sB0, 0);
   MOE_ISSUE_A(sA0, 0);
-  MOE_ISSUE_A(sA1, BK);
   MOE_ISSUE_B(sB1, 2 * BK);
-  MOE_ISSUE_A(sA2, 2 * BK);
-  wait_vmcnt<2 * IA + IB>();  // A stage 0 and B stages 0-1 landed
+  MOE_ISSUE_A(sA1, 2 * BK);
+  wait_vmcnt<IA + IB>();  // A and B double stage 0 landed
   stage_barrier();
   Frag<MI, NB> f0, f1;
   read_frag<SWIGLU, MI, NB, NWN>(f0, sA0, sB0, 0, 0, wm, wn, fr, fh, live);
 
-  // One stage s: A from ring slot s % 4, B from double-stage slot (s / 2) % 3
-  // (half `tp`).  The barrier in the middle makes stage s+1 visible and frees
-  // A slot s-1 (refilled with stage s+3) and, on even s, B slot (s/2 + 2) % 3
-  // (refilled with stages s+4, s+5).  Between two waits exactly IA + IB
-  // instructions are issued, so the wait count never changes; past the end
-  // the last K step is re-loaded into slots nobody reads.
-#define MOE_STAGE(tA, tB, tp, nA, nB, np, dA, s, ISSB, dB)                                   \
+  // One stage s: A from double-stage slot (s / 2) % 2, B from slot (s / 2) %
+  // 3, half s % 2.  The barrier in the middle makes stage s+1 visible.  An
+  // odd s has just read the second half of its A slot: its wait also covers
+  // this wave's LDS reads, and after the barrier the slot takes A double
+  // stage (s + 3) / 2.  An even s frees B slot (s/2 + 2) % 3 (read last in
+  // stage s-1) and refills it with double stage s/2 + 2.  Loads are issued
+  // in the order A(d), B(d+1), A(d+1), B(d+2), ...: an odd s needs A and B
+  // double stage (s+1)/2, after which only B((s+1)/2 + 1) was issued (IB
+  // loads may stay in flight); an even s needs nothing new (IB + IA).  Past
+  // the end the last double stage is re-loaded into slots nobody reads, so
+  // the counts never change.
+#define MOE_STAGE(tA, tB, tp, nA, nB, np, s, ODD, dA, dB)                                   \
   read_frag<SWIGLU, MI, NB, NWN>(f1, tA, tB, 1, tp, wm, wn, fr, fh, live);                   \
   mfma_frag<MI, NB>(acc, f0, live);                                                           \
   interleave_mfma_ds_read<NM, NR>();                                                          \
-  wait_vmcnt<PER_STAGE>();                                                                    \
+  if (ODD) { wait_vmcnt_lgkm0<IB>(); } else { wait_vmcnt<IB + IA>(); }                        \
   stage_barrier();                                                                            \
-  MOE_ISSUE_A(dA, min((s) + 3, KT - 1) * BK);                                                 \
-  if (ISSB) { MOE_ISSUE_B(dB, min((s) / 2 + 2, KT2 - 1) * 2 * BK); }                          \
+  if (ODD) { MOE_ISSUE_A(dA, min(((s) + 3) / 2, KT2 - 1) * 2 * BK); }                         \
+  else { MOE_ISSUE_B(dB, min((s) / 2 + 2, KT2 - 1) * 2 * BK); }                               \
   read_frag<SWIGLU, MI, NB, NWN>(f0, nA, nB, 0, np, wm, wn, fr, fh, live);                   \
   mfma_frag<MI, NB>(acc, f1, live);                                                           \
   interleave_mfma_ds_read<NM, NR>();
 
-#define MOE_STAGES_0_3(kt)                                        \
-  MOE_STAGE(sA0, sB0, 0, sA1, sB0, 1, sA3, (kt), 1, sB2)          \
-  MOE_STAGE(sA1, sB0, 1, sA2, sB1, 0, sA0, (kt) + 1, 0, sB0)      \
-  MOE_STAGE(sA2, sB1, 0, sA3, sB1, 1, sA1, (kt) + 2, 1, sB0)      \
-  MOE_STAGE(sA3, sB1, 1, sA0, sB2, 0, sA2, (kt) + 3, 0, sB0)
-#define MOE_STAGES_4_7(kt)                                        \
-  MOE_STAGE(sA0, sB2, 0, sA1, sB2, 1, sA3, (kt) + 4, 1, sB1)      \
-  MOE_STAGE(sA1, sB2, 1, sA2, sB0, 0, sA0, (kt) + 5, 0, sB1)      \
-  MOE_STAGE(sA2, sB0, 0, sA3, sB0, 1, sA1, (kt) + 6, 1, sB2)      \
-  MOE_STAGE(sA3, sB0, 1, sA0, sB1, 0, sA2, (kt) + 7, 0, sB2)
-#define MOE_STAGES_8_11(kt)                                       \
-  MOE_STAGE(sA0, sB1, 0, sA1, sB1, 1, sA3, (kt) + 8, 1, sB0)      \
-  MOE_STAGE(sA1, sB1, 1, sA2, sB2, 0, sA0, (kt) + 9, 0, sB0)      \
-  MOE_STAGE(sA2, sB2, 0, sA3, sB2, 1, sA1, (kt) + 10, 1, sB1)     \
-  MOE_STAGE(sA3, sB2, 1, sA0, sB0, 0, sA2, (kt) + 11, 0, sB1)
+// stage s: A slot (s/2)%2, B slot (s/2)%3, half s%2; odd s refills A slot
+// ((s+3)/2)%2 (the one just read), even s refills B slot (s/2+2)%3
+#define MOE_STAGES_0_3(kt)                                         \
+  MOE_STAGE(sA0, sB0, 0, sA0, sB0, 1, (kt), 0, sA0, sB2)           \
+  MOE_STAGE(sA0, sB0, 1, sA1, sB1, 0, (kt) + 1, 1, sA0, sB2)       \
+  MOE_STAGE(sA1, sB1, 0, sA1, sB1, 1, (kt) + 2, 0, sA1, sB0)       \
+  MOE_STAGE(sA1, sB1, 1, sA0, sB2, 0, (kt) + 3, 1, sA1, sB0)
+#define MOE_STAGES_4_7(kt)                                         \
+  MOE_STAGE(sA0, sB2, 0, sA0, sB2, 1, (kt) + 4, 0, sA0, sB1)       \
+  MOE_STAGE(sA0, sB2, 1, sA1, sB0, 0, (kt) + 5, 1, sA0, sB1)       \
+  MOE_STAGE(sA1, sB0, 0, sA1, sB0, 1, (kt) + 6, 0, sA1, sB2)       \
+  MOE_STAGE(sA1, sB0, 1, sA0, sB1, 0, (kt) + 7, 1, sA1, sB2)
+#define MOE_STAGES_8_11(kt)                                        \
+  MOE_STAGE(sA0, sB1, 0, sA0, sB1, 1, (kt) + 8, 0, sA0, sB0)       \
+  MOE_STAGE(sA0, sB1, 1, sA1, sB2, 0, (kt) + 9, 1, sA0, sB0)       \
+  MOE_STAGE(sA1, sB2, 0, sA1, sB2, 1, (kt) + 10, 0, sA1, sB1)      \
+  MOE_STAGE(sA1, sB2, 1, sA0, sB0, 0, (kt) + 11, 1, sA1, sB1)
 
   int kt = 0;
   for (; kt + 12 <= KT; kt += 12) {
@@ -428,10 +427,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const uint16_t *__restrict__ B2, void *__restrict__ C, const int32_t *__restrict__ offsets,
     int G, int rows, int N, int K, int nt_count, char *__restrict__ ws, int cus) {
-  // 4 A stages (64 KB) and 3 B double stages (96 KB): all 160 KB of LDS.
+  // 2 A double stages (64 KB) and 3 B double stages (96 KB): all 160 KB of LDS.
   // The scheduler table lives in the last B slot, which is first loaded
   // after every wave has passed the prologue barrier.
-  __shared__ u32x4 sA0[SLOTS_MAX], sA1[SLOTS_MAX], sA2[SLOTS_MAX], sA3[SLOTS_MAX];
+  __shared__ u32x4 sA0[SLOTS_A2MAX], sA1[SLOTS_A2MAX];
   __shared__ u32x4 sB0[SLOTS_B2], sB1[SLOTS_B2], sB2[SLOTS_B2];
   static_assert(sizeof(int) * (3 * (MOE_MAX_GROUPS + 1) + NW) <= sizeof(u32x4) * SLOTS_B2,
                 "scheduler table must fit in one B slot");
@@ -474,7 +473,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   // flow cost more than the saved MFMAs there.
 #define MOE_TILE(BMV, SKIPV)                                                                  \
   run_tile<BMV, SWIGLU, OUT_F32, NW, SKIPV>(tile, A, B, B2, C, rows, N, K, kbeg, kt, part, sA0, \
-                                            sA1, sA2, sA3, sB0, sB1, sB2)
+                                            sA1, sB0, sB1, sB2)
   if (h > 128) {
     if (SWIGLU && h <= 224) MOE_TILE(256, SWIGLU); else MOE_TILE(256, false);
   } else if (h > 64) {
