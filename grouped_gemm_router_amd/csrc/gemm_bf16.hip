@@ -432,14 +432,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   // after every wave has passed the prologue barrier.
   __shared__ u32x4 sA0[SLOTS_A2MAX], sA1[SLOTS_A2MAX];
   __shared__ u32x4 sB0[SLOTS_B2], sB1[SLOTS_B2], sB2[SLOTS_B2];
-  static_assert(sizeof(int) * (3 * (MOE_MAX_GROUPS + 1) + NW) <= sizeof(u32x4) * SLOTS_B2,
+  static_assert(sizeof(int) * 3 * (MOE_MAX_GROUPS + 1) <= sizeof(u32x4) * SLOTS_B2,
                 "scheduler table must fit in one B slot");
   int *s_cum = reinterpret_cast<int *>(sB2);
   int *s_off = s_cum + MOE_MAX_GROUPS + 1;
   int *s_ord = s_off + MOE_MAX_GROUPS + 1;
-  int *s_tmp = s_ord + MOE_MAX_GROUPS;
 
-  sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_tmp, s_off, s_ord, SWIGLU);
+  sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_off, s_ord, SWIGLU);
   const int total = s_cum[G] * nt_count;
   const int KT = K / BK;  // a multiple of 4
   const int S = ws != nullptr ? split_slices(total, cus, KT) : 1;

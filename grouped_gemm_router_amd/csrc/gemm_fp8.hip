@@ -53,11 +53,10 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
   __shared__ __attribute__((aligned(16))) float lS[2][FBM];
   __shared__ float s_amax[2][FBM];
   __shared__ int s_cum[MOE_MAX_GROUPS + 1];
-  __shared__ int s_tmp[4];
   __shared__ int s_off[MOE_MAX_GROUPS + 1];
   __shared__ int s_ord[MOE_MAX_GROUPS];
 
-  sched_build<FNTH>(offsets, G, rows, FBM, s_cum, s_tmp, s_off, s_ord, SWIGLU);
+  sched_build<FNTH>(offsets, G, rows, FBM, s_cum, s_off, s_ord, SWIGLU);
   const int total = s_cum[G] * nt_count;
   const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;

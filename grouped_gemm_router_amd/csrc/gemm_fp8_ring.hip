@@ -405,11 +405,10 @@ __global__ __launch_bounds__(NTH, 1) void gemm_fp8_ring_kernel(
   __shared__ float sS0[SROWS], sS1[SROWS];
   __shared__ float s_amax[OUT_FP8 ? NWN * BM_MAX : 1];
   __shared__ int s_cum[MOE_MAX_GROUPS + 1];
-  __shared__ int s_tmp[NW];
   __shared__ int s_off[MOE_MAX_GROUPS + 1];
   __shared__ int s_ord[MOE_MAX_GROUPS];
 
-  sched_build<NTH>(offsets, G, rows, BM_MAX, s_cum, s_tmp, s_off, s_ord, SWIGLU);
+  sched_build<NTH>(offsets, G, rows, BM_MAX, s_cum, s_off, s_ord, SWIGLU);
   const int total = s_cum[G] * nt_count;
   const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;

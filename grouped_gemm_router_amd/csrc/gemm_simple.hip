@@ -29,14 +29,13 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(
     void *__restrict__ C, const int32_t *__restrict__ offsets, int G, int rows, int N, int K,
     int nt_count) {
   __shared__ int s_cum[MOE_MAX_GROUPS + 1];
-  __shared__ int s_tmp[4];
   __shared__ int s_off[MOE_MAX_GROUPS + 1];
   __shared__ int s_ord[MOE_MAX_GROUPS];
   __shared__ float As[SBK][SBM + 1];
   __shared__ float Bs[SBK][SBN + 1];
   __shared__ float B2s[SWIGLU ? SBK : 1][SBN + 1];
 
-  sched_build<256>(offsets, G, rows, SBM, s_cum, s_tmp, s_off, s_ord, SWIGLU);
+  sched_build<256>(offsets, G, rows, SBM, s_cum, s_off, s_ord, SWIGLU);
   const int total = s_cum[G] * nt_count;
   const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;

@@ -111,88 +111,65 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ int sched_class(int m) { return m > 128 ? 0 : (m > 64 ? 1 : 2); }
 
-// Block-wide exclusive scan of one int per thread; *total gets the sum.
-// s_tmp holds NTHREADS / 64 ints.  Starts with a barrier, so s_tmp may be
-// reused by consecutive calls.
-template <int NTHREADS>
-__device__ __forceinline__ int block_exclusive_scan(int v, int *s_tmp, int *total) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+// Exclusive scan over the 64 lanes of a wave; *total gets the sum.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
+  const int lane = threadIdx.x & (kWave - 1);
   int incl = v;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(incl, o, kWave);
+    const int y = __shfl_up(incl, o, kWave);
     if (lane >= o) incl += y;
   }
-  __syncthreads();
-  if (lane == kWave - 1) s_tmp[wv] = incl;
-  __syncthreads();
-  int base = 0, all = 0;
-  for (int w = 0; w < NTHREADS / kWave; ++w) {
-    const int t = s_tmp[w];
-    if (w < wv) base += t;
-    all += t;
-  }
-  *total = all;
-  return base + incl - v;
+  *total = __shfl(incl, kWave - 1, kWave);
+  return incl - v;
 }
 
 // Block-wide: fills, in LDS, off[0..G] with the clamped offsets, ord[p] =
 // the group at position p of the tile order, and cum[0..G] = row tiles of
-// the groups at positions before p (cum[G] = all row tiles).  s_tmp holds
-// NTHREADS / 64 ints.  Must be called by all threads of the block.
+// the groups at positions before p (cum[G] = all row tiles).  All threads
+// load the offsets; the first wave alone then builds the order and the
+// prefix (each lane a contiguous run of groups, wave-level scans), so the
+// block meets at two barriers only.  Must be called by all threads.
 template <int NTHREADS>
 __device__ __forceinline__ void sched_build(const int32_t *__restrict__ offsets, int G,
-                                            int rows, int BM, int *cum, int *s_tmp, int *off,
-                                            int *ord, bool by_class) {
-  // each thread owns a contiguous run of groups (then of positions)
-  const int tid = threadIdx.x;
-  const int per = (G + NTHREADS - 1) / NTHREADS;
-  const int g0 = tid * per;
-  // classes 0 and 1 counted in the low and high 16 bits (G < 65536)
-  int local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int g = g0 + i;
-    if (g < G) {
-      const int a = min(max(offsets[g], 0), rows);
-      const int b = min(max(offsets[g + 1], 0), rows);
-      const int c = by_class ? sched_class(max(b - a, 0)) : 0;
-      local += c == 0 ? 1 : (c == 1 ? 1 << 16 : 0);
-    }
-  }
-  int tot;
-  const int before = block_exclusive_scan<NTHREADS>(local, s_tmp, &tot);
-  const int n0 = tot & 0xffff, n1 = tot >> 16;
-  int c0 = before & 0xffff, c1 = before >> 16;
-  for (int i = 0; i < per; ++i) {
-    const int g = g0 + i;
-    if (g < G) {
-      const int a = min(max(offsets[g], 0), rows);
-      const int b = min(max(offsets[g + 1], 0), rows);
-      const int m = max(b - a, 0);
-      const int c = by_class ? sched_class(m) : 0;
-      const int pos = c == 0 ? c0 : (c == 1 ? n0 + c1 : n0 + n1 + (g - c0 - c1));
-      c0 += c == 0;
-      c1 += c == 1;
-      ord[pos] = g;
-      cum[pos] = (m + BM - 1) / BM;  // row tiles, scanned in place below
-      off[g] = a;
-      if (g == G - 1) off[G] = b;
-    }
-  }
+                                            int rows, int BM, int *cum, int *off, int *ord,
+                                            bool by_class) {
+  for (int g = threadIdx.x; g <= G; g += NTHREADS) off[g] = min(max(offsets[g], 0), rows);
   __syncthreads();
-  int run = 0;
-  for (int i = 0; i < per; ++i)
-    if (g0 + i < G) run += cum[g0 + i];
-  run = block_exclusive_scan<NTHREADS>(run, s_tmp, &tot);
-  for (int i = 0; i < per; ++i) {
-    const int p = g0 + i;
-    if (p < G) {
-      const int t = cum[p];
-      cum[p] = run;
-      run += t;
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int per = (G + kWave - 1) / kWave;
+    const int g0 = lane * per, g1 = min(G, g0 + per);
+    // row tiles per class and groups of classes 0 and 1 in this lane's run
+    int t0 = 0, t1 = 0, t2 = 0, n0 = 0, n1 = 0;
+    for (int g = g0; g < g1; ++g) {
+      const int m = max(off[g + 1] - off[g], 0);
+      const int c = by_class ? sched_class(m) : 0;
+      const int t = (m + BM - 1) / BM;
+      if (c == 0) { t0 += t; ++n0; } else if (c == 1) { t1 += t; ++n1; } else { t2 += t; }
     }
+    int T0, T1, T2, N0, N1;
+    int q0 = wave_exclusive_scan(t0, &T0), q1 = wave_exclusive_scan(t1, &T1);
+    int q2 = wave_exclusive_scan(t2, &T2);
+    int p0 = wave_exclusive_scan(n0, &N0), p1 = wave_exclusive_scan(n1, &N1);
+    // class-2 groups before g0 = g0 minus those of classes 0 and 1
+    int p2 = N0 + N1 + (min(g0, G) - p0 - p1);
+    p1 += N0;
+    q1 += T0;
+    q2 += T0 + T1;
+    for (int g = g0; g < g1; ++g) {
+      const int m = max(off[g + 1] - off[g], 0);
+      const int c = by_class ? sched_class(m) : 0;
+      const int t = (m + BM - 1) / BM;
+      int pos, at;
+      if (c == 0) { pos = p0++; at = q0; q0 += t; }
+      else if (c == 1) { pos = p1++; at = q1; q1 += t; }
+      else { pos = p2++; at = q2; q2 += t; }
+      ord[pos] = g;
+      cum[pos] = at;
+    }
+    if (lane == 0) cum[G] = T0 + T1 + T2;
   }
-  if (tid == 0) cum[G] = tot;
   __syncthreads();
 }
 
@@ -207,12 +184,17 @@ struct Tile {
 // the LDS tables from sched_build; nt_count column tiles per row tile.
 __device__ __forceinline__ Tile sched_tile(int L, const int *cum, const int *ord, const int *off,
                                            int G, int BM, int nt_count, int chunk) {
-  // find position p with cum[p] * nt_count <= L < cum[p+1] * nt_count
-  int lo = 0, hi = G;  // invariant: cum[lo]*nt <= L < cum[hi]*nt
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (cum[mid] * nt_count <= L) lo = mid; else hi = mid;
-  }
+  // the last position lo < G with cum[lo] * nt_count <= L (cum is
+  // non-decreasing and cum[0] = 0 <= L): a wave-wide ballot over every
+  // step-th position, then one over the positions of that block
+  const int lane = threadIdx.x & (kWave - 1);
+  const int step = (G + kWave - 1) / kWave;
+  int q = lane * step;
+  unsigned long long hit = __ballot(q < G && cum[min(q, G)] * nt_count <= L);
+  const int base = (__popcll(hit) - 1) * step;
+  q = base + lane;
+  hit = __ballot(lane < step && q < G && cum[min(q, G)] * nt_count <= L);
+  const int lo = base + __popcll(hit) - 1;
   // cum[lo+1] > cum[lo], so position lo never holds an empty group
   const int g = ord[lo];
   int mt_g = cum[lo + 1] - cum[lo];
