@@ -1,5 +1,5 @@
 // gemm_fp8_ring.hip -- FP8 (E4M3) block-scaled grouped GEMM for gfx950,
-// operands streamed through a 4-stage LDS ring of LDS-direct loads.
+// operands streamed through LDS rings of LDS-direct loads.
 //
 // "DeepGEMM walkthrough" §2.3 (C ~ (A_q / scale_A)(B_q / scale_B); the
 // stored scales here are the dequantisation multipliers, the reciprocal of
@@ -9,12 +9,15 @@
 //   C[r][n] = sum_kb sA[r][kb] * sB[g][n/128][kb] * (sum_{k in kb} Aq Bq)
 //
 // Design (CDNA4, 64-wide waves, 8 waves in a 2 x 4 grid):
-//   * a K step is 64 fp8 columns = 64 bytes per tile row, the same row size
-//     as the bf16 kernel's 32-column step, so the LDS ring, the 16-byte
-//     piece swizzle and the load issue are the same: tile rows move
-//     HBM/L2 -> LDS with global_load_lds_dwordx4, three steps ahead, each step
-//     waiting only for its own stage and meeting the other waves at a plain
-//     s_barrier;
+//   * a K step is 64 fp8 columns; operand rows move HBM/L2 -> LDS with
+//     global_load_lds_dwordx4 as whole 128-byte pieces, i.e. two steps = one
+//     128-column scale block at a time (the TCP sends one L2 request per
+//     line touched: half the requests of 64-byte pieces).  A runs through
+//     two such double-step slots, B through three, refilled one and two
+//     double steps ahead; each double step waits only for its own loads and
+//     meets the other waves at one plain s_barrier.  Measured on the
+//     DeepSeek shapes against 4-stage rings of 64-byte pieces: gate/up 2.03
+//     -> 1.90 ms, down 1.11 -> 1.04 ms;
 //   * one v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit E8M0 block
 //     scales) per 32 x 32 block and step; its result is the exact-scale
 //     partial sum of 64 products, folded into the fp32 accumulator with the
@@ -25,13 +28,18 @@
 //     one sB per wave column (a scalar load), not one per accumulator row;
 //   * activation scales are stored group-major, [K/128][rows], so one
 //     block's scales for the tile rows are one contiguous run; they travel
-//     with every even step (the first of a 128-column block): one 4-byte
-//     LDS-direct load per wave (32 rows, each fetched by two lanes) into one
-//     of two LDS slots, read once per block.  Exactly one of any two
-//     consecutive steps carries it, so every step still waits for the same
-//     count;
-//   * tile heights 64 / 128 / 256 rows are chosen per tile from its row count,
-//     as in the bf16 kernel (a group's last tile shrinks to what it holds);
+//     with their block's A double step: one 4-byte LDS-direct load per wave
+//     (32 rows, each fetched by two lanes) into the scale slot of that A
+//     slot, read once per block;
+//   * tile heights 64 / 128 / 192 rows are chosen per tile from its row
+//     count, as in the bf16 kernel (a group's last tile shrinks to what it
+//     holds); 192, not 256: two 256-row A slots, three B slots and the scale
+//     slots do not fit the 160 KB of LDS;
+//   * the main loop runs six double steps per trip (the slot pattern
+//     repeats every six) and leaves a trip after two or four of them when K
+//     ends there; the exits cost one full load drain per trip, where the
+//     compiler's wait analysis loses track (a tail after the loop instead
+//     spilled the accumulators);
 //   * SwiGLU: the weight tile holds 128 gate rows then the 128 matching up
 //     rows; wave column wn takes gate rows [32 wn, +32) and up rows
 //     [128 + 32 wn, +32), so silu(gate) * up pairs in registers; E4M3 output
@@ -43,16 +51,18 @@ namespace {
 
 using namespace moe;
 
-constexpr int BM_MAX = 256, BN = 256, BK = 64;  // BK: fp8 columns (= bytes) per step
+constexpr int BM_MAX = 192, BN = 256, BK = 64;  // BK: fp8 columns (= bytes) per step
 constexpr int PIECES = BK / 16;                 // 16-byte pieces per tile row (4)
-constexpr int SLOTS_MAX = BM_MAX * PIECES;      // 16-byte slots per A stage (16 KB at most)
-constexpr int SLOTS_B = BN * PIECES;            // 16-byte slots per B stage (16 KB)
+constexpr int PIECES2 = 2 * PIECES;             // 16-byte pieces per 128-byte row (two steps)
+constexpr int SLOTS_A2MAX = BM_MAX * PIECES2;   // 16-byte slots per A double step (24 KB)
+constexpr int SLOTS_B2 = BN * PIECES2;          // 16-byte slots per B double step (32 KB)
 constexpr int NW = 8, NWN = 4;                  // waves, wave columns (2 wave rows)
 constexpr int NB = 2;                           // 32-row weight blocks per wave
 constexpr int NTH = NW * 64;
 constexpr int SROWS = NW * 64;                  // activation-scale slot (32 rows per wave, x2)
 
-__device__ __forceinline__ int swz(int row, int p) { return p ^ ((row ^ (row >> 2)) & 3); }
+// piece p of a 128-byte row r sits at slot p ^ ((r >> 1) & 7) of the row
+__device__ __forceinline__ int swz(int row, int p) { return p ^ ((row >> 1) & 7); }
 
 // weight-tile row of wave column wn, 32-row block nb
 template <bool SWIGLU>
@@ -93,19 +103,20 @@ __device__ __forceinline__ void dma_to_lds(const void *g, void *l) {
     __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 4, 0, 0);
 }
 
-// the 32 bytes (64 K columns split in two lane halves) of row r
-__device__ __forceinline__ i32x8 frag(const u32x4 *t, int r, int fh) {
-  const u32x4 lo = t[r * PIECES + swz(r, 2 * fh)];
-  const u32x4 hi = t[r * PIECES + swz(r, 2 * fh + 1)];
+// the 32 bytes (64 K columns split in two lane halves) of row r in step
+// `par` (0 or 1) of a double step
+__device__ __forceinline__ i32x8 frag(const u32x4 *t, int r, int fh, int par) {
+  const u32x4 lo = t[r * PIECES2 + swz(r, par * PIECES + 2 * fh)];
+  const u32x4 hi = t[r * PIECES2 + swz(r, par * PIECES + 2 * fh + 1)];
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
 struct Ring {
-  u32x4 *a[4];
-  u32x4 *b[4];
-  float *sa[2];  // activation scales of a 128-column block, slot = block % 2
-  float *amax;  // [NWN][BM_MAX]
+  u32x4 *a0, *a1;       // A double steps (separate LDS arrays)
+  u32x4 *b0, *b1, *b2;  // B double steps
+  float *s0, *s1;       // activation scales of A slot 0 / 1's scale block
+  float *amax;          // [NWN][BM_MAX], in A slot 0 (epilogue only)
 };
 
 template <int BM, bool SWIGLU, bool OUT_FP8, bool SKIP>
@@ -118,11 +129,9 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
                                          float *__restrict__ Cs, int rows, int N, int K,
                                          const Ring &ring) {
   constexpr int MI = BM / 64;            // 32-token blocks per wave
-  constexpr int SLOTS_A = BM * PIECES;
-  constexpr bool A_DW = SLOTS_A < NW * 64;  // 64-row tile: 4-byte loads for A
-  constexpr int IA = A_DW ? (SLOTS_A * 4) / NW / 64 : SLOTS_A / NW / 64;
-  constexpr int IB = SLOTS_B / NW / 64;
-  constexpr int OPS = IA + IB;            // operand loads per wave and stage
+  constexpr int SLOTS_A2 = BM * PIECES2;
+  constexpr int IA = SLOTS_A2 / NW / 64;  // A loads per wave and double step
+  constexpr int IB = SLOTS_B2 / NW / 64;  // B loads per wave and double step
   static_assert(IA >= 1 && IB >= 1, "tile too small for the wave count");
 
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
@@ -138,9 +147,10 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
   }
   const int KB = K / 128, NBK = N / 128;  // scale blocks along K and N
 
-  // LDS-direct sources (see the bf16 kernel for the slot layout): a
-  // wave-uniform base (SGPRs) plus a 32-bit per-lane byte offset, which keeps
-  // the addresses to one VGPR each
+  // LDS-direct sources (whole 128-byte row pieces: two steps, one scale
+  // block): wave wv fills slots [wv*SLOTS/NW, +SLOTS/NW) of each double
+  // step, 64 per instruction, slot s holding piece swz(row, s % 8) of row
+  // s / 8; a wave-uniform base (SGPRs) plus a 32-bit per-lane byte offset
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   const int gu = __builtin_amdgcn_readfirstlane(tile.g);
   const int ntu = __builtin_amdgcn_readfirstlane(tile.nt);
@@ -148,47 +158,38 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
   uint32_t gb[IB];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
-    int r, off;
-    if (A_DW) {
-      const int q = (wv * IA + i) * 64 + lane;
-      const int sl = q / 4;
-      r = sl / PIECES;
-      off = swz(r, sl % PIECES) * 16 + (q % 4) * 4;
-    } else {
-      const int sl = wv * (SLOTS_A / NW) + i * 64 + lane;
-      r = sl / PIECES;
-      off = swz(r, sl % PIECES) * 16;
-    }
+    const int sl = wv * (SLOTS_A2 / NW) + i * 64 + lane;
+    const int r = sl / PIECES2;
     const int m = min(tile.m0 + r, rows - 1);
-    ga[i] = (uint32_t)m * (uint32_t)K + off;
+    ga[i] = (uint32_t)m * (uint32_t)K + swz(r, sl % PIECES2) * 16;
   }
   // the B tile of wave wv comes from one matrix: SwiGLU waves 0-3 fill the
   // 128 gate rows, waves 4-7 the 128 up rows
   const uint8_t *bbase = ((SWIGLU && wvu >= NW / 2) ? B2q : Bq) + (size_t)gu * N * K;
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
-    const int sl = wv * (SLOTS_B / NW) + i * 64 + lane;
-    const int r = sl / PIECES;
-    const int p = swz(r, sl % PIECES);
+    const int sl = wv * (SLOTS_B2 / NW) + i * 64 + lane;
+    const int r = sl / PIECES2;
     const int n = SWIGLU ? ntu * 128 + (r & 127)
                          : min(ntu * 256 + r, N - 1);  // N % 256 == 128: half tile
-    gb[i] = (uint32_t)n * (uint32_t)K + p * 16;
+    gb[i] = (uint32_t)n * (uint32_t)K + swz(r, sl % PIECES2) * 16;
   }
-  // activation scales [K/128][rows]: wave wv loads tile rows [32 wv, +32),
-  // each by lanes l and l + 32 (the second copy lands in an unused half);
-  // rows past the tile read a clamped row and are never used
+  // activation scales [K/128][rows]: each A double step carries its block's
+  // scales into the matching scale slot; wave wv loads tile rows [32 wv,
+  // +32), each by lanes l and l + 32 (the second copy lands in an unused
+  // half); rows past the tile read a clamped row and are never used
   const uint32_t gs = (uint32_t)min(tile.m0 + wv * 32 + (lane & 31), rows - 1) * 4u;
-  const int dma_a = A_DW ? wv * IA * 16 : wv * (SLOTS_A / NW);
-  constexpr int STEP_A = A_DW ? 16 : 64;
-  const int dma_b = wv * (SLOTS_B / NW);
-#define MOE_ISSUE(st, kt, SC, SLOT)                                                        \
-  _Pragma("unroll") for (int i = 0; i < IA; ++i)                                          \
-    dma_to_lds<A_DW ? 4 : 16>(Aq + (ga[i] + (kt) * BK), ring.a[st] + dma_a + i * STEP_A); \
-  _Pragma("unroll") for (int i = 0; i < IB; ++i)                                          \
-    dma_to_lds<16>(bbase + (gb[i] + (kt) * BK), ring.b[st] + dma_b + i * 64);             \
-  if (SC)                                                                                 \
-    dma_to_lds<4>(reinterpret_cast<const uint8_t *>(As + (size_t)((kt) / 2) * rows) + gs,  \
-                  ring.sa[SLOT] + wv * 64);
+  const int dma_a = wv * (SLOTS_A2 / NW);
+  const int dma_b = wv * (SLOTS_B2 / NW);
+  float sa[MI];  // this lane's token scales for the current block
+  // issue order per double step: A(kb) with its scales, then B(kb + 1)
+#define MOE_ISSUE_A(dA, dS, kb)                                                             \
+  _Pragma("unroll") for (int i = 0; i < IA; ++i)                                           \
+    dma_to_lds<16>(Aq + (ga[i] + (kb) * 128), (dA) + dma_a + i * 64);                      \
+  dma_to_lds<4>(reinterpret_cast<const uint8_t *>(As + (size_t)(kb) * rows) + gs, (dS) + wv * 64);
+#define MOE_ISSUE_B(dB, kb)                                                                 \
+  _Pragma("unroll") for (int i = 0; i < IB; ++i)                                           \
+    dma_to_lds<16>(bbase + (gb[i] + (kb) * 128), (dB) + dma_b + i * 64);
 
   // weight scales of this wave's two 32-row blocks: [g][n-block][kb]; the
   // indices are wave-uniform, so these are scalar loads
@@ -213,60 +214,80 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
   constexpr bool FOLD2 = BM <= 128;
   f32x16 pt[FOLD2 ? MI : 1][NB];
   const int fr = lane & 31, fh = lane >> 5;
-  const int KT = K / BK;  // a multiple of 4
 
-  // stage t carries the scales of block t/2 iff t is even, into slot
-  // (t/2) % 2; with 4 steps per loop trip (kt % 4 == 0) both are fixed per
-  // unrolled step
-  MOE_ISSUE(0, 0, true, 0);
-  MOE_ISSUE(1, 1, false, 0);
-  MOE_ISSUE(2, 2, true, 1);
-  float sa[MI];  // this lane's token scales for the current block
+  // Double step d (K columns [128 d, 128 d + 128), one scale block): A from
+  // slot d % 2, B from slot d % 3.  Loads go out in the order A(d+1),
+  // scales(d+1), B(d+2), so waiting until only the last B's IB loads may be
+  // outstanding makes A(d), scales(d) and B(d) land; one barrier per double
+  // step makes them visible and frees the slots of double step d-1, which
+  // take A(d+1) and B(d+2).  Past the end the last block is re-loaded into
+  // slots nobody reads, so the count never changes.
+  MOE_ISSUE_A(ring.a0, ring.s0, 0);
+  MOE_ISSUE_B(ring.b0, 0);
+  MOE_ISSUE_B(ring.b1, min(1, KB - 1));
 
-  // Step s: wait for stage s (stages s+1 and s+2 -- 2 OPS + 1 loads -- may
-  // still be in flight), barrier (stage s visible; every wave is past its
-  // reads of stage s-1, whose buffer takes step s+3, and of the scale slot
-  // that step s+3 refills), issue step s+3 (the last three steps re-load the
-  // final step into buffers nobody reads, so the wait count never changes),
-  // then fragments, MFMAs and the fold.
-#define MOE_STEP(st, s)                                                                     \
+#define MOE_DSTEP(tA, tS, tB, nA, nS, nB, dd)                                               \
   {                                                                                         \
-    wait_vmcnt<2 * OPS + 1>();                                                              \
+    wait_vmcnt<IB>();                                                                       \
     stage_barrier();                                                                        \
-    MOE_ISSUE(((st) + 3) & 3, min((s) + 3, KT - 1), ((st) & 1) == 1, (st) == 1 ? 0 : 1);    \
-    const float s0 = sb0[(s) >> 1], s1 = sb1[(s) >> 1];                                     \
-    i32x8 w[NB];                                                                            \
-    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                       \
-      w[nb] = frag(ring.b[st], b_row<SWIGLU>(wn, nb) + fr, fh);                             \
     _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) {                                     \
-      if (mi >= live) break;                                                                \
       const int r = wm * (MI * 32) + mi * 32 + fr;                                          \
-      const i32x8 x = frag(ring.a[st], r, fh);                                              \
-      if (((st) & 1) == 0) sa[mi] = ring.sa[(st) >> 1][(r >> 5) * 64 + (r & 31)];           \
-      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                   \
-        if (FOLD2 && ((st) & 1) == 0) {                                                     \
-          pt[FOLD2 ? mi : 0][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(         \
-              w[nb], x, f32x16{}, 0, 0, 0, 127, 0, 127);                                    \
-        } else {                                                                            \
-          const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                 \
-              w[nb], x, FOLD2 ? pt[FOLD2 ? mi : 0][nb] : f32x16{}, 0, 0, 0, 127, 0, 127);   \
-          const float c = sa[mi] * (nb == 0 ? s0 : s1);                                     \
-          _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2)                                 \
-            acc[mi][nb][r2] = fmaf(p[r2], c, acc[mi][nb][r2]);                              \
+      sa[mi] = (tS)[(r >> 5) * 64 + (r & 31)];                                              \
+    }                                                                                       \
+    MOE_ISSUE_A(nA, nS, min((dd) + 1, KB - 1));                                             \
+    MOE_ISSUE_B(nB, min((dd) + 2, KB - 1));                                                 \
+    const int du_ = __builtin_amdgcn_readfirstlane(dd); /* uniform: scalar loads */        \
+    const float s0 = sb0[du_], s1 = sb1[du_];                                               \
+    _Pragma("unroll") for (int par = 0; par < 2; ++par) {                                   \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+      i32x8 w[NB];                                                                          \
+      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                     \
+        w[nb] = frag(tB, b_row<SWIGLU>(wn, nb) + fr, fh, par);                              \
+      _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) {                                   \
+        if (mi >= live) break;                                                              \
+        const i32x8 x = frag(tA, wm * (MI * 32) + mi * 32 + fr, fh, par);                   \
+        _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                 \
+          if (FOLD2 && par == 0) {                                                          \
+            pt[FOLD2 ? mi : 0][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(       \
+                w[nb], x, f32x16{}, 0, 0, 0, 127, 0, 127);                                  \
+          } else {                                                                          \
+            const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
+                w[nb], x, FOLD2 ? pt[FOLD2 ? mi : 0][nb] : f32x16{}, 0, 0, 0, 127, 0, 127); \
+            const float c = sa[mi] * (nb == 0 ? s0 : s1);                                   \
+            _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2)                               \
+              acc[mi][nb][r2] = fmaf(p[r2], c, acc[mi][nb][r2]);                            \
+          }                                                                                 \
         }                                                                                   \
       }                                                                                     \
     }                                                                                       \
   }
+  // (tA, tB): slots of double step d; (nA, nB): the slots A(d+1), B(d+2) go to
+#define MOE_DSTEPS_0_1(kb)                                                        \
+  MOE_DSTEP(ring.a0, ring.s0, ring.b0, ring.a1, ring.s1, ring.b2, (kb))           \
+  MOE_DSTEP(ring.a1, ring.s1, ring.b1, ring.a0, ring.s0, ring.b0, (kb) + 1)
+#define MOE_DSTEPS_2_3(kb)                                                        \
+  MOE_DSTEP(ring.a0, ring.s0, ring.b2, ring.a1, ring.s1, ring.b1, (kb) + 2)       \
+  MOE_DSTEP(ring.a1, ring.s1, ring.b0, ring.a0, ring.s0, ring.b2, (kb) + 3)
+#define MOE_DSTEPS_4_5(kb)                                                        \
+  MOE_DSTEP(ring.a0, ring.s0, ring.b1, ring.a1, ring.s1, ring.b0, (kb) + 4)       \
+  MOE_DSTEP(ring.a1, ring.s1, ring.b2, ring.a0, ring.s0, ring.b1, (kb) + 5)
 
-  for (int kt = 0; kt < KT; kt += 4) {
-    MOE_STEP(0, kt)
-    MOE_STEP(1, kt + 1)
-    MOE_STEP(2, kt + 2)
-    MOE_STEP(3, kt + 3)
+  // KB is even: the last trip stops after 2, 4 or 6 double steps
+  for (int kb = 0; kb < KB; kb += 6) {
+    MOE_DSTEPS_0_1(kb)
+    if (kb + 2 >= KB) break;
+    MOE_DSTEPS_2_3(kb)
+    if (kb + 4 >= KB) break;
+    MOE_DSTEPS_4_5(kb)
   }
   wait_vmcnt<0>();  // no LDS-direct load may still be landing when the tile ends
-#undef MOE_STEP
-#undef MOE_ISSUE
+  __syncthreads();  // every wave is past its reads of the slots the epilogue reuses
+#undef MOE_DSTEPS_0_1
+#undef MOE_DSTEPS_2_3
+#undef MOE_DSTEPS_4_5
+#undef MOE_DSTEP
+#undef MOE_ISSUE_A
+#undef MOE_ISSUE_B
 
   // epilogue.  32x32 accumulator layout: lane holds column (token) lane%32;
   // register r holds row (weight row) 8*(r/4) + 4*(lane/32) + r%4, so each
@@ -323,7 +344,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
     // would write 16 bytes into each of 32 rows per instruction.  The 16-byte
     // piece index is XORed with the token row, so the reads are conflict free.
     __syncthreads();
-    char *const stg = reinterpret_cast<char *>(wm == 0 ? ring.b[0] : ring.b[1]);
+    char *const stg = reinterpret_cast<char *>(wm == 0 ? ring.b0 : ring.b1);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -343,7 +364,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
         if (m < tile.mend && n < N)
           *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(C) + (size_t)m * N + n) =
               *reinterpret_cast<const u32x4 *>(
-                  reinterpret_cast<const char *>(wr == 0 ? ring.b[0] : ring.b[1]) + rr * 512 +
+                  reinterpret_cast<const char *>(wr == 0 ? ring.b0 : ring.b1) + rr * 512 +
                   ((pc ^ rr) << 4));
       }
       __syncthreads();  // the staging blocks are rewritten for the next mi
@@ -400,25 +421,32 @@ __global__ __launch_bounds__(NTH, 1) void gemm_fp8_ring_kernel(
     const float *__restrict__ Bs, const uint8_t *__restrict__ B2q,
     const float *__restrict__ B2s, void *__restrict__ C, float *__restrict__ Cs,
     const int32_t *__restrict__ offsets, int G, int rows, int N, int K, int nt_count) {
-  __shared__ u32x4 sA0[SLOTS_MAX], sA1[SLOTS_MAX], sA2[SLOTS_MAX], sA3[SLOTS_MAX];
-  __shared__ u32x4 sB0[SLOTS_B], sB1[SLOTS_B], sB2[SLOTS_B], sB3[SLOTS_B];
+  // 2 A and 3 B double steps and two scale slots (148 KB of LDS).  The
+  // scheduler tables live in B slot 2, first loaded after every wave has
+  // passed the first barrier; the epilogue's row maxima in A slot 0 once the
+  // loop is done.
+  __shared__ u32x4 sA0[SLOTS_A2MAX], sA1[SLOTS_A2MAX];
+  __shared__ u32x4 sB0[SLOTS_B2], sB1[SLOTS_B2], sB2[SLOTS_B2];
   __shared__ float sS0[SROWS], sS1[SROWS];
-  __shared__ float s_amax[OUT_FP8 ? NWN * BM_MAX : 1];
-  __shared__ int s_cum[MOE_MAX_GROUPS + 1];
-  __shared__ int s_off[MOE_MAX_GROUPS + 1];
-  __shared__ int s_ord[MOE_MAX_GROUPS];
+  static_assert(sizeof(int) * 3 * (MOE_MAX_GROUPS + 1) <= sizeof(u32x4) * SLOTS_B2,
+                "scheduler tables must fit in one B slot");
+  static_assert(sizeof(float) * NWN * BM_MAX <= sizeof(u32x4) * SLOTS_A2MAX,
+                "row maxima must fit in one A slot");
+  int *s_cum = reinterpret_cast<int *>(sB2);
+  int *s_off = s_cum + MOE_MAX_GROUPS + 1;
+  int *s_ord = s_off + MOE_MAX_GROUPS + 1;
 
   sched_build<NTH>(offsets, G, rows, BM_MAX, s_cum, s_off, s_ord, SWIGLU);
   const int total = s_cum[G] * nt_count;
   const int L = tile_of_workgroup((int)blockIdx.x, total);
   if (L < 0) return;
   const Tile tile = sched_tile(L, s_cum, s_ord, s_off, G, BM_MAX, nt_count, kTileChunk);
-  const Ring ring{{sA0, sA1, sA2, sA3}, {sB0, sB1, sB2, sB3}, {sS0, sS1}, s_amax};
+  const Ring ring{sA0, sA1, sB0, sB1, sB2, sS0, sS1, reinterpret_cast<float *>(sA0)};
   const int h = tile.mend - tile.m0;  // wave-uniform
-  if (h == 256)
-    run_tile<256, SWIGLU, OUT_FP8, false>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+  if (h == BM_MAX)
+    run_tile<BM_MAX, SWIGLU, OUT_FP8, false>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
   else if (h > 128)
-    run_tile<256, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+    run_tile<BM_MAX, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
   else if (h > 64)
     run_tile<128, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
   else

@@ -146,11 +146,11 @@ def host_scales(Cs):
     return Cs.t().cpu().numpy()
 
 
-# K % 256 == 0 runs the LDS-ring kernel (tile heights 64 / 128 / 256 picked
+# K % 256 == 0 runs the LDS-ring kernel (tile heights 64 / 128 / 192 picked
 # per tile: the sizes cross every switch point), other K the general one;
 # N = 384 leaves half a 256-column tile in the plain GEMM.
 @pytest.mark.parametrize("sizes", [[0, 1, 127, 128, 129, 300], [64], [5, 0, 200],
-                                   [64, 65, 256, 257, 320, 384, 385]])
+                                   [64, 65, 256, 257, 320, 384, 385], [191, 192, 193]])
 @pytest.mark.parametrize("N,K,swiglu", [(256, 128, False), (384, 256, False), (128, 384, True),
                                         (256, 128, True), (384, 512, False), (256, 1024, True),
                                         (512, 768, False)])
