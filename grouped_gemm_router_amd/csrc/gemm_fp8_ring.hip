@@ -36,10 +36,11 @@
 //     holds); 192, not 256: two 256-row A slots, three B slots and the scale
 //     slots do not fit the 160 KB of LDS;
 //   * the main loop runs six double steps per trip (the slot pattern
-//     repeats every six) and leaves a trip after two or four of them when K
-//     ends there; the exits cost one full load drain per trip, where the
-//     compiler's wait analysis loses track (a tail after the loop instead
-//     spilled the accumulators);
+//     repeats every six); the K % 768 / 128 double steps that do not fill a
+//     trip run ahead of it, and the loop then starts at that phase of the
+//     pattern, so its body has no exit.  Exits inside the body made the
+//     compiler drain every load once per trip (4-5 %), a tail after the
+//     loop spilled the accumulators;
 //   * SwiGLU: the weight tile holds 128 gate rows then the 128 matching up
 //     rows; wave column wn takes gate rows [32 wn, +32) and up rows
 //     [128 + 32 wn, +32), so silu(gate) * up pairs in registers; E4M3 output
@@ -261,30 +262,42 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
       }                                                                                     \
     }                                                                                       \
   }
-  // (tA, tB): slots of double step d; (nA, nB): the slots A(d+1), B(d+2) go to
-#define MOE_DSTEPS_0_1(kb)                                                        \
-  MOE_DSTEP(ring.a0, ring.s0, ring.b0, ring.a1, ring.s1, ring.b2, (kb))           \
-  MOE_DSTEP(ring.a1, ring.s1, ring.b1, ring.a0, ring.s0, ring.b0, (kb) + 1)
-#define MOE_DSTEPS_2_3(kb)                                                        \
-  MOE_DSTEP(ring.a0, ring.s0, ring.b2, ring.a1, ring.s1, ring.b1, (kb) + 2)       \
-  MOE_DSTEP(ring.a1, ring.s1, ring.b0, ring.a0, ring.s0, ring.b2, (kb) + 3)
-#define MOE_DSTEPS_4_5(kb)                                                        \
-  MOE_DSTEP(ring.a0, ring.s0, ring.b1, ring.a1, ring.s1, ring.b0, (kb) + 4)       \
-  MOE_DSTEP(ring.a1, ring.s1, ring.b2, ring.a0, ring.s0, ring.b1, (kb) + 5)
+  // the six phases of the slot pattern: (A, its scales, B) read by double
+  // step d = 6 t + p, then the slots that take A(d+1) and B(d+2)
+#define MOE_P0(dd) MOE_DSTEP(ring.a0, ring.s0, ring.b0, ring.a1, ring.s1, ring.b2, (dd))
+#define MOE_P1(dd) MOE_DSTEP(ring.a1, ring.s1, ring.b1, ring.a0, ring.s0, ring.b0, (dd))
+#define MOE_P2(dd) MOE_DSTEP(ring.a0, ring.s0, ring.b2, ring.a1, ring.s1, ring.b1, (dd))
+#define MOE_P3(dd) MOE_DSTEP(ring.a1, ring.s1, ring.b0, ring.a0, ring.s0, ring.b2, (dd))
+#define MOE_P4(dd) MOE_DSTEP(ring.a0, ring.s0, ring.b1, ring.a1, ring.s1, ring.b0, (dd))
+#define MOE_P5(dd) MOE_DSTEP(ring.a1, ring.s1, ring.b2, ring.a0, ring.s0, ring.b1, (dd))
 
-  // KB is even: the last trip stops after 2, 4 or 6 double steps
-  for (int kb = 0; kb < KB; kb += 6) {
-    MOE_DSTEPS_0_1(kb)
-    if (kb + 2 >= KB) break;
-    MOE_DSTEPS_2_3(kb)
-    if (kb + 4 >= KB) break;
-    MOE_DSTEPS_4_5(kb)
+  // KB is even.  The first KB % 6 double steps run ahead of the loop, so
+  // the loop runs whole trips of six and has no exit in its body (exits
+  // there make the compiler drain every load once per trip: 4-5 % measured)
+  const int head = KB % 6;
+  if (head == 0) {
+    for (int kb = 0; kb < KB; kb += 6) {
+      MOE_P0(kb) MOE_P1(kb + 1) MOE_P2(kb + 2) MOE_P3(kb + 3) MOE_P4(kb + 4) MOE_P5(kb + 5)
+    }
+  } else if (head == 2) {
+    MOE_P0(0) MOE_P1(1)
+    for (int kb = 2; kb < KB; kb += 6) {
+      MOE_P2(kb) MOE_P3(kb + 1) MOE_P4(kb + 2) MOE_P5(kb + 3) MOE_P0(kb + 4) MOE_P1(kb + 5)
+    }
+  } else {
+    MOE_P0(0) MOE_P1(1) MOE_P2(2) MOE_P3(3)
+    for (int kb = 4; kb < KB; kb += 6) {
+      MOE_P4(kb) MOE_P5(kb + 1) MOE_P0(kb + 2) MOE_P1(kb + 3) MOE_P2(kb + 4) MOE_P3(kb + 5)
+    }
   }
   wait_vmcnt<0>();  // no LDS-direct load may still be landing when the tile ends
   __syncthreads();  // every wave is past its reads of the slots the epilogue reuses
-#undef MOE_DSTEPS_0_1
-#undef MOE_DSTEPS_2_3
-#undef MOE_DSTEPS_4_5
+#undef MOE_P0
+#undef MOE_P1
+#undef MOE_P2
+#undef MOE_P3
+#undef MOE_P4
+#undef MOE_P5
 #undef MOE_DSTEP
 #undef MOE_ISSUE_A
 #undef MOE_ISSUE_B
