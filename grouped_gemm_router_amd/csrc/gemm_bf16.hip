@@ -431,41 +431,48 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
     const uint16_t *__restrict__ B2, void *__restrict__ C, const int32_t *__restrict__ offsets,
     int G, int rows, int N, int K, int nt_count, char *__restrict__ ws, int cus) {
   // 2 A double stages (64 KB) and 3 B double stages (96 KB): all 160 KB of LDS.
-  // The scheduler table lives in the last B slot, which is first loaded
-  // after every wave has passed the prologue barrier.
+  // The scheduler's result (8 ints) passes through the last B slot, which is
+  // first loaded after every wave has passed the prologue barrier.
   __shared__ u32x4 sA0[SLOTS_A2MAX], sA1[SLOTS_A2MAX];
   __shared__ u32x4 sB0[SLOTS_B2], sB1[SLOTS_B2], sB2[SLOTS_B2];
-  static_assert(sizeof(int) * 3 * (MOE_MAX_GROUPS + 1) <= sizeof(u32x4) * SLOTS_B2,
-                "scheduler table must fit in one B slot");
-  int *s_cum = reinterpret_cast<int *>(sB2);
-  int *s_off = s_cum + MOE_MAX_GROUPS + 1;
-  int *s_ord = s_off + MOE_MAX_GROUPS + 1;
-
-  sched_build<NW * 64>(offsets, G, rows, BM_MAX, s_cum, s_off, s_ord, SWIGLU);
-  const int total = s_cum[G] * nt_count;
   const int KT = K / BK;  // a multiple of 4
-  const int S = ws != nullptr ? split_slices(total, cus, KT) : 1;
-  const int n_split = S > 1 ? total % cus : 0;
-  const int full_end = total - n_split;
   const int w = (int)blockIdx.x;
+  // workgroups [0, full_end) take one tile each; with a split tail, S
+  // workgroups per tile after that, one K-slice each
+  auto plan = [&](int total, int *S, int *n_split, int *full_end) {
+    *S = ws != nullptr ? split_slices(total, cus, KT) : 1;
+    *n_split = *S > 1 ? total % cus : 0;
+    *full_end = total - *n_split;
+  };
+  auto pick = [&](int total) {
+    int S, n_split, full_end;
+    plan(total, &S, &n_split, &full_end);
+    if (w < full_end) return w;
+    const int jj = (w - full_end) / S;
+    return jj < n_split ? full_end + jj : -1;
+  };
+  // the scheduler's result lives in the last B slot until the prologue
+  const Sched sc = sched_lookup(offsets, G, rows, BM_MAX, nt_count, kTileChunk, SWIGLU,
+                                reinterpret_cast<int *>(sB2), pick);
+  int S, n_split, full_end;
+  plan(sc.total, &S, &n_split, &full_end);
   if (ws != nullptr && w == 0 && threadIdx.x == 0) {
     int *hdr = reinterpret_cast<int *>(ws);
     hdr[0] = n_split;
     hdr[1] = S;
   }
-  int L = tile_of_workgroup(w, full_end), kbeg = 0, kt = KT, j = -1, slice = 0;
+  if (sc.L < 0) return;
+  int kbeg = 0, kt = KT, j = -1, slice = 0;
   float *part = nullptr;
-  if (L < 0) {  // a K-slice of a split tile, or nothing
+  if (w >= full_end) {  // a K-slice of split tile j
     j = (w - full_end) / S;
     slice = (w - full_end) - j * S;
-    if (j >= n_split) return;
-    L = full_end + j;
     kt = KT / S;
     kbeg = slice * kt * BK;
     part = reinterpret_cast<float *>(ws + split_partial_offset(cus)) +
            (size_t)(j * S + slice) * kPartialFloats;
   }
-  const Tile tile = sched_tile(L, s_cum, s_ord, s_off, G, BM_MAX, nt_count, kTileChunk);
+  const Tile tile = sc.tile;
   if (part != nullptr && slice == 0 && threadIdx.x == 0)
     reinterpret_cast<int4 *>(ws + split_desc_offset())[j] = make_int4(tile.m0, tile.mend, tile.nt, 0);
   const int h = tile.mend - tile.m0;  // wave-uniform

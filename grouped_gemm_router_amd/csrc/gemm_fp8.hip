@@ -52,15 +52,13 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
   __shared__ u32x4 lB[2][B_PIECES];
   __shared__ __attribute__((aligned(16))) float lS[2][FBM];
   __shared__ float s_amax[2][FBM];
-  __shared__ int s_cum[MOE_MAX_GROUPS + 1];
-  __shared__ int s_off[MOE_MAX_GROUPS + 1];
-  __shared__ int s_ord[MOE_MAX_GROUPS];
+  __shared__ int s_x[8];
 
-  sched_build<FNTH>(offsets, G, rows, FBM, s_cum, s_off, s_ord, SWIGLU);
-  const int total = s_cum[G] * nt_count;
-  const int L = tile_of_workgroup((int)blockIdx.x, total);
-  if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, s_ord, s_off, G, FBM, nt_count, kTileChunk);
+  const int w = (int)blockIdx.x;
+  const Sched sc = sched_lookup(offsets, G, rows, FBM, nt_count, kTileChunk, SWIGLU, s_x,
+                                [w](int total) { return tile_of_workgroup(w, total); });
+  if (sc.L < 0) return;
+  const Tile tile = sc.tile;
 
   const int tid = threadIdx.x;
   const int lane = lane_id(), wv = tid / kWave;

@@ -435,25 +435,21 @@ __global__ __launch_bounds__(NTH, 1) void gemm_fp8_ring_kernel(
     const float *__restrict__ B2s, void *__restrict__ C, float *__restrict__ Cs,
     const int32_t *__restrict__ offsets, int G, int rows, int N, int K, int nt_count) {
   // 2 A and 3 B double steps and two scale slots (148 KB of LDS).  The
-  // scheduler tables live in B slot 2, first loaded after every wave has
-  // passed the first barrier; the epilogue's row maxima in A slot 0 once the
-  // loop is done.
+  // scheduler's result (8 ints) passes through B slot 2, first loaded after
+  // every wave has passed the first barrier; the epilogue's row maxima live
+  // in A slot 0 once the loop is done.
   __shared__ u32x4 sA0[SLOTS_A2MAX], sA1[SLOTS_A2MAX];
   __shared__ u32x4 sB0[SLOTS_B2], sB1[SLOTS_B2], sB2[SLOTS_B2];
   __shared__ float sS0[SROWS], sS1[SROWS];
-  static_assert(sizeof(int) * 3 * (MOE_MAX_GROUPS + 1) <= sizeof(u32x4) * SLOTS_B2,
-                "scheduler tables must fit in one B slot");
   static_assert(sizeof(float) * NWN * BM_MAX <= sizeof(u32x4) * SLOTS_A2MAX,
                 "row maxima must fit in one A slot");
-  int *s_cum = reinterpret_cast<int *>(sB2);
-  int *s_off = s_cum + MOE_MAX_GROUPS + 1;
-  int *s_ord = s_off + MOE_MAX_GROUPS + 1;
-
-  sched_build<NTH>(offsets, G, rows, BM_MAX, s_cum, s_off, s_ord, SWIGLU);
-  const int total = s_cum[G] * nt_count;
-  const int L = tile_of_workgroup((int)blockIdx.x, total);
-  if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, s_ord, s_off, G, BM_MAX, nt_count, kTileChunk);
+  // the scheduler's result lives in the last B slot until the prologue
+  const int w = (int)blockIdx.x;
+  const Sched sc = sched_lookup(offsets, G, rows, BM_MAX, nt_count, kTileChunk, SWIGLU,
+                                reinterpret_cast<int *>(sB2),
+                                [w](int total) { return tile_of_workgroup(w, total); });
+  if (sc.L < 0) return;
+  const Tile tile = sc.tile;
   const Ring ring{sA0, sA1, sB0, sB1, sB2, sS0, sS1, reinterpret_cast<float *>(sA0)};
   const int h = tile.mend - tile.m0;  // wave-uniform
   if (h == BM_MAX)

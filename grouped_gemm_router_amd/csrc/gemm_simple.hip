@@ -28,18 +28,16 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(
     const void *__restrict__ A, const void *__restrict__ B, const void *__restrict__ B2,
     void *__restrict__ C, const int32_t *__restrict__ offsets, int G, int rows, int N, int K,
     int nt_count) {
-  __shared__ int s_cum[MOE_MAX_GROUPS + 1];
-  __shared__ int s_off[MOE_MAX_GROUPS + 1];
-  __shared__ int s_ord[MOE_MAX_GROUPS];
+  __shared__ int s_x[8];
   __shared__ float As[SBK][SBM + 1];
   __shared__ float Bs[SBK][SBN + 1];
   __shared__ float B2s[SWIGLU ? SBK : 1][SBN + 1];
 
-  sched_build<256>(offsets, G, rows, SBM, s_cum, s_off, s_ord, SWIGLU);
-  const int total = s_cum[G] * nt_count;
-  const int L = tile_of_workgroup((int)blockIdx.x, total);
-  if (L < 0) return;
-  const Tile tile = sched_tile(L, s_cum, s_ord, s_off, G, SBM, nt_count, kTileChunk);
+  const int w = (int)blockIdx.x;
+  const Sched sc = sched_lookup(offsets, G, rows, SBM, nt_count, kTileChunk, SWIGLU, s_x,
+                                [w](int total) { return tile_of_workgroup(w, total); });
+  if (sc.L < 0) return;
+  const Tile tile = sc.tile;
   const int n0 = tile.nt * SBN;
   const size_t boff = (size_t)tile.g * N * K;
 

@@ -111,66 +111,22 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ int sched_class(int m) { return m > 128 ? 0 : (m > 64 ? 1 : 2); }
 
-// Exclusive scan over the 64 lanes of a wave; *total gets the sum.
+// Exclusive scan over the 64 lanes of a wave; *total gets the sum.  DPP
+// (no LDS round trips): a Hillis-Steele scan inside each row of 16 lanes
+// (row_shr 1, 2, 4, 8; a lane whose source lies outside its row adds 0),
+// then lane 15 of each row pair is added into the row above it (row_bcast15
+// into rows 1 and 3) and lane 31 into the upper half (row_bcast31 into rows
+// 2 and 3).  Must be called by a whole wave.
 __device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
-  const int lane = threadIdx.x & (kWave - 1);
   int incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
-  *total = __shfl(incl, kWave - 1, kWave);
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xf, 0xf, false);  // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xf, 0xf, false);  // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xf, 0xf, false);  // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xf, 0xf, false);  // row_shr:8
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  *total = __builtin_amdgcn_readlane(incl, kWave - 1);
   return incl - v;
-}
-
-// Block-wide: fills, in LDS, off[0..G] with the clamped offsets, ord[p] =
-// the group at position p of the tile order, and cum[0..G] = row tiles of
-// the groups at positions before p (cum[G] = all row tiles).  All threads
-// load the offsets; the first wave alone then builds the order and the
-// prefix (each lane a contiguous run of groups, wave-level scans), so the
-// block meets at two barriers only.  Must be called by all threads.
-template <int NTHREADS>
-__device__ __forceinline__ void sched_build(const int32_t *__restrict__ offsets, int G,
-                                            int rows, int BM, int *cum, int *off, int *ord,
-                                            bool by_class) {
-  for (int g = threadIdx.x; g <= G; g += NTHREADS) off[g] = min(max(offsets[g], 0), rows);
-  __syncthreads();
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    const int per = (G + kWave - 1) / kWave;
-    const int g0 = lane * per, g1 = min(G, g0 + per);
-    // row tiles per class and groups of classes 0 and 1 in this lane's run
-    int t0 = 0, t1 = 0, t2 = 0, n0 = 0, n1 = 0;
-    for (int g = g0; g < g1; ++g) {
-      const int m = max(off[g + 1] - off[g], 0);
-      const int c = by_class ? sched_class(m) : 0;
-      const int t = (m + BM - 1) / BM;
-      if (c == 0) { t0 += t; ++n0; } else if (c == 1) { t1 += t; ++n1; } else { t2 += t; }
-    }
-    int T0, T1, T2, N0, N1;
-    int q0 = wave_exclusive_scan(t0, &T0), q1 = wave_exclusive_scan(t1, &T1);
-    int q2 = wave_exclusive_scan(t2, &T2);
-    int p0 = wave_exclusive_scan(n0, &N0), p1 = wave_exclusive_scan(n1, &N1);
-    // class-2 groups before g0 = g0 minus those of classes 0 and 1
-    int p2 = N0 + N1 + (min(g0, G) - p0 - p1);
-    p1 += N0;
-    q1 += T0;
-    q2 += T0 + T1;
-    for (int g = g0; g < g1; ++g) {
-      const int m = max(off[g + 1] - off[g], 0);
-      const int c = by_class ? sched_class(m) : 0;
-      const int t = (m + BM - 1) / BM;
-      int pos, at;
-      if (c == 0) { pos = p0++; at = q0; q0 += t; }
-      else if (c == 1) { pos = p1++; at = q1; q1 += t; }
-      else { pos = p2++; at = q2; q2 += t; }
-      ord[pos] = g;
-      cum[pos] = at;
-    }
-    if (lane == 0) cum[G] = T0 + T1 + T2;
-  }
-  __syncthreads();
 }
 
 struct Tile {
@@ -179,41 +135,6 @@ struct Tile {
   int mend;  // one past the last valid row of the tile (<= group end)
   int nt;    // column tile index
 };
-
-// Maps a linear tile id to (group, rows, column tile).  cum, ord and off are
-// the LDS tables from sched_build; nt_count column tiles per row tile.
-__device__ __forceinline__ Tile sched_tile(int L, const int *cum, const int *ord, const int *off,
-                                           int G, int BM, int nt_count, int chunk) {
-  // the last position lo < G with cum[lo] * nt_count <= L (cum is
-  // non-decreasing and cum[0] = 0 <= L): a wave-wide ballot over every
-  // step-th position, then one over the positions of that block
-  const int lane = threadIdx.x & (kWave - 1);
-  const int step = (G + kWave - 1) / kWave;
-  int q = lane * step;
-  unsigned long long hit = __ballot(q < G && cum[min(q, G)] * nt_count <= L);
-  const int base = (__popcll(hit) - 1) * step;
-  q = base + lane;
-  hit = __ballot(lane < step && q < G && cum[min(q, G)] * nt_count <= L);
-  const int lo = base + __popcll(hit) - 1;
-  // cum[lo+1] > cum[lo], so position lo never holds an empty group
-  const int g = ord[lo];
-  int mt_g = cum[lo + 1] - cum[lo];
-  int li = L - cum[lo] * nt_count;
-  int per_chunk = chunk * mt_g;
-  int c = li / per_chunk;
-  int within = li - c * per_chunk;
-  int cw = min(chunk, nt_count - c * chunk);
-  int mt = within / cw;
-  int nt = c * chunk + (within - mt * cw);
-  Tile t;
-  t.g = g;
-  int a = off[g];
-  int mg = max(off[g + 1] - a, 0);
-  t.m0 = a + mt * BM;
-  t.mend = min(a + mg, t.m0 + BM);
-  t.nt = nt;
-  return t;
-}
 
 // Tile order.  Linear tile ids run group by group (size classes as above);
 // inside a group, chunks of
@@ -225,6 +146,97 @@ __device__ __forceinline__ Tile sched_tile(int L, const int *cum, const int *ord
 // its L2.  Measured on the Mixtral shapes against giving each XCD its own
 // contiguous range of tiles: gate/up 2.00 -> 1.87 ms, down 1.23 -> 1.04 ms.
 constexpr int kTileChunk = 16;
+
+// Result of sched_lookup: the workgroup's tile, the tile count and the
+// linear id that was looked up (-1: nothing to do).
+struct Sched {
+  Tile tile;
+  int total;
+  int L;
+};
+
+// The device tile scheduler.  Groups have clamped offsets o[g] =
+// min(max(offsets[g], 0), rows) and m_g = max(o[g+1] - o[g], 0) rows, cut
+// into ceil(m_g / BM) row tiles of nt_count column tiles each; with
+// by_class the groups are taken class by class (sched_class), in group order
+// inside a class.  pick(total) maps the total tile count to the linear id
+// this workgroup runs (or -1); the result holds that id's tile.
+//
+// The first wave alone does the work, in registers: each lane loads the
+// offsets of a contiguous run of groups (all loads in flight at once), three
+// DPP scans give every group its first tile id, and the one lane whose run
+// holds the picked id writes the tile to s_x (8 ints of LDS); the block
+// meets at one barrier.  Must be called by all threads.
+template <class Pick>
+__device__ __forceinline__ Sched sched_lookup(const int32_t *__restrict__ offsets, int G, int rows,
+                                              int BM, int nt_count, int chunk, bool by_class,
+                                              int *s_x, Pick pick) {
+  constexpr int kRun = (MOE_MAX_GROUPS + kWave - 1) / kWave;  // groups per lane at most
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int per = (G + kWave - 1) / kWave;
+    const int g0 = lane * per;
+    const int n = max(0, min(G, g0 + per) - g0);  // groups in this lane's run
+    int o[kRun + 1];
+#pragma unroll
+    for (int i = 0; i <= kRun; ++i)
+      o[i] = (i <= n && g0 + i <= G) ? min(max(offsets[g0 + i], 0), rows) : 0;
+    // row tiles of this lane's run, per class
+    int t0 = 0, t1 = 0, t2 = 0;
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      if (i < n) {
+        const int m = max(o[i + 1] - o[i], 0);
+        const int c = by_class ? sched_class(m) : 0;
+        const int t = (m + BM - 1) / BM;
+        if (c == 0) t0 += t; else if (c == 1) t1 += t; else t2 += t;
+      }
+    }
+    int T0, T1, T2;
+    int q0 = wave_exclusive_scan(t0, &T0);
+    int q1 = wave_exclusive_scan(t1, &T1) + T0;
+    int q2 = wave_exclusive_scan(t2, &T2) + T0 + T1;
+    const int total = (T0 + T1 + T2) * nt_count;
+    const int L = pick(total);  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      if (i < n) {
+        const int m = max(o[i + 1] - o[i], 0);
+        const int c = by_class ? sched_class(m) : 0;
+        const int t = (m + BM - 1) / BM;
+        int at;
+        if (c == 0) { at = q0; q0 += t; } else if (c == 1) { at = q1; q1 += t; } else { at = q2; q2 += t; }
+        const int li = L - at * nt_count;  // tile id inside the group
+        if (L >= 0 && li >= 0 && li < t * nt_count) {
+          // chunks of `chunk` column tiles, row tiles fastest within a chunk
+          const int per_chunk = chunk * t;
+          const int ch = li / per_chunk;
+          const int within = li - ch * per_chunk;
+          const int cw = min(chunk, nt_count - ch * chunk);
+          const int mt = within / cw;
+          const int m0 = o[i] + mt * BM;
+          s_x[0] = g0 + i;
+          s_x[1] = m0;
+          s_x[2] = min(o[i] + m, m0 + BM);
+          s_x[3] = ch * chunk + (within - mt * cw);
+        }
+      }
+    }
+    if (lane == 0) {
+      s_x[4] = total;
+      s_x[5] = L;
+    }
+  }
+  __syncthreads();
+  Sched r;
+  r.tile.g = s_x[0];
+  r.tile.m0 = s_x[1];
+  r.tile.mend = s_x[2];
+  r.tile.nt = s_x[3];
+  r.total = s_x[4];
+  r.L = s_x[5];
+  return r;
+}
 
 // Linear tile id of workgroup w, or -1 for a workgroup with nothing to do.
 __device__ __forceinline__ int tile_of_workgroup(int w, int total) { return w < total ? w : -1; }
