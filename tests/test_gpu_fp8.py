@@ -170,6 +170,30 @@ def test_fp8_gemm_bf16_out(orc, sizes, N, K, swiglu):
     assert_within(C.float().cpu().numpy(), ref, bound)
 
 
+# The 1040-group limit (the scheduler's lanes hold runs of 17 groups), mostly
+# empty or tiny groups plus one of each tile height; K = 256 runs the LDS-ring
+# kernel, K = 128 the general one.
+@pytest.mark.parametrize("K,swiglu", [(256, False), (256, True), (128, False)])
+def test_fp8_gemm_max_groups(orc, K, swiglu):
+    rng = np.random.default_rng(91)
+    G, N = 1040, 128
+    sizes = rng.integers(0, 3, G)
+    sizes[rng.permutation(G)[:4]] = [193, 129, 64, 257]
+    offs, Aq, As, Bq, Bs, B2q, B2s = make_fp8(sizes, N, K, 95 + K, swiglu)
+    a = api()
+    rows = int(offs[-1])
+    dAq, dAs, dBq, dBs, dB2q, dB2s = dev_operands(Aq, As, Bq, Bs, B2q, B2s)
+    C = torch.full((rows, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    a.moe_grouped_gemm_fp8(dAq, dAs, dBq, dBs, C, torch.from_numpy(offs).to(DEV), B2_q=dB2q,
+                           B2_scale=dB2s, epi=a.MOE_EPI_SWIGLU if swiglu else a.MOE_EPI_NONE)
+    torch.cuda.synchronize()
+    ref, bound = fp8_ref_and_bound(orc, Aq.numpy(), As.numpy(), Bq.numpy(), Bs.numpy(),
+                                   None if B2q is None else B2q.numpy(),
+                                   None if B2s is None else B2s.numpy(), offs, np.arange(rows),
+                                   swiglu, 2.0 ** -8)
+    assert_within(C.float().cpu().numpy(), ref, bound)
+
+
 @pytest.mark.parametrize("sizes", [[0, 3, 129, 256], [40], [70, 300]])
 @pytest.mark.parametrize("N,K", [(256, 256), (128, 128), (384, 512)])
 def test_fp8_gemm_e4m3_out_swiglu(orc, sizes, N, K):

@@ -114,6 +114,32 @@ def test_rows_outside_groups_untouched():
     assert (C[25:].float() == 7.0).all()
 
 
+def many_group_sizes(G, seed):
+    """G groups, most of them empty or a few rows, with one of every tile
+    height (64, 128, 256 and a 256 + 1 split) among them."""
+    rng = np.random.default_rng(seed)
+    sizes = rng.integers(0, 4, G)
+    sizes[rng.permutation(G)[:4]] = [300, 129, 64, 257]
+    return sizes
+
+
+# Group counts that give the scheduler's lanes runs of different lengths:
+# 65 (runs of 2, the last lane's cut short), 129 (runs of 3) and the
+# 1040-group limit (runs of 17, the longest).  K = 128 runs the MFMA kernel,
+# K = 64 the vector path.
+@pytest.mark.parametrize("G", [65, 129, 1040])
+@pytest.mark.parametrize("K", [128, 64])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_many_groups_all_rows(orc, G, K, swiglu):
+    sizes = many_group_sizes(G, 800 + G)
+    N = 128 if swiglu else 256
+    A, B, B2, offs = make(sizes, N, K, torch.bfloat16, 810 + G + K, swiglu)
+    C = gpu_gemm(A, B, B2, offs, torch.bfloat16, swiglu)
+    ref, bound = ref_and_bound(orc, np_of(A), np_of(B), None if B2 is None else np_of(B2), offs,
+                               np.arange(A.shape[0]), swiglu, 2.0 ** -8)
+    assert_within(C.float().cpu().numpy(), ref, bound)
+
+
 def _sampled_check(orc, A, B, B2, offs, C, swiglu, per_group=4):
     rows = sample_rows(offs, per_group=per_group, seed=1)
     An = np_of(A[torch.from_numpy(rows).to(DEV)])
