@@ -192,7 +192,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build measures the MoE layer on a single "
+        print("bench.py runs on one GPU only: it measures the MoE layer on a single "
               "MI355X (no collectives); got --gpus %d / WORLD_SIZE %d" % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
