@@ -495,11 +495,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
 
 // Sum of the S partial tiles of each split tile, in slice order, then the
 // epilogue.  Work item (j, rb) is rows [16 rb, 16 rb + 16) of split tile j;
-// the grid is one workgroup per CU looping over the items, so the launch
+// the grid is four workgroups per CU looping over the items, so the launch
 // stays cheap when nothing was split (the plan is only known on the
-// device); a thread handles 4 consecutive B-tile columns (16 bytes per
-// partial).
+// device).  A thread owns RPT (row, 4-column group) pairs of an item and
+// issues the loads of all of them, every slice, before the first add (16
+// bytes per partial); the adds then run in slice order.
 constexpr int kReduceRows = 16;
+constexpr int kReduceWGPerCU = 4;
 
 template <bool SWIGLU, bool OUT_F32>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const char *__restrict__ ws,
@@ -507,6 +509,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const char *__restric
   const int *hdr = reinterpret_cast<const int *>(ws);
   const int n_split = hdr[0], S = hdr[1];
   constexpr int RB = BM_MAX / kReduceRows;
+  constexpr int C4 = SWIGLU ? BN / 8 : BN / 4;  // 4-column groups per output row
+  constexpr int RPT = kReduceRows * C4 / 256;   // (row, group) pairs per thread
+  static_assert(RPT * 256 == kReduceRows * C4, "an item is a whole number of passes");
   for (int item = blockIdx.x; item < n_split * RB; item += gridDim.x) {
     const int j = item / RB, r0 = (item % RB) * kReduceRows;
     const int4 d = reinterpret_cast<const int4 *>(ws + split_desc_offset())[j];
@@ -514,34 +519,46 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const char *__restric
     if (r0 >= h) continue;
     const float *P = reinterpret_cast<const float *>(ws + split_partial_offset(cus)) +
                      (size_t)j * S * kPartialFloats;
-    constexpr int C4 = SWIGLU ? BN / 8 : BN / 4;  // 4-column groups per output row
-    for (int idx = threadIdx.x; idx < kReduceRows * C4; idx += 256) {
+    float4 g[RPT][kSplitMax], u[RPT][kSplitMax];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int idx = i * 256 + (int)threadIdx.x;
       const int r = r0 + idx / C4, c = (idx % C4) * 4;
-      if (r >= h) break;  // idx / C4 only grows
       const float *p0 = P + (size_t)r * BN + c;
-      float4 g = *reinterpret_cast<const float4 *>(p0);
-      float4 u = SWIGLU ? *reinterpret_cast<const float4 *>(p0 + BN / 2) : float4{};
-      for (int q = 1; q < S; ++q) {
-        const float4 a = *reinterpret_cast<const float4 *>(p0 + q * kPartialFloats);
-        g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
-        if (SWIGLU) {
-          const float4 b = *reinterpret_cast<const float4 *>(p0 + q * kPartialFloats + BN / 2);
-          u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+#pragma unroll
+      for (int q = 0; q < kSplitMax; ++q) {
+        if (q < S && r < h) {
+          g[i][q] = *reinterpret_cast<const float4 *>(p0 + q * kPartialFloats);
+          if (SWIGLU) u[i][q] = *reinterpret_cast<const float4 *>(p0 + q * kPartialFloats + BN / 2);
         }
       }
-      float v[4] = {g.x, g.y, g.z, g.w};
-      if (SWIGLU) {
-        const float uu[4] = {u.x, u.y, u.z, u.w};
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)  // silu as in the tile epilogue
-          v[i] = OUT_F32 ? v[i] / (1.0f + expf(-v[i])) * uu[i]
-                         : v[i] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * v[i])) * uu[i];
+    for (int i = 0; i < RPT; ++i) {
+      const int idx = i * 256 + (int)threadIdx.x;
+      const int r = r0 + idx / C4, c = (idx % C4) * 4;
+      if (r >= h) continue;
+      float4 gs = g[i][0], us = SWIGLU ? u[i][0] : float4{};
+#pragma unroll
+      for (int q = 1; q < kSplitMax; ++q) {
+        if (q < S) {
+          gs.x += g[i][q].x; gs.y += g[i][q].y; gs.z += g[i][q].z; gs.w += g[i][q].w;
+          if (SWIGLU) { us.x += u[i][q].x; us.y += u[i][q].y; us.z += u[i][q].z; us.w += u[i][q].w; }
+        }
+      }
+      float v[4] = {gs.x, gs.y, gs.z, gs.w};
+      if (SWIGLU) {
+        const float uu[4] = {us.x, us.y, us.z, us.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)  // silu as in the tile epilogue
+          v[e] = OUT_F32 ? v[e] / (1.0f + expf(-v[e])) * uu[e]
+                         : v[e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * v[e])) * uu[e];
       }
       const size_t o = (size_t)(d.x + r) * N + (size_t)d.z * (SWIGLU ? BN / 2 : BN) + c;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (OUT_F32) static_cast<float *>(C)[o + i] = v[i];
-        else static_cast<uint16_t *>(C)[o + i] = f32_to_bf16_bits(v[i]);
+      for (int e = 0; e < 4; ++e) {
+        if (OUT_F32) static_cast<float *>(C)[o + e] = v[e];
+        else static_cast<uint16_t *>(C)[o + e] = f32_to_bf16_bits(v[e]);
       }
     }
   }
@@ -558,7 +575,8 @@ void launch_t(const void *A, const void *B, const void *B2, void *C, const int32
                      static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(B2), C,
                      offsets, G, rows, N, K, nt, ws, cus);
   if (ws == nullptr) return;
-  hipLaunchKernelGGL((split_reduce_kernel<SWIGLU, OUT_F32>), dim3((unsigned)cus), dim3(256), 0, s,
+  hipLaunchKernelGGL((split_reduce_kernel<SWIGLU, OUT_F32>), dim3((unsigned)(kReduceWGPerCU * cus)),
+                     dim3(256), 0, s,
                      ws, C, N, cus);
 }
 
