@@ -109,13 +109,39 @@ def traffic_record(fetch_csv: str, write_csv: str, kernel: str, config: str) -> 
 LIBRARY_KERNELS = re.compile(r"route_|perm_|gemm_|split_reduce|combine_|stats_|quantize")
 
 
-def trace_summary(stats_csv: str, config: str, command: str) -> str:
-    """Markdown table of a rocprofv3 kernel_stats.csv."""
+def timed_averages(trace_csv: str, last: int) -> dict:
+    """Average duration (ns) of the last `last` dispatches of every kernel in
+    a rocprofv3 kernel_trace.csv (in dispatch order): the timed steps of a
+    bench run, without its warm-up calls."""
+    per = {}
+    for r in csv.DictReader(open(trace_csv)):
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for name, v in per.items():
+        v.sort()
+        tail = [d for _, d in v[-last:]]
+        out[name] = sum(tail) / len(tail)
+    return out
+
+
+def trace_summary(stats_csv: str, config: str, command: str, trace_csv: str = None,
+                  timed: int = 0) -> str:
+    """Markdown table of a rocprofv3 kernel_stats.csv; with the matching
+    kernel_trace.csv, also the average over the last `timed` calls."""
     rows = list(csv.DictReader(open(stats_csv)))
+    tavg = timed_averages(trace_csv, timed) if trace_csv and timed > 0 else None
     lines = ["# Kernel trace: MoE layer step, %s" % config, "",
              "Command (from /tmp, `$REPO` = repository root, one MI355X):", "",
-             "```", command, "```", "",
-             "| Kernel | Calls | Avg (us) | Min (us) | Max (us) |", "|---|---|---|---|---|"]
+             "```", command, "```", ""]
+    if tavg is not None:
+        lines += ["'Timed avg' is the mean of each kernel's last %d calls (the bench's timed "
+                  "steps, without the warm-up calls run before the clocks settle); it is the "
+                  "figure to compare with the bench's per-kernel HIP-event times." % timed, "",
+                  "| Kernel | Calls | Avg (us) | Timed avg (us) | Min (us) | Max (us) |",
+                  "|---|---|---|---|---|---|"]
+    else:
+        lines += ["| Kernel | Calls | Avg (us) | Min (us) | Max (us) |", "|---|---|---|---|---|"]
     other_calls, other_ns = 0, 0.0
     for r in rows:
         name = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "")
@@ -123,9 +149,15 @@ def trace_summary(stats_csv: str, config: str, command: str) -> str:
             other_calls += int(r["Calls"])
             other_ns += float(r["TotalDurationNs"])
             continue
-        lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (
-            name.split("(")[0], r["Calls"], float(r["AverageNs"]) / 1e3,
-            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+        if tavg is not None:
+            lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.2f |" % (
+                name.split("(")[0], r["Calls"], float(r["AverageNs"]) / 1e3,
+                tavg.get(r["Name"], float("nan")) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3))
+        else:
+            lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (
+                name.split("(")[0], r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
     lines += ["", "Input generation and copies outside the layer (torch kernels): %d calls, "
               "%.1f ms in total." % (other_calls, other_ns / 1e6), ""]
     return "\n".join(lines)
@@ -138,12 +170,15 @@ def main() -> None:
     p.add_argument("--kernel", choices=sorted(KERNEL_PATTERNS))
     p.add_argument("--stats", help="kernel_stats.csv of a kernel trace")
     p.add_argument("--command", help="the rocprofv3 command of the trace")
+    p.add_argument("--trace", help="kernel_trace.csv of the same run (per dispatch)")
+    p.add_argument("--timed", type=int, default=0,
+                   help="with --trace: average the last this many calls of each kernel")
     p.add_argument("--config", required=True)
     p.add_argument("--out", required=True,
                    help="traffic: output path without extension (.json); trace: the .md path")
     a = p.parse_args()
     if a.stats:
-        text = trace_summary(a.stats, a.config, a.command or "")
+        text = trace_summary(a.stats, a.config, a.command or "", a.trace, a.timed)
         with open(a.out, "w") as f:
             f.write(text)
         print(text)
