@@ -362,6 +362,52 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
       }
     return;
   }
+  if constexpr (SWIGLU && !OUT_F32) {
+    // bf16 gate/up output: the whole tile (BM rows x 128 columns, at most
+    // 64 KB) is staged at once -- wave row wm into A slot wm, both free once
+    // every wave is past the last stage -- then every thread stores its
+    // 16-byte row pieces: one barrier instead of two per 32-row block, all
+    // of a thread's stores in flight together.  The 16-byte piece index is
+    // XORed with bit 2 of the row, so the two rows one write instruction
+    // touches (4 apart) fall in different banks.
+    constexpr int TC = BN / 2;      // output columns of the tile
+    constexpr int ROWB = TC * 2;    // bytes per staged row
+    constexpr int PPR = ROWB / 16;  // 16-byte pieces per row
+    constexpr int WR = MI * 32;     // rows of one wave row
+    static_assert(WR * ROWB <= (int)sizeof(u32x4) * SLOTS_A2MAX, "a wave row must fit an A slot");
+    __syncthreads();  // every wave is done reading the rings
+    char *const stg_w = reinterpret_cast<char *>(wm == 0 ? sA0 : sA1);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int nb = 0; nb < NB / 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
+          const int c = wn * (TC / NWN) + nb * 32 + col;
+          const float g = acc[mi][nb][r], u = acc[mi][nb + NB / 2][r];
+          // hardware exp2 and reciprocal (each within 1 ulp; far below the
+          // bf16 rounding)
+          const float v = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * g)) * u;
+          const int off = row * ROWB + ((((c * 2) >> 4) ^ ((row >> 2) & 1)) << 4) + ((c * 2) & 15);
+          *reinterpret_cast<__bf16 *>(stg_w + off) = (__bf16)v;  // round to nearest even
+        }
+    __syncthreads();
+    const size_t col0 = (size_t)tile.nt * TC;
+#pragma unroll
+    for (int i = 0; i < (2 * WR * PPR) / (NW * 64); ++i) {
+      const int q = i * (NW * 64) + tid;
+      const int wr = q / (WR * PPR), rr = (q / PPR) % WR, pc = q % PPR;
+      const int m = tile.m0 + wr * WR + rr;
+      if (m < tile.mend) {
+        const char *sp = reinterpret_cast<const char *>(wr == 0 ? sA0 : sA1) + rr * ROWB +
+                         ((pc ^ ((rr >> 2) & 1)) << 4);
+        *reinterpret_cast<u32x4 *>(static_cast<char *>(C) + ((size_t)m * N + col0) * 2 + pc * 16) =
+            *reinterpret_cast<const u32x4 *>(sp);
+      }
+    }
+    return;
+  }
   // Output, one 32-row block (mi) of every wave at a time: each wave writes
   // its values into LDS -- wave row wm into B slot wm, free once every wave
   // is past the last stage -- as [32 rows][TC columns] of the output type,

@@ -155,6 +155,71 @@ struct Sched {
   int L;
 };
 
+// The first wave's part of sched_lookup for runs of at most RUN groups per
+// lane: each lane loads the offsets of its run (all loads unconditional,
+// the index clamped to G, so that they are in flight at once -- a load under
+// a lane condition gets its own wait), three DPP scans give every group its
+// first tile id, and the lane whose run holds the picked id writes the tile.
+template <int RUN, class Pick>
+__device__ __forceinline__ void sched_wave(const int32_t *__restrict__ offsets, int G, int rows,
+                                           int BM, int nt_count, int chunk, bool by_class,
+                                           int *s_x, Pick pick) {
+  const int lane = threadIdx.x;
+  const int per = (G + kWave - 1) / kWave;
+  const int g0 = lane * per;
+  const int n = max(0, min(G, g0 + per) - g0);  // groups in this lane's run
+  int o[RUN + 1];
+#pragma unroll
+  for (int i = 0; i <= RUN; ++i) o[i] = offsets[min(g0 + i, G)];
+#pragma unroll
+  for (int i = 0; i <= RUN; ++i) o[i] = (i <= n) ? min(max(o[i], 0), rows) : 0;
+  // row tiles of this lane's run, per class
+  int t0 = 0, t1 = 0, t2 = 0;
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    if (i < n) {
+      const int m = max(o[i + 1] - o[i], 0);
+      const int c = by_class ? sched_class(m) : 0;
+      const int t = (m + BM - 1) / BM;
+      if (c == 0) t0 += t; else if (c == 1) t1 += t; else t2 += t;
+    }
+  }
+  int T0, T1, T2;
+  int q0 = wave_exclusive_scan(t0, &T0);
+  int q1 = wave_exclusive_scan(t1, &T1) + T0;
+  int q2 = wave_exclusive_scan(t2, &T2) + T0 + T1;
+  const int total = (T0 + T1 + T2) * nt_count;
+  const int L = pick(total);  // wave-uniform
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    if (i < n) {
+      const int m = max(o[i + 1] - o[i], 0);
+      const int c = by_class ? sched_class(m) : 0;
+      const int t = (m + BM - 1) / BM;
+      int at;
+      if (c == 0) { at = q0; q0 += t; } else if (c == 1) { at = q1; q1 += t; } else { at = q2; q2 += t; }
+      const int li = L - at * nt_count;  // tile id inside the group
+      if (L >= 0 && li >= 0 && li < t * nt_count) {
+        // chunks of `chunk` column tiles, row tiles fastest within a chunk
+        const int per_chunk = chunk * t;
+        const int ch = li / per_chunk;
+        const int within = li - ch * per_chunk;
+        const int cw = min(chunk, nt_count - ch * chunk);
+        const int mt = within / cw;
+        const int m0 = o[i] + mt * BM;
+        s_x[0] = g0 + i;
+        s_x[1] = m0;
+        s_x[2] = min(o[i] + m, m0 + BM);
+        s_x[3] = ch * chunk + (within - mt * cw);
+      }
+    }
+  }
+  if (lane == 0) {
+    s_x[4] = total;
+    s_x[5] = L;
+  }
+}
+
 // The device tile scheduler.  Groups have clamped offsets o[g] =
 // min(max(offsets[g], 0), rows) and m_g = max(o[g+1] - o[g], 0) rows, cut
 // into ceil(m_g / BM) row tiles of nt_count column tiles each; with
@@ -162,70 +227,25 @@ struct Sched {
 // inside a class.  pick(total) maps the total tile count to the linear id
 // this workgroup runs (or -1); the result holds that id's tile.
 //
-// The first wave alone does the work, in registers: each lane loads the
-// offsets of a contiguous run of groups (all loads in flight at once), three
-// DPP scans give every group its first tile id, and the one lane whose run
-// holds the picked id writes the tile to s_x (8 ints of LDS); the block
-// meets at one barrier.  Must be called by all threads.
+// The first wave alone does the work, in registers (sched_wave, compiled for
+// a few run lengths: up to 64, 256, 512 and MOE_MAX_GROUPS groups), and
+// writes the tile to s_x (8 ints of LDS); the block meets at one barrier.
+// Must be called by all threads.
 template <class Pick>
 __device__ __forceinline__ Sched sched_lookup(const int32_t *__restrict__ offsets, int G, int rows,
                                               int BM, int nt_count, int chunk, bool by_class,
                                               int *s_x, Pick pick) {
   constexpr int kRun = (MOE_MAX_GROUPS + kWave - 1) / kWave;  // groups per lane at most
   if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    const int per = (G + kWave - 1) / kWave;
-    const int g0 = lane * per;
-    const int n = max(0, min(G, g0 + per) - g0);  // groups in this lane's run
-    int o[kRun + 1];
-#pragma unroll
-    for (int i = 0; i <= kRun; ++i)
-      o[i] = (i <= n && g0 + i <= G) ? min(max(offsets[g0 + i], 0), rows) : 0;
-    // row tiles of this lane's run, per class
-    int t0 = 0, t1 = 0, t2 = 0;
-#pragma unroll
-    for (int i = 0; i < kRun; ++i) {
-      if (i < n) {
-        const int m = max(o[i + 1] - o[i], 0);
-        const int c = by_class ? sched_class(m) : 0;
-        const int t = (m + BM - 1) / BM;
-        if (c == 0) t0 += t; else if (c == 1) t1 += t; else t2 += t;
-      }
-    }
-    int T0, T1, T2;
-    int q0 = wave_exclusive_scan(t0, &T0);
-    int q1 = wave_exclusive_scan(t1, &T1) + T0;
-    int q2 = wave_exclusive_scan(t2, &T2) + T0 + T1;
-    const int total = (T0 + T1 + T2) * nt_count;
-    const int L = pick(total);  // wave-uniform
-#pragma unroll
-    for (int i = 0; i < kRun; ++i) {
-      if (i < n) {
-        const int m = max(o[i + 1] - o[i], 0);
-        const int c = by_class ? sched_class(m) : 0;
-        const int t = (m + BM - 1) / BM;
-        int at;
-        if (c == 0) { at = q0; q0 += t; } else if (c == 1) { at = q1; q1 += t; } else { at = q2; q2 += t; }
-        const int li = L - at * nt_count;  // tile id inside the group
-        if (L >= 0 && li >= 0 && li < t * nt_count) {
-          // chunks of `chunk` column tiles, row tiles fastest within a chunk
-          const int per_chunk = chunk * t;
-          const int ch = li / per_chunk;
-          const int within = li - ch * per_chunk;
-          const int cw = min(chunk, nt_count - ch * chunk);
-          const int mt = within / cw;
-          const int m0 = o[i] + mt * BM;
-          s_x[0] = g0 + i;
-          s_x[1] = m0;
-          s_x[2] = min(o[i] + m, m0 + BM);
-          s_x[3] = ch * chunk + (within - mt * cw);
-        }
-      }
-    }
-    if (lane == 0) {
-      s_x[4] = total;
-      s_x[5] = L;
-    }
+    const int per = (G + kWave - 1) / kWave;  // wave-uniform
+    if (per <= 1)
+      sched_wave<1>(offsets, G, rows, BM, nt_count, chunk, by_class, s_x, pick);
+    else if (per <= 4)
+      sched_wave<4>(offsets, G, rows, BM, nt_count, chunk, by_class, s_x, pick);
+    else if (per <= 8)
+      sched_wave<8>(offsets, G, rows, BM, nt_count, chunk, by_class, s_x, pick);
+    else
+      sched_wave<kRun>(offsets, G, rows, BM, nt_count, chunk, by_class, s_x, pick);
   }
   __syncthreads();
   Sched r;
