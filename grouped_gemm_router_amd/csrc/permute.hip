@@ -38,6 +38,10 @@ using namespace moe;
 constexpr int kBlk = 64;  // tokens per rank block (one wave)
 
 // ---- 1. rank ---------------------------------------------------------------
+// KMAX >= k: a lane loads its token's k expert ids once, all loads
+// unconditional (token and slot indices clamped into range) so that they
+// are in flight together, and keeps them for both passes.
+template <int KMAX>
 __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t *__restrict__ idx, int T,
                                                         int k, int E, int nblk,
                                                         int32_t *__restrict__ blk_counts,
@@ -46,24 +50,30 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t *__restric
   const int lane = lane_id(), wv = threadIdx.x / kWave;
   const int b = blockIdx.x * 4 + wv;
   unsigned long long *mine = bits + (size_t)wv * E;
-  for (int e = lane; e < E; e += kWave) mine[e] = 0ull;
-  __syncthreads();
   const int t = b * kBlk + lane;
   const bool live = (b < nblk) && (t < T);
+  int ev[KMAX];
+  const size_t row = (size_t)min(t, T - 1) * k;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) ev[j] = idx[row + min(j, k - 1)];
+  for (int e = lane; e < E; e += kWave) mine[e] = 0ull;
+  __syncthreads();
   if (live) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j];
-      if (e >= 0 && e < E) atomicOr(&mine[e], 1ull << lane);
-    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k && ev[j] >= 0 && ev[j] < E) atomicOr(&mine[ev[j]], 1ull << lane);
   }
   __syncthreads();
   if (live) {
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j];
-      int r = -1;
-      if (e >= 0 && e < E) r = __popcll(mine[e] & below);
-      flat_to_row[(size_t)t * k + j] = r;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k) {
+        const int e = ev[j];
+        int r = -1;
+        if (e >= 0 && e < E) r = __popcll(mine[e] & below);
+        flat_to_row[(size_t)t * k + j] = r;
+      }
     }
   }
   if (b < nblk)
@@ -331,9 +341,16 @@ hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *
   const int nblk = (T + kBlk - 1) / kBlk;
   int32_t *blk = static_cast<int32_t *>(ws);
   int32_t *ovf_start = blk + (size_t)nblk * E;
-  hipLaunchKernelGGL(perm_rank_kernel, dim3((nblk + 3) / 4), dim3(256),
-                     sizeof(unsigned long long) * 4 * (size_t)E, s, topk_idx, T, k, E, nblk, blk,
-                     flat_to_row);
+  const size_t rank_lds = sizeof(unsigned long long) * 4 * (size_t)E;
+  if (k <= 2)
+    hipLaunchKernelGGL(perm_rank_kernel<2>, dim3((nblk + 3) / 4), dim3(256), rank_lds, s,
+                       topk_idx, T, k, E, nblk, blk, flat_to_row);
+  else if (k <= 8)
+    hipLaunchKernelGGL(perm_rank_kernel<8>, dim3((nblk + 3) / 4), dim3(256), rank_lds, s,
+                       topk_idx, T, k, E, nblk, blk, flat_to_row);
+  else
+    hipLaunchKernelGGL(perm_rank_kernel<MOE_MAX_TOPK>, dim3((nblk + 3) / 4), dim3(256), rank_lds,
+                       s, topk_idx, T, k, E, nblk, blk, flat_to_row);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, T, E, n_shared, nblk, capacity,
