@@ -350,16 +350,28 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
       }
     }
   } else if (!OUT_FP8) {
-    // bf16 output, staged per 32-token block: every wave writes its 32
-    // tokens x 64 columns into a [32 tokens][256 columns] block of LDS (wave
-    // row wm in B slot wm, free once every wave is past the last step), then
-    // all threads store whole 16-byte row pieces, where the direct stores
-    // would write 16 bytes into each of 32 rows per instruction.  The 16-byte
-    // piece index is XORed with the token row, so the reads are conflict free.
+    // bf16 output, staged whole: every wave writes its 32-token x 64-column
+    // blocks into LDS as [32 tokens][256 columns] blocks -- tile row block
+    // b = wm * MI + mi in half b % 2 of B slot b / 2 (the whole tile is at
+    // most 192 x 256 x 2 bytes, the three B slots) -- then, after one
+    // barrier, every thread stores its whole 16-byte row pieces, all in
+    // flight together (the direct stores would write 16 bytes into each of 32
+    // rows per instruction).  The 16-byte piece index is XORed with the token
+    // row, so the reads are conflict free.
+    constexpr int BLK = 32 * 512;  // bytes per staged 32-row block
+    static_assert(2 * BLK <= (int)sizeof(u32x4) * SLOTS_B2, "two row blocks per B slot");
+    static_assert(BM <= 6 * 32, "the tile must fit the three B slots");
+    char *const s0 = reinterpret_cast<char *>(ring.b0);
+    char *const s1 = reinterpret_cast<char *>(ring.b1);
+    char *const s2 = reinterpret_cast<char *>(ring.b2);
+    auto slot = [s0, s1, s2](int b) -> char * {
+      const int sl = b >> 1;
+      return (sl == 0 ? s0 : (sl == 1 ? s1 : s2)) + (b & 1) * BLK;
+    };
     __syncthreads();
-    char *const stg = reinterpret_cast<char *>(wm == 0 ? ring.b0 : ring.b1);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
+      char *const stg = slot(wm * MI + mi);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -369,18 +381,18 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
               uint2{bf16x2_bits(acc[mi][nb][4 * j], acc[mi][nb][4 * j + 1]),
                     bf16x2_bits(acc[mi][nb][4 * j + 2], acc[mi][nb][4 * j + 3])};
         }
-      __syncthreads();
-      for (int q = tid; q < 2 * 32 * 32; q += NTH) {
-        const int wr = q >> 10, rr = (q >> 5) & 31, pc = q & 31;
-        const int m = tile.m0 + wr * (MI * 32) + mi * 32 + rr;
-        const int n = tile.nt * 256 + pc * 8;
-        if (m < tile.mend && n < N)
-          *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(C) + (size_t)m * N + n) =
-              *reinterpret_cast<const u32x4 *>(
-                  reinterpret_cast<const char *>(wr == 0 ? ring.b0 : ring.b1) + rr * 512 +
-                  ((pc ^ rr) << 4));
-      }
-      __syncthreads();  // the staging blocks are rewritten for the next mi
+    }
+    __syncthreads();
+    static_assert((BM * 32) % NTH == 0, "whole store passes");
+#pragma unroll
+    for (int i = 0; i < BM * 32 / NTH; ++i) {
+      const int q = i * NTH + tid;
+      const int row = q >> 5, pc = q & 31, rr = row & 31;
+      const int m = tile.m0 + row;
+      const int n = tile.nt * 256 + pc * 8;
+      if (m < tile.mend && n < N)
+        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(C) + (size_t)m * N + n) =
+            *reinterpret_cast<const u32x4 *>(slot(row >> 5) + rr * 512 + ((pc ^ rr) << 4));
     }
   } else {
     // columns nt*256 + 64 wn + 32 nb + 8 j + 4 fh + i; quantisation group
