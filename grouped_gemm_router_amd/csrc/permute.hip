@@ -180,6 +180,19 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_sha
 }
 
 // ---- 3. scatter + row copy ----------------------------------------------------
+// Maximum over each aligned group of 8 lanes, by DPP (no LDS round
+// trips): swap neighbours (quad_perm 1,0,3,2), then pairs (quad_perm
+// 2,3,0,1), then the two quads of the group (row_half_mirror).
+__device__ __forceinline__ float group_max8(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                   0, __builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                   0, __builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                   0, __builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false)));
+  return v;
+}
+
 template <int ESIZE, bool QUANT>
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
     const void *__restrict__ xv, int T, int d, const int32_t *__restrict__ idx, int k, int E,
@@ -251,43 +264,46 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
       }
     }
   } else {
-    // one 1 x 128 group per 16 lanes, 8 elements per lane
+    // one 1 x 128 group per 8 lanes, 16 elements (one 16-byte E4M3 store)
+    // per lane
     const int gpr = d / 128;
     const int items = (t1 - t0) * gpr;
-    const int lane16 = threadIdx.x & 15;
+    const int lane8 = threadIdx.x & 7;
     uint8_t *dst = static_cast<uint8_t *>(x_perm);
-    // every 16-lane group iterates the same number of times, so the
-    // shuffles below always see their whole group; each iteration takes two
-    // groups (stride apart) and issues both loads before using either
-    const int stride = blockDim.x >> 4;
+    // every 8-lane group iterates the same number of times (the group max
+    // below needs its whole group); each iteration takes two groups (stride
+    // apart) and issues both loads before using either
+    const int stride = blockDim.x >> 3;
     const int rounds = (items + 2 * stride - 1) / (2 * stride);
     for (int rd = 0; rd < rounds; ++rd) {
-      float v[2][8];
+      float v[2][16];
       int its[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int it = rd * 2 * stride + h * stride + (threadIdx.x >> 4);
+        const int it = rd * 2 * stride + h * stride + (threadIdx.x >> 3);
         its[h] = it;
         if (it < items) {
           const int tt = it / gpr, gi = it - tt * gpr;
-          const size_t e0 = (size_t)(t0 + tt) * d + gi * 128 + lane16 * 8;
+          const size_t e0 = (size_t)(t0 + tt) * d + gi * 128 + lane8 * 16;
           if (ESIZE == 2) {
-            const uint4 raw = *reinterpret_cast<const uint4 *>(x + e0 * 2);
-            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+            const uint4 r0 = *reinterpret_cast<const uint4 *>(x + e0 * 2);
+            const uint4 r1 = *reinterpret_cast<const uint4 *>(x + e0 * 2 + 16);
+            const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 8; ++i) {
               v[h][2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
               v[h][2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
             }
           } else {
-            const float4 a = *reinterpret_cast<const float4 *>(x + e0 * 4);
-            const float4 b2 = *reinterpret_cast<const float4 *>(x + e0 * 4 + 16);
-            v[h][0] = a.x; v[h][1] = a.y; v[h][2] = a.z; v[h][3] = a.w;
-            v[h][4] = b2.x; v[h][5] = b2.y; v[h][6] = b2.z; v[h][7] = b2.w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float4 a = *reinterpret_cast<const float4 *>(x + e0 * 4 + 16 * i);
+              v[h][4 * i] = a.x; v[h][4 * i + 1] = a.y; v[h][4 * i + 2] = a.z; v[h][4 * i + 3] = a.w;
+            }
           }
         } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[h][i] = 0.f;
+          for (int i = 0; i < 16; ++i) v[h][i] = 0.f;
         }
       }
 #pragma unroll
@@ -298,13 +314,15 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
         const int t = t0 + tt;
         float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[h][i]));
-        amax = group_max(amax, 16);
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[h][i]));
+        amax = group_max8(amax);
         const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
         // v / sc is at most 448 in magnitude, so the hardware conversion
         // gives exactly the codes of f32_to_e4m3
-        const uint2 q = make_uint2(e4m3x4(v[h][0] / sc, v[h][1] / sc, v[h][2] / sc, v[h][3] / sc),
-                                   e4m3x4(v[h][4] / sc, v[h][5] / sc, v[h][6] / sc, v[h][7] / sc));
+        const uint4 q = make_uint4(e4m3x4(v[h][0] / sc, v[h][1] / sc, v[h][2] / sc, v[h][3] / sc),
+                                   e4m3x4(v[h][4] / sc, v[h][5] / sc, v[h][6] / sc, v[h][7] / sc),
+                                   e4m3x4(v[h][8] / sc, v[h][9] / sc, v[h][10] / sc, v[h][11] / sc),
+                                   e4m3x4(v[h][12] / sc, v[h][13] / sc, v[h][14] / sc, v[h][15] / sc));
         if (ok) {
           for (int j = 0; j < k + n_shared; ++j) {
             size_t row;
@@ -315,14 +333,15 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
             } else {
               row = shared_base + (size_t)(j - k) * T + t;
             }
-            *reinterpret_cast<uint2 *>(dst + row * d + gi * 128 + lane16 * 8) = q;
-            if (lane16 == 0) x_scale[(size_t)gi * srows + row] = sc;
+            *reinterpret_cast<uint4 *>(dst + row * d + gi * 128 + lane8 * 16) = q;
+            if (lane8 == 0) x_scale[(size_t)gi * srows + row] = sc;
           }
         }
       }
     }
   }
 }
+
 
 }  // namespace
 
