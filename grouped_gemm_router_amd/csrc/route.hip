@@ -159,6 +159,48 @@ __global__ __launch_bounds__(kThreads) void route_logits_f32(const float *__rest
   part[p] = acc;
 }
 
+// Segment all-reductions over aligned groups of W lanes (W = 2 ... 64).
+// Step s pairs every lane with one partner in the other half of its
+// 2^(s+1)-lane block: s = 0, 1 swap neighbours and pairs (DPP quad_perm),
+// s = 2, 3 mirror within 8 and 16 lanes (DPP row_half_mirror, row_mirror),
+// s = 4, 5 exchange with lane ^ 16 and lane ^ 32 (LDS permute).  Every
+// step is an exchange, so all lanes of a segment end with the same value
+// (also for sums: each pair adds the same two numbers).
+template <int S>
+__device__ __forceinline__ int seg_partner(int v) {
+  if constexpr (S == 0) return __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, false);
+  else if constexpr (S == 1) return __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, false);
+  else if constexpr (S == 2) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false);
+  else if constexpr (S == 3) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);
+  else if constexpr (S == 4) return __shfl_xor(v, 16, kWave);
+  else return __shfl_xor(v, 32, kWave);
+}
+template <int S>
+__device__ __forceinline__ float seg_partner(float v) {
+  return __builtin_bit_cast(float, seg_partner<S>(__builtin_bit_cast(int, v)));
+}
+
+template <int W, int S = 0>
+__device__ __forceinline__ float seg_max(float v) {
+  if constexpr ((2 << S) > W) return v;
+  else return seg_max<W, S + 1>(fmaxf(v, seg_partner<S>(v)));
+}
+template <int W, int S = 0>
+__device__ __forceinline__ float seg_sum(float v) {
+  if constexpr ((2 << S) > W) return v;
+  else return seg_sum<W, S + 1>(v + seg_partner<S>(v));
+}
+// argmax on the key (value descending, index ascending)
+template <int W, int S = 0>
+__device__ __forceinline__ void seg_argmax(float &bv, int &be) {
+  if constexpr ((2 << S) <= W) {
+    const float ov = seg_partner<S>(bv);
+    const int oe = seg_partner<S>(be);
+    if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    seg_argmax<W, S + 1>(bv, be);
+  }
+}
+
 // One token per segment of W lanes (W = 8 ... 64, so 64 / W tokens per
 // wave when E <= 32); a lane holds NPER = ceil(E / W) experts, e = lane + W i.
 // The S partials of a value are loaded eight slices at a time, all issued
@@ -209,14 +251,12 @@ __global__ __launch_bounds__(kThreads) void route_select(
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NPER; ++i) mx = fmaxf(mx, v[i]);
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  mx = seg_max<W>(mx);
   float z = 0.f;
 #pragma unroll
   for (int i = 0; i < NPER; ++i)
     if (ok[i]) z += expf(v[i] - mx);
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kWave);
+  z = seg_sum<W>(z);
 
   uint32_t taken = 0;
   float my_w = 0.f;
@@ -233,12 +273,7 @@ __global__ __launch_bounds__(kThreads) void route_select(
       }
     }
     // segment-wide argmax on (value desc, index asc)
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-    }
+    seg_argmax<W>(bv, be);
     if (be != 0x7fffffff && (be % W) == sl_lane) taken |= 1u << (be / W);
     if (sl_lane == j) {
       my_idx = be;
@@ -247,8 +282,7 @@ __global__ __launch_bounds__(kThreads) void route_select(
   }
   if (renorm) {
     float sw = sl_lane < k ? my_w : 0.f;
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) sw += __shfl_xor(sw, o, kWave);
+    sw = seg_sum<W>(sw);
     my_w = my_w / sw;
   }
   if (tok && sl_lane < k) {
@@ -337,23 +371,16 @@ __global__ __launch_bounds__(kThreads) void route_fused_small(
     v = -INFINITY;
   }
   float mx = v;
-#pragma unroll
-  for (int o = EP / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  mx = seg_max<EP>(mx);
   float z = ok ? expf(v - mx) : 0.f;
-#pragma unroll
-  for (int o = EP / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kWave);
+  z = seg_sum<EP>(z);
   bool taken = false;
   float my_w = 0.f;
   int my_idx = 0;
   for (int j = 0; j < k; ++j) {
     float bv = (ok && !taken) ? v : -INFINITY;
     int be = (ok && !taken) ? e : 0x7fffffff;
-#pragma unroll
-    for (int o = EP / 2; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-    }
+    seg_argmax<EP>(bv, be);
     if (be == e) taken = true;
     if (e == j) {
       my_idx = be;
@@ -362,8 +389,7 @@ __global__ __launch_bounds__(kThreads) void route_fused_small(
   }
   if (renorm) {
     float sw = e < k ? my_w : 0.f;
-#pragma unroll
-    for (int o = EP / 2; o > 0; o >>= 1) sw += __shfl_xor(sw, o, kWave);
+    sw = seg_sum<EP>(sw);
     my_w = my_w / sw;
   }
   if (t < T && e < k) {
