@@ -89,12 +89,8 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t *__restric
 // every thread gets its own prefix, and *total receives the sum.
 __device__ __forceinline__ int block_excl_scan(int v, int *s_wave, int *total) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
+  int wave_total;
+  const int incl = wave_exclusive_scan(v, &wave_total) + v;  // DPP, no LDS round trips
   if (lane == kWave - 1) s_wave[wv] = incl;
   __syncthreads();
   int base = 0, all = 0;
