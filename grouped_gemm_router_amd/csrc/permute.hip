@@ -267,16 +267,17 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
     const int lane8 = threadIdx.x & 7;
     uint8_t *dst = static_cast<uint8_t *>(x_perm);
     // every 8-lane group iterates the same number of times (the group max
-    // below needs its whole group); each iteration takes two groups (stride
-    // apart) and issues both loads before using either
+    // below needs its whole group); each iteration takes HG groups (stride
+    // apart) and issues all their loads before using any
+    constexpr int HG = 8;
     const int stride = blockDim.x >> 3;
-    const int rounds = (items + 2 * stride - 1) / (2 * stride);
+    const int rounds = (items + HG * stride - 1) / (HG * stride);
     for (int rd = 0; rd < rounds; ++rd) {
-      float v[2][16];
-      int its[2];
+      float v[HG][16];
+      int its[HG];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int it = rd * 2 * stride + h * stride + (threadIdx.x >> 3);
+      for (int h = 0; h < HG; ++h) {
+        const int it = rd * HG * stride + h * stride + (threadIdx.x >> 3);
         its[h] = it;
         if (it < items) {
           const int tt = it / gpr, gi = it - tt * gpr;
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
         }
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < HG; ++h) {
         const int it = its[h];
         const bool ok = it < items;
         const int tt = ok ? it / gpr : 0, gi = ok ? it - tt * gpr : 0;
