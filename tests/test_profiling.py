@@ -1,6 +1,8 @@
-"""CPU checks of the traffic record built from rocprofv3 counter CSVs: the
-kernel and copy dispatches are told apart by name, counters are summed over
-their instances per dispatch, and the copy calibration scales KiB to bytes."""
+"""CPU checks of the profile summaries built from rocprofv3 CSVs.  Traffic
+record: the kernel and copy dispatches are told apart by name, counters are
+summed over their instances per dispatch, and the copy calibration scales
+KiB to bytes.  Trace summary: the timed column averages each kernel's last
+dispatches in dispatch order."""
 import csv
 import json
 
