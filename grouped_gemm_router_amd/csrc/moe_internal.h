@@ -94,8 +94,9 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 // ---------------------------------------------------------------------------
 // device-side group/tile scheduler shared by the grouped GEMM kernels.
 //
-// Each group g owns rows [o_g, o_g + M_g) with o_g = clamp(offsets[g], 0,
-// rows) and M_g = max(0, clamp(offsets[g+1]) - o_g).  Group g is cut into
+// Each group g owns rows [o_g, o_g + M_g) with o_g the largest of
+// clamp(offsets[h], 0, rows) over h <= g and M_g = o_{g+1} - o_g, so the
+// groups never hold more than `rows` rows in all.  Group g is cut into
 // mt_g = ceil(M_g / BM) row tiles and nt column tiles.  Groups are taken in
 // index order, or (by_class) in three classes by size -- M_g > 128, then
 // 64 < M_g <= 128, then the rest -- each class in index order: the tallest
@@ -127,6 +128,19 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
   incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xc, 0xf, false);  // row_bcast:31
   *total = __builtin_amdgcn_readlane(incl, kWave - 1);
   return incl - v;
+}
+
+// Inclusive running maximum over the 64 lanes of a wave, for values >= 0
+// (DPP as in wave_exclusive_scan; a lane without a source takes 0, the
+// identity here).  Must be called by a whole wave.
+__device__ __forceinline__ int wave_inclusive_max(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
 }
 
 struct Tile {
@@ -173,6 +187,27 @@ __device__ __forceinline__ void sched_wave(const int32_t *__restrict__ offsets, 
   for (int i = 0; i <= RUN; ++i) o[i] = offsets[min(g0 + i, G)];
 #pragma unroll
   for (int i = 0; i <= RUN; ++i) o[i] = (i <= n) ? min(max(o[i], 0), rows) : 0;
+  // Make the clamped offsets non-decreasing (each becomes the largest
+  // offset up to its group), so the groups' rows never add up to more than
+  // `rows` and the tile count stays within host_row_tile_bound whatever the
+  // array holds: a running maximum inside the run, then the maximum of the
+  // runs of all lower lanes.
+  int run_max = o[0];
+#pragma unroll
+  for (int i = 1; i <= RUN; ++i) {
+    if (i <= n) {
+      o[i] = max(o[i], o[i - 1]);
+      run_max = o[i];
+    }
+  }
+  {
+    const int incl = wave_inclusive_max(run_max);
+    int before = __shfl_up(incl, 1, kWave);
+    if (lane == 0) before = 0;
+#pragma unroll
+    for (int i = 0; i <= RUN; ++i)
+      if (i <= n) o[i] = max(o[i], before);
+  }
   // row tiles of this lane's run, per class
   int t0 = 0, t1 = 0, t2 = 0;
 #pragma unroll
@@ -221,7 +256,8 @@ __device__ __forceinline__ void sched_wave(const int32_t *__restrict__ offsets, 
 }
 
 // The device tile scheduler.  Groups have clamped offsets o[g] =
-// min(max(offsets[g], 0), rows) and m_g = max(o[g+1] - o[g], 0) rows, cut
+// max over h <= g of min(max(offsets[h], 0), rows) (non-decreasing, at most
+// rows) and m_g = o[g+1] - o[g] rows, cut
 // into ceil(m_g / BM) row tiles of nt_count column tiles each; with
 // by_class the groups are taken class by class (sched_class), in group order
 // inside a class.  pick(total) maps the total tile count to the linear id

@@ -220,8 +220,10 @@ moe_status_t moe_router_stats(const float *logits, const int32_t *counts, int T,
  * A [rows][K], B and B2 [G][N][K] of type ab_dt (MOE_F32 or MOE_BF16),
  * accumulation in fp32, C [rows][N] of type c_dt (MOE_F32 or MOE_BF16).
  * B2 must be NULL unless epi == MOE_EPI_SWIGLU.  Rows of C outside every
- * group are not written.  offsets values are clamped to [0, rows], so a bad
- * offsets array gives wrong results but no out-of-bounds access.
+ * group are not written.  offsets values are clamped to [0, rows] and read
+ * as their running maximum (group g owns rows [o_g, o_{g+1}) with o_g the
+ * largest clamped offset up to g), so a bad offsets array gives wrong
+ * results but no out-of-bounds access, in C and in the workspace.
  * Requires K % 8 == 0, 1 <= G <= MOE_MAX_GROUPS.
  *
  * ws (device, 16-byte aligned, caller-owned scratch) lets the bf16 path cut

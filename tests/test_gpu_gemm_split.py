@@ -160,3 +160,28 @@ def test_decode_gate_up_split_sampled(orc):
     n_split, S = expected_plan(sizes, 112, 4096, cus())
     assert header(ws) == (n_split, S)
     _sampled_check(orc, A, B, B2, offs, C, True, per_group=2)
+
+
+def test_non_monotone_offsets_stay_in_bounds(orc):
+    """Offsets that go down are a caller error; the scheduler reads each
+    clamped offset as the largest one up to its group, so the groups never
+    hold more than `rows` rows and the tile count stays within the bound the
+    workspace is sized for.  Here [0, 1024, 0, 1024, 0, 1024, 0] read as
+    independent ranges would make 12 row tiles against a host bound of 10 and
+    place split partials past the workspace; read as a running maximum it is
+    group 0 with all 1024 rows and five empty groups.  A guard region after
+    the workspace must come back untouched and every row must be group 0's
+    product."""
+    a = api()
+    rows, N, K, G = 1024, 256, 8192, 6
+    offs = np.array([0, 1024, 0, 1024, 0, 1024, 0], dtype=np.int32)
+    A, B, _, _ = make([rows] + [0] * (G - 1), N, K, torch.bfloat16, 804, False)
+    need = a.moe_grouped_gemm_workspace_size(G, rows, N, K, torch.bfloat16, a.MOE_EPI_NONE)
+    guard = 1 << 20
+    buf = torch.full((need + guard,), 0xAB, dtype=torch.uint8, device=DEV)
+    C = run(A, B, None, offs, torch.bfloat16, False, buf[:need])
+    assert header(buf) == expected_plan([rows] + [0] * (G - 1), 1, K, cus())
+    assert bool((buf[need:] == 0xAB).all()), "the kernel wrote past its workspace"
+    ref, bound = ref_and_bound(orc, np_of(A), np_of(B[:1]), None,
+                               np.array([0, rows], np.int32), np.arange(rows), False, 2.0 ** -8)
+    assert_within(C.float().cpu().numpy(), ref, bound)
