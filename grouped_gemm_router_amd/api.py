@@ -19,12 +19,13 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH 
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_ROUTE_RENORM, MOE_ROUTE_FROM_LOGITS = 1, 2
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTS = ["moe_status_string", "moe_abi_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute_capped", "moe_router_stats_workspace_size",
            "moe_router_stats",
-           "moe_permute", "moe_grouped_gemm_workspace_size", "moe_grouped_gemm",
+           "moe_permute", "moe_permute_noalloc", "moe_grouped_gemm_workspace_size",
+           "moe_grouped_gemm",
            "moe_grouped_gemm_fp8", "moe_combine",
            "moe_quantize_fp8"]
 
@@ -54,6 +55,9 @@ def _load():
     lib.moe_permute.restype = i32
     lib.moe_permute.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                 vp, vp, sz, vp]
+    lib.moe_permute_noalloc.restype = i32
+    lib.moe_permute_noalloc.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, vp, vp,
+                                        vp, vp, vp, vp]
     lib.moe_permute_capped.restype = i32
     lib.moe_permute_capped.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, i32, vp, vp, vp,
                                        vp, vp, vp, vp, vp, vp, sz, vp]
@@ -167,6 +171,23 @@ def moe_permute(x, topk_idx, E, n_shared, x_perm, counts, offsets, perm_src, fla
                                           _ptr(counts), _ptr(offsets), _ptr(perm_src),
                                           _ptr(flat_to_row), _ptr(ws), ws_bytes,
                                           _stream(stream)))
+
+
+PERMUTE_NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def moe_permute_noalloc(x, topk_idx, E, n_shared, x_perm, counts, offsets, perm_src,
+                        flat_to_row, *, x_perm_scale=None, stream=None):
+    """moe_permute without a workspace: the library's static device scratch
+    (PERMUTE_NOALLOC_SCRATCH_BYTES per GPU) holds the per-block counts, so
+    the call allocates nothing.  Calls that overlap on one GPU race."""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    _check("moe_permute_noalloc",
+           lib.moe_permute_noalloc(_ptr(x), _dt(x), T, d, _ptr(topk_idx), k, E, n_shared,
+                                   _dt(x_perm), _ptr(x_perm), _ptr(x_perm_scale), _ptr(counts),
+                                   _ptr(offsets), _ptr(perm_src), _ptr(flat_to_row),
+                                   _stream(stream)))
 
 
 def moe_permute_capped(x, topk_idx, E, n_shared, capacity, x_perm, counts, offsets, perm_src,

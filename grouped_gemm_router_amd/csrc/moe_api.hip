@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -101,7 +101,8 @@ moe_status_t permute_checked(const void *x, moe_dtype_t x_dt, int T, int d,
                              moe_dtype_t out_dt, void *x_perm, float *x_perm_scale,
                              int32_t *counts, int32_t *offsets, int32_t *perm_src,
                              int32_t *flat_to_row, int32_t *overflow, int32_t *n_overflow,
-                             void *ws, size_t ws_bytes, moe_stream_t stream) {
+                             void *ws, size_t ws_bytes, bool static_scratch,
+                             moe_stream_t stream) {
   if (T < 0 || d < 8 || E < 1 || k < 1 || k > E || n_shared < 0 || capacity < 0)
     return MOE_ERR_INVALID;
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || n_shared > 8) return MOE_ERR_UNSUPPORTED;
@@ -120,8 +121,14 @@ moe_status_t permute_checked(const void *x, moe_dtype_t x_dt, int T, int d,
       !opt_aligned4(overflow) || !opt_aligned4(n_overflow))
     return MOE_ERR_INVALID;
   const size_t need = permute_ws_bytes(T, k, E);
-  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
-  if (need > 0 && !aligned4(ws)) return MOE_ERR_INVALID;
+  if (static_scratch) {  // moe_permute_noalloc: the library's static scratch
+    if (need > MOE_PERMUTE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    if (T == 0) return MOE_OK;
+    if (permute_noalloc_scratch(&ws) != hipSuccess) return MOE_ERR_LAUNCH;
+  } else {
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (need > 0 && !aligned4(ws)) return MOE_ERR_INVALID;
+  }
   if (T == 0) return MOE_OK;
   return launched(launch_permute(x, x_dt, T, d, topk_idx, k, E, n_shared, capacity, out_dt,
                                  x_perm, x_perm_scale, counts, offsets, perm_src, flat_to_row,
@@ -137,7 +144,17 @@ moe_status_t moe_permute(const void *x, moe_dtype_t x_dt, int T, int d, const in
                          moe_stream_t stream) {
   return permute_checked(x, x_dt, T, d, topk_idx, k, E, n_shared, INT32_MAX, out_dt, x_perm,
                          x_perm_scale, counts, offsets, perm_src, flat_to_row, nullptr, nullptr,
-                         ws, ws_bytes, stream);
+                         ws, ws_bytes, false, stream);
+}
+
+moe_status_t moe_permute_noalloc(const void *x, moe_dtype_t x_dt, int T, int d,
+                                 const int32_t *topk_idx, int k, int E, int n_shared,
+                                 moe_dtype_t out_dt, void *x_perm, float *x_perm_scale,
+                                 int32_t *counts, int32_t *offsets, int32_t *perm_src,
+                                 int32_t *flat_to_row, moe_stream_t stream) {
+  return permute_checked(x, x_dt, T, d, topk_idx, k, E, n_shared, INT32_MAX, out_dt, x_perm,
+                         x_perm_scale, counts, offsets, perm_src, flat_to_row, nullptr, nullptr,
+                         nullptr, 0, true, stream);
 }
 
 moe_status_t moe_permute_capped(const void *x, moe_dtype_t x_dt, int T, int d,
@@ -149,7 +166,7 @@ moe_status_t moe_permute_capped(const void *x, moe_dtype_t x_dt, int T, int d,
                                 moe_stream_t stream) {
   return permute_checked(x, x_dt, T, d, topk_idx, k, E, n_shared, capacity, out_dt, x_perm,
                          x_perm_scale, counts, offsets, perm_src, flat_to_row, overflow,
-                         n_overflow, ws, ws_bytes, stream);
+                         n_overflow, ws, ws_bytes, false, stream);
 }
 
 size_t moe_router_stats_workspace_size(int T, int E) {

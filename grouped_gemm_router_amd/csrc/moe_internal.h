@@ -319,6 +319,9 @@ hipError_t launch_route(const void *x, const void *w_router, int dt, const float
                         int32_t *topk_idx, float *topk_w, float *ws, hipStream_t s);
 
 size_t permute_ws_bytes(int T, int k, int E);
+// device address of moe_permute_noalloc's static scratch on the current
+// device (MOE_PERMUTE_NOALLOC_SCRATCH_BYTES bytes)
+hipError_t permute_noalloc_scratch(void **ptr);
 // capacity: rows kept per expert (INT_MAX: drop-less); overflow and
 // n_overflow may be null
 hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *topk_idx,

@@ -29,6 +29,8 @@
 //               (absmax over 16 lanes, s = absmax / 448, RNE) on the way.
 // Rows within an expert come out in ascending flat index t*k + j, exactly as
 // a stable sort by expert id orders them.
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace {
@@ -340,7 +342,39 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
 }
 
 
+// Library-owned scratch of moe_permute_noalloc (the per-block counts and
+// overflow starts that moe_permute keeps in its workspace), one copy per GPU
+// the library runs on, held until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): permute_noalloc_scratch looks up its device address.
+static __device__ __align__(256) unsigned char scratch[MOE_PERMUTE_NOALLOC_SCRATCH_BYTES];
+
 }  // namespace
+
+// Device address of `scratch` on the current device.  The first call on a
+// device asks the runtime (hipGetSymbolAddress, with that device current)
+// and keeps the address per device; later calls reuse it.  No allocation.
+hipError_t permute_noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    void *p = cache[dev].load(std::memory_order_acquire);
+    if (p != nullptr) {
+      *ptr = p;
+      return hipSuccess;
+    }
+  }
+  void *p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (cached) cache[dev].store(p, std::memory_order_release);
+  *ptr = p;
+  return hipSuccess;
+}
 
 size_t permute_ws_bytes(int T, int k, int E) {
   (void)k;

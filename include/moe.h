@@ -160,6 +160,32 @@ moe_status_t moe_permute(const void *x, moe_dtype_t x_dt, int T, int d,
                          int32_t *flat_to_row, void *ws, size_t ws_bytes,
                          moe_stream_t stream);
 
+/* Bytes of the static device scratch moe_permute_noalloc uses. */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/*
+ * moe_permute without a workspace argument, for callers that cannot
+ * allocate device memory at call time: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments (minus
+ * ws / ws_bytes), same results, same kernels as moe_permute.
+ * The per-block counts that moe_permute keeps in its workspace live instead
+ * in a library-owned static device array of MOE_PERMUTE_NOALLOC_SCRATCH_BYTES
+ * bytes, one per GPU, held until the process ends; this call itself calls
+ * no allocator.  Sizes whose moe_permute_workspace_size(T, k, E) exceeds that
+ * limit return MOE_ERR_WORKSPACE and launch nothing (the limit allows, e.g.,
+ * T up to 65472 at E = 256 and T up to 16320 at E = 1024).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (the kernels write every value they read, so nothing needs
+ * clearing between calls): two calls that can run at the same time on one
+ * GPU (different streams, no ordering between them) race and give wrong
+ * results.  Order them, e.g. on one stream.
+ */
+moe_status_t moe_permute_noalloc(const void *x, moe_dtype_t x_dt, int T, int d,
+                                 const int32_t *topk_idx, int k, int E, int n_shared,
+                                 moe_dtype_t out_dt, void *x_perm, float *x_perm_scale,
+                                 int32_t *counts, int32_t *offsets, int32_t *perm_src,
+                                 int32_t *flat_to_row, moe_stream_t stream);
+
 /*
  * moe_permute with a per-expert capacity ("Dense GEMM to TP MoE" §5.1: at
  * inference a capacity factor caps the tokens each expert takes and the

@@ -62,7 +62,7 @@ NUL = C.c_void_p(0)
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), "libmoe.so does not export %s" % n
 
@@ -70,7 +70,7 @@ def test_every_declared_function_is_exported(lib):
 def test_status_strings_and_version(lib):
     for s in range(5):
         assert lib.moe_status_string(s)
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 def test_route_validation(lib):
@@ -117,6 +117,26 @@ def test_permute_validation_and_workspace(lib):
     assert p(BF16, 64, 4096, 2, 8, 0, BF16, P, 1 << 20) == INVALID        # scales only for fp8
     assert p(BF16, 64, 4096, 9, 8, 0, BF16, NUL, 1 << 20) == INVALID      # k > E
     assert p(BF16, 0, 4096, 2, 8, 0, BF16, NUL, 0) == OK                  # T == 0
+
+
+def test_permute_noalloc_validation(lib):
+    """The allocation-free permute checks its arguments like moe_permute and
+    refuses sizes whose per-block counts exceed its static scratch, before
+    any launch (and before it looks up the scratch on a device)."""
+    vp, i32 = C.c_void_p, C.c_int
+    lib.moe_permute_noalloc.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp,
+                                        vp, vp, vp]
+    p = lambda T, d, k, E, odt=BF16, scale=NUL: lib.moe_permute_noalloc(  # noqa: E731
+        P, BF16, T, d, P, k, E, 0, odt, P, scale, P, P, P, P, NUL)
+    limit = 1 << 20
+    assert lib.moe_permute_workspace_size(65472, 8, 256) <= limit
+    assert lib.moe_permute_workspace_size(65536, 8, 256) > limit
+    assert p(65536, 4096, 8, 256) == WORKSPACE
+    assert p(16384, 4096, 8, 1024) == WORKSPACE
+    assert p(64, 4096, 9, 8) == INVALID                 # k > E
+    assert p(64, 4096, 2, 8, F32) == UNSUPPORTED        # dtype change
+    assert p(64, 4096, 2, 8, E4M3, NUL) == INVALID      # fp8 needs scales
+    assert p(0, 4096, 2, 8) == OK                       # T == 0: nothing launched
 
 
 def test_permute_workspace_error_is_reported(lib):
