@@ -100,16 +100,14 @@ def extras(cfg, layer, x, reps, stream):
     from grouped_gemm_router_amd import api
     T, E, k, d = cfg.T, cfg.E, cfg.k, cfg.d
     dev = x.device
-    lg = torch.empty((T, E), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    api.moe_route(x, layer.w_router, idx, w, logits=lg, logit_bias=layer.bias)
+    ps = torch.empty((api.prob_sum_blocks(T), E), dtype=torch.float32, device=dev)
+    api.moe_route(x, layer.w_router, idx, w, logit_bias=layer.bias, prob_sums=ps)
     counts = torch.empty((E,), dtype=torch.int32, device=dev)
     f = torch.empty((E,), dtype=torch.float32, device=dev)
     P = torch.empty_like(f)
     summ = torch.empty((3,), dtype=torch.float32, device=dev)
-    sws = torch.empty((max(api.moe_router_stats_workspace_size(T, E), 4),), dtype=torch.uint8,
-                      device=dev)
     out = {}
     # permutation under a capacity factor of 1.0
     cap = -(-T * k // E)
@@ -127,10 +125,10 @@ def extras(cfg, layer, x, reps, stream):
     out["permute_capped_cf1"] = {"ms": round(ms, 5), "capacity": cap,
                                  "dropped": int(nov.item()), "GB/s": round(by / ms / 1e6, 1),
                                  "hbm_frac": round(by / ms / 1e6 / HBM_PEAK_GBS, 4)}
-    # router statistics (reads the logits and the counts)
-    run = lambda: api.moe_router_stats(lg, counts, k, 0.01, f, P, summ, ws=sws)  # noqa: E731
+    # router statistics (reads the route's probability sums and the counts)
+    run = lambda: api.moe_router_stats(ps, counts, T, k, 0.01, f, P, summ)  # noqa: E731
     ms = timed(run, reps, stream)
-    by = T * E * 4 + E * 4 * 3 + 12
+    by = ps.numel() * 4 + E * 4 * 3 + 12
     s = summ.cpu().tolist()
     out["router_stats"] = {"ms": round(ms, 5), "GB/s": round(by / ms / 1e6, 1),
                            "hbm_frac": round(by / ms / 1e6 / HBM_PEAK_GBS, 4),

@@ -19,11 +19,10 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH 
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_ROUTE_RENORM, MOE_ROUTE_FROM_LOGITS = 1, 2
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 EXPORTS = ["moe_status_string", "moe_abi_version", "moe_route_workspace_size", "moe_route",
-           "moe_permute_workspace_size", "moe_permute_capped", "moe_router_stats_workspace_size",
-           "moe_router_stats",
+           "moe_permute_workspace_size", "moe_permute_capped", "moe_router_stats",
            "moe_permute", "moe_permute_noalloc", "moe_grouped_gemm_workspace_size",
            "moe_grouped_gemm",
            "moe_grouped_gemm_fp8", "moe_combine",
@@ -49,7 +48,8 @@ def _load():
     lib.moe_route.restype = i32
     lib.moe_route_workspace_size.restype = sz
     lib.moe_route_workspace_size.argtypes = [i32, i32, i32]
-    lib.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp, sz, vp]
+    lib.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp, vp, sz,
+                              vp]
     lib.moe_permute_workspace_size.restype = sz
     lib.moe_permute_workspace_size.argtypes = [i32, i32, i32]
     lib.moe_permute.restype = i32
@@ -61,10 +61,8 @@ def _load():
     lib.moe_permute_capped.restype = i32
     lib.moe_permute_capped.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, i32, vp, vp, vp,
                                        vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.moe_router_stats_workspace_size.restype = sz
-    lib.moe_router_stats_workspace_size.argtypes = [i32, i32]
     lib.moe_router_stats.restype = i32
-    lib.moe_router_stats.argtypes = [vp, vp, i32, i32, i32, C.c_float, vp, vp, vp, vp, sz, vp]
+    lib.moe_router_stats.argtypes = [vp, vp, i32, i32, i32, C.c_float, vp, vp, vp, vp]
     lib.moe_grouped_gemm_workspace_size.restype = sz
     lib.moe_grouped_gemm_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.moe_grouped_gemm.restype = i32
@@ -129,13 +127,22 @@ def moe_route_workspace_size(T: int, d: int, E: int) -> int:
     return int(lib.moe_route_workspace_size(T, d, E))
 
 
-def moe_route(x, w_router, topk_idx, topk_w, *, logits=None, logit_bias=None, flags=0, ws=None,
-              stream=None):
+PROB_SUM_BLOCK = 16  # tokens per block of moe_route's probability sums
+
+
+def prob_sum_blocks(T: int) -> int:
+    return (T + PROB_SUM_BLOCK - 1) // PROB_SUM_BLOCK
+
+
+def moe_route(x, w_router, topk_idx, topk_w, *, logits=None, logit_bias=None, flags=0,
+              prob_sums=None, ws=None, stream=None):
     """Router scoring + top-k.  x [T][d], w_router [E][d] (fp32 or bf16);
     topk_idx [T][k] int32 and topk_w [T][k] fp32 are written; logits [T][E]
-    fp32 is written if given (read instead with MOE_ROUTE_FROM_LOGITS).
-    ws: device workspace of moe_route_workspace_size(T, d, E) bytes; when
-    None, one is allocated here for this call."""
+    fp32 is written if given (read instead with MOE_ROUTE_FROM_LOGITS);
+    prob_sums [ceil(T/16)][E] fp32, if given, receives per-block sums of the
+    softmax probabilities (for moe_router_stats).  ws: device workspace of
+    moe_route_workspace_size(T, d, E) bytes; when None, one is allocated here
+    for this call."""
     T, k = topk_idx.shape
     if flags & MOE_ROUTE_FROM_LOGITS:
         E = logits.shape[1]
@@ -146,12 +153,14 @@ def moe_route(x, w_router, topk_idx, topk_w, *, logits=None, logit_bias=None, fl
         E = w_router.shape[0]
         dt = _dt(x)
         if ws is None:
-            ws = torch.empty(moe_route_workspace_size(T, d, E), dtype=torch.uint8,
+            ws = torch.empty(max(moe_route_workspace_size(T, d, E), 4), dtype=torch.uint8,
                              device=topk_idx.device)
         ws_bytes = ws.numel() * ws.element_size()
+    if prob_sums is not None and tuple(prob_sums.shape) != (prob_sum_blocks(T), E):
+        raise ValueError("prob_sums must be [ceil(T/16)][E] = [%d][%d]" % (prob_sum_blocks(T), E))
     _check("moe_route", lib.moe_route(_ptr(x), _ptr(w_router), dt, _ptr(logit_bias), T, d, E,
                                       k, flags, _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
-                                      _ptr(ws), ws_bytes, _stream(stream)))
+                                      _ptr(prob_sums), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_permute_workspace_size(T: int, k: int, E: int) -> int:
@@ -207,22 +216,16 @@ def moe_permute_capped(x, topk_idx, E, n_shared, capacity, x_perm, counts, offse
                                   _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def moe_router_stats_workspace_size(T: int, E: int) -> int:
-    return int(lib.moe_router_stats_workspace_size(T, E))
-
-
-def moe_router_stats(logits, counts, k, alpha, f, P, summary, *, ws=None, stream=None):
-    """Load-balance statistics: f [E], P [E], summary [3] = (aux loss,
-    max/mean count, entropy in bits).  ws: moe_router_stats_workspace_size
-    bytes; when None, one is allocated here for this call."""
-    T, E = logits.shape
-    if ws is None:
-        ws = torch.empty(max(moe_router_stats_workspace_size(T, E), 4), dtype=torch.uint8,
-                         device=logits.device)
-    ws_bytes = ws.numel() * ws.element_size()
+def moe_router_stats(prob_sums, counts, T, k, alpha, f, P, summary, *, stream=None):
+    """Load-balance statistics from moe_route's probability sums
+    [ceil(T/16)][E] and moe_permute's counts [E]: f [E], P [E], summary [3] =
+    (aux loss, max/mean count, entropy in bits)."""
+    E = prob_sums.shape[1]
+    if prob_sums.shape[0] != prob_sum_blocks(T):
+        raise ValueError("prob_sums must have ceil(T/16) = %d rows" % prob_sum_blocks(T))
     _check("moe_router_stats",
-           lib.moe_router_stats(_ptr(logits), _ptr(counts), T, E, k, float(alpha), _ptr(f),
-                                _ptr(P), _ptr(summary), _ptr(ws), ws_bytes, _stream(stream)))
+           lib.moe_router_stats(_ptr(prob_sums), _ptr(counts), T, E, k, float(alpha), _ptr(f),
+                                _ptr(P), _ptr(summary), _stream(stream)))
 
 
 def moe_grouped_gemm_workspace_size(G: int, rows: int, N: int, K: int, dtype, epi: int) -> int:

@@ -74,27 +74,6 @@ __device__ __forceinline__ int b_row(int wn, int nb) {
   return wn * (BN / NWN) + nb * 32;
 }
 
-// s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 layout:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-  __builtin_amdgcn_s_waitcnt(imm);
-}
-
-// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's LDS reads are complete too
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-  constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
-  __builtin_amdgcn_s_waitcnt(imm);
-}
-
-// workgroup barrier without the release fence of __syncthreads(); callers
-// have already waited (vmcnt) for the loads the next stage reads
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-typedef __attribute__((address_space(3))) void lds_void;
-
 // LDS-direct load: lane i's SZ bytes from g land at l + i * SZ
 template <int SZ>
 __device__ __forceinline__ void dma_to_lds(const uint16_t *g, u32x4 *l) {

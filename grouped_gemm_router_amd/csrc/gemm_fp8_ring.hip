@@ -83,19 +83,6 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
-// s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-  __builtin_amdgcn_s_waitcnt(imm);
-}
-
-// workgroup barrier without __syncthreads()'s release fence, which would
-// drain every LDS-direct load still in flight
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-typedef __attribute__((address_space(3))) void lds_void;
-
 template <int SZ>
 __device__ __forceinline__ void dma_to_lds(const void *g, void *l) {
   if constexpr (SZ == 16)

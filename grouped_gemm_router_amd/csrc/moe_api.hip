@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 
 bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -66,12 +66,13 @@ size_t moe_route_workspace_size(int T, int d, int E) {
 
 moe_status_t moe_route(const void *x, const void *w_router, moe_dtype_t dt,
                        const float *logit_bias, int T, int d, int E, int k, unsigned flags,
-                       float *logits, int32_t *topk_idx, float *topk_w, void *ws,
-                       size_t ws_bytes, moe_stream_t stream) {
+                       float *logits, int32_t *topk_idx, float *topk_w, float *prob_sums,
+                       void *ws, size_t ws_bytes, moe_stream_t stream) {
   if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (flags & ~(MOE_ROUTE_RENORM | MOE_ROUTE_FROM_LOGITS)) return MOE_ERR_INVALID;
-  if (!aligned4(topk_idx) || !aligned4(topk_w)) return MOE_ERR_INVALID;
+  if (!aligned4(topk_idx) || !aligned4(topk_w) || !opt_aligned4(prob_sums))
+    return MOE_ERR_INVALID;
   const bool from_logits = (flags & MOE_ROUTE_FROM_LOGITS) != 0;
   if (from_logits) {
     if (!aligned4(logits)) return MOE_ERR_INVALID;
@@ -86,7 +87,7 @@ moe_status_t moe_route(const void *x, const void *w_router, moe_dtype_t dt,
   }
   if (T == 0) return MOE_OK;
   return launched(launch_route(x, w_router, dt, logit_bias, T, d, E, k, flags, logits, topk_idx,
-                               topk_w, static_cast<float *>(ws), as_stream(stream)));
+                               topk_w, prob_sums, static_cast<float *>(ws), as_stream(stream)));
 }
 
 size_t moe_permute_workspace_size(int T, int k, int E) {
@@ -169,25 +170,17 @@ moe_status_t moe_permute_capped(const void *x, moe_dtype_t x_dt, int T, int d,
                          n_overflow, ws, ws_bytes, false, stream);
 }
 
-size_t moe_router_stats_workspace_size(int T, int E) {
-  if (T < 0 || E < 1) return 0;
-  return router_stats_ws_bytes(T, E);
-}
-
-moe_status_t moe_router_stats(const float *logits, const int32_t *counts, int T, int E, int k,
-                              float alpha, float *f, float *P, float *summary, void *ws,
-                              size_t ws_bytes, moe_stream_t stream) {
+moe_status_t moe_router_stats(const float *prob_sums, const int32_t *counts, int T, int E, int k,
+                              float alpha, float *f, float *P, float *summary,
+                              moe_stream_t stream) {
   if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID;
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
-  if (!aligned4(logits) || !aligned4(counts) || !aligned4(f) || !aligned4(P) ||
+  if (!aligned4(prob_sums) || !aligned4(counts) || !aligned4(f) || !aligned4(P) ||
       !aligned4(summary))
     return MOE_ERR_INVALID;
-  const size_t need = router_stats_ws_bytes(T, E);
-  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
-  if (need > 0 && !aligned4(ws)) return MOE_ERR_INVALID;
   if (T == 0) return MOE_OK;
-  return launched(launch_router_stats(logits, counts, T, E, k, alpha, f, P, summary,
-                                      static_cast<float *>(ws), as_stream(stream)));
+  return launched(launch_router_stats(prob_sums, counts, T, E, k, alpha, f, P, summary,
+                                      as_stream(stream)));
 }
 
 size_t moe_grouped_gemm_workspace_size(int G, int rows, int N, int K, moe_dtype_t ab_dt,

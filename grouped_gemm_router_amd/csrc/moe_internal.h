@@ -92,6 +92,32 @@ __device__ __forceinline__ float group_max(float v, int width) {
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // ---------------------------------------------------------------------------
+// waits and barriers of the LDS-direct pipelines
+// ---------------------------------------------------------------------------
+
+// s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 layout:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's LDS reads are complete too
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// workgroup barrier without the release fence of __syncthreads(), which
+// would drain every LDS-direct load still in flight; callers have already
+// waited (vmcnt) for the loads the next stage reads
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---------------------------------------------------------------------------
 // device-side group/tile scheduler shared by the grouped GEMM kernels.
 //
 // Each group g owns rows [o_g, o_g + M_g) with o_g the largest of
@@ -310,13 +336,13 @@ inline int host_row_tile_bound(int rows, int G, int BM) { return rows / BM + G; 
 
 size_t route_ws_bytes(int T, int d, int E);
 
-size_t router_stats_ws_bytes(int T, int E);
-hipError_t launch_router_stats(const float *logits, const int32_t *counts, int T, int E, int k,
-                               float alpha, float *f, float *P, float *summary, float *ws,
-                               hipStream_t s);
+hipError_t launch_router_stats(const float *prob_sums, const int32_t *counts, int T, int E, int k,
+                               float alpha, float *f, float *P, float *summary, hipStream_t s);
+// prob_sums: [ceil(T/16)][E] per-block sums of the softmax probabilities, or null
 hipError_t launch_route(const void *x, const void *w_router, int dt, const float *bias,
                         int T, int d, int E, int k, unsigned flags, float *logits,
-                        int32_t *topk_idx, float *topk_w, float *ws, hipStream_t s);
+                        int32_t *topk_idx, float *topk_w, float *prob_sums, float *ws,
+                        hipStream_t s);
 
 size_t permute_ws_bytes(int T, int k, int E);
 // device address of moe_permute_noalloc's static scratch on the current

@@ -1,29 +1,27 @@
-// route.hip -- router scoring, softmax and top-k selection in one launch.
+// route.hip -- router scoring, softmax and top-k selection.
 //
 // "DeepGEMM walkthrough" §2.1: p = Softmax(W_r x); keep the k highest
 // scoring experts; the same p weights the combine.  "Dense GEMM to TP MoE"
 // §4.2: the router is a linear layer with weight [num_experts][hidden_dim].
+// "MoE in practice" §3.2 fuses the logits with the softmax and moves top-k to
+// the GPU.
 //
-// E <= 32 with bf16 inputs: one launch (route_fused_small below; the
-// logits are a few dot products per token, so the partial-logit round trip
-// would dominate).  Otherwise two launches:
+// E <= 32: one launch (route_small_bf16 / route_small_f32), scoring,
+// softmax and top-k of 16 tokens per workgroup, no workspace.
+// E > 32: two launches,
 //   logits   a split-K GEMM x [T][d] . w_router[E][d]^T on the matrix cores
-//            (v_mfma_f32_32x32x16_bf16): a workgroup (4 waves) owns 128
-//            tokens x EB experts (EB = 32, 64 or 128) over one slice of the
-//            d axis and writes fp32 partial logits part[s][t][e] to the
-//            workspace.  Tiles are staged through LDS 64 columns at a time,
-//            double buffered through registers; tokens, experts and columns
-//            past the end read as zero.  Split-K gives enough workgroups to
-//            fill the chip when T/128 x E/EB alone would not, and 128 x 128
-//            tiles keep the re-reads of x and w_router from L2 low.  fp32
-//            inputs (small configurations) take a plain per-thread dot
-//            product with one slice.
-//   select   one token per segment of lanes (the next power of two >= E,
-//            at most a wave): sum of the partials in slice order
-//            (deterministic; eight slices' loads in flight at once) plus the
-//            bias, export of the logits, segment max, sum of exp, then k
-//            rounds of a segment-wide argmax with the key (logit descending,
-//            index ascending).
+//            writing fp32 partial logits part[s][t][e] to the workspace
+//            (route_logits_split: 128 tokens x 256 experts per workgroup
+//            over one slice of the d axis, operands staged through a
+//            three-slot LDS ring by LDS-direct loads; d % 64 != 0 and fp32
+//            inputs take the register-staged route_logits_bf16 and the
+//            per-thread route_logits_f32);
+//   select   a wave per token (route_select_wave): the slices added in
+//            slice order (deterministic), + bias, export, softmax, k rounds
+//            of a wave-wide argmax on (logit descending, index ascending).
+// Every path can also write, per block of 16 consecutive tokens, the sum of
+// the softmax probabilities of each expert (prob_sums [ceil(T/16)][E]): the
+// router statistics take their mean gate probabilities from it.
 #include "moe_internal.h"
 
 namespace {
@@ -31,10 +29,11 @@ namespace {
 using namespace moe;
 
 constexpr int kThreads = 256;  // 4 waves
-constexpr int RT = 128;        // tokens per logits tile
+constexpr int RT = 128;        // tokens per logits tile (register-staged kernel)
 constexpr int RK = 64;         // columns per K step
 constexpr int RP = RK / 8;     // 16-byte pieces per tile row
 constexpr int kTargetWG = 512; // two workgroups per CU
+constexpr int kSumBlock = 16;  // tokens per probability-sum block (and per one-launch workgroup)
 
 // piece p of row r is stored at slot p ^ (r & 7): eight consecutive rows of
 // one piece (one fragment read phase) land in eight distinct bank groups
@@ -42,9 +41,9 @@ __device__ __forceinline__ int rswz(int r, int p) { return p ^ (r & 7); }
 
 __host__ __device__ inline int route_eb(int E) { return E <= 32 ? 32 : (E <= 64 ? 64 : 128); }
 
-// number of d-slices: grow while the grid is below two workgroups per CU and
-// slices keep at least four K steps on average; then drop the slices that
-// equal steps per slice leave empty
+// number of d-slices of the register-staged kernel: grow while the grid is
+// below two workgroups per CU and slices keep at least four K steps on
+// average; then drop the slices that equal steps per slice leave empty
 inline int route_splits(int T, int d, int E) {
   const long long tiles = (long long)((T + RT - 1) / RT) * ((E + route_eb(E) - 1) / route_eb(E));
   const int kt = (d + RK - 1) / RK;
@@ -201,186 +200,166 @@ __device__ __forceinline__ void seg_argmax(float &bv, int &be) {
   }
 }
 
-// One token per segment of W lanes (W = 8 ... 64, so 64 / W tokens per
-// wave when E <= 32); a lane holds NPER = ceil(E / W) experts, e = lane + W i.
-// The S partials of a value are loaded eight slices at a time, all issued
-// before the first is used, and added in slice order.  Segment-wide max,
-// sum of exp and k rounds of argmax use xor shuffles inside the segment.
-template <int W, int NPER>
-__global__ __launch_bounds__(kThreads) void route_select(
-    const float *__restrict__ part, int S, const float *__restrict__ bias, int T, int E, int k,
-    int renorm, float *__restrict__ logits_out, int32_t *__restrict__ topk_idx,
-    float *__restrict__ topk_w) {
-  constexpr int TPW = kWave / W;  // tokens per wave
-  const int lane = lane_id(), wv = threadIdx.x / kWave, sl_lane = lane % W;
-  const int t = (blockIdx.x * (kThreads / kWave) + wv) * TPW + lane / W;
-  const bool tok = t < T;  // no early return: the shuffles need every lane
-  bool ok[NPER];
-  size_t base[NPER];
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int e = sl_lane + i * W;
-    ok[i] = tok && e < E;
-    base[i] = (size_t)(tok ? t : 0) * E + (e < E ? e : 0);
-  }
-  float v[NPER];
-  constexpr int CH = 8;  // slices loaded per round
-  for (int s0 = 0; s0 < S; s0 += CH) {
-    float q[CH][NPER];
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-#pragma unroll
-      for (int i = 0; i < NPER; ++i)
-        q[j][i] = (s0 + j < S && ok[i]) ? part[(size_t)(s0 + j) * T * E + base[i]] : 0.f;
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-#pragma unroll
-      for (int i = 0; i < NPER; ++i)
-        if (s0 + j < S) v[i] = (s0 + j == 0) ? q[j][i] : v[i] + q[j][i];
-  }
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int e = sl_lane + i * W;
-    if (ok[i]) {
-      if (bias) v[i] += bias[e];
-      if (logits_out) logits_out[base[i]] = v[i];
-    } else {
-      v[i] = -INFINITY;
-    }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) mx = fmaxf(mx, v[i]);
-  mx = seg_max<W>(mx);
-  float z = 0.f;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i)
-    if (ok[i]) z += expf(v[i] - mx);
-  z = seg_sum<W>(z);
 
-  uint32_t taken = 0;
-  float my_w = 0.f;
-  int my_idx = 0;
-  for (int j = 0; j < k; ++j) {
-    // best untaken candidate held by this lane
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const int e = sl_lane + i * W;
-      if (ok[i] && !((taken >> i) & 1u)) {
-        if (v[i] > bv || (v[i] == bv && e < be)) { bv = v[i]; be = e; }
-      }
-    }
-    // segment-wide argmax on (value desc, index asc)
-    seg_argmax<W>(bv, be);
-    if (be != 0x7fffffff && (be % W) == sl_lane) taken |= 1u << (be / W);
-    if (sl_lane == j) {
-      my_idx = be;
-      my_w = expf(bv - mx) / z;
-    }
-  }
-  if (renorm) {
-    float sw = sl_lane < k ? my_w : 0.f;
-    sw = seg_sum<W>(sw);
-    my_w = my_w / sw;
-  }
-  if (tok && sl_lane < k) {
-    topk_idx[(size_t)t * k + sl_lane] = my_idx;
-    topk_w[(size_t)t * k + sl_lane] = my_w;
-  }
+// ---------------------------------------------------------------------------
+// E > 32, bf16, d % 64 == 0: split-K logits on the matrix cores.
+//
+// A workgroup (8 waves, one per CU: the ring takes 144 KB of LDS) owns 128
+// tokens x 256 experts over one slice of the d axis.  Stages of 64 columns
+// (128-byte row pieces, whole cache lines) move HBM/L2 -> LDS with
+// global_load_lds_dwordx4 through a ring of three slots (stage s + 2 is
+// issued while stage s is multiplied), each wave waits only for its own
+// loads and the waves meet at a plain s_barrier.  Piece p of row r sits at
+// slot p ^ ((r >> 1) & 7), so the fragment reads (32 rows x one piece) hit
+// distinct banks.  Waves form a 2 x 4 grid of 64 x 64 outputs
+// (v_mfma_f32_32x32x16_bf16, 2 x 2 blocks).  Rows past T and experts past E
+// are loaded clamped and never stored.  The slice's fp32 partial logits go
+// to part[slice][t][e].  Against the register-staged 128 x 128 kernel this
+// reads x and w_router from L2 once per 256 experts and 128 tokens and keeps
+// two stages in flight.
+constexpr int LT = 128, LE = 256, LK = 64;
+constexpr int LNW = 8, LTH = LNW * kWave;
+constexpr int LWT = LT / 64, LWE = LE / 64;        // wave grid (tokens x experts), 64 x 64 each
+constexpr int LSA = LT * 8, LSB = LE * 8;          // 16-byte slots of an A / B stage
+constexpr int LIA = LSA / LTH, LIB = LSB / LTH;    // LDS-direct loads per thread and stage
+constexpr int kSplitTargetWG = 256;                // one workgroup per CU
+static_assert(LWT * LWE == LNW, "the waves must tile the workgroup's outputs");
+
+__device__ __forceinline__ int lswz(int row, int p) { return p ^ ((row >> 1) & 7); }
+
+// slices of the split kernel: double while the grid stays within one
+// workgroup per CU and slices keep at least four stages
+inline int route_split_slices(int T, int d, int E) {
+  const long long tiles = (long long)((T + LT - 1) / LT) * ((E + LE - 1) / LE);
+  const int nst = d / LK;
+  int S = 1;
+  while (tiles * S * 2 <= kSplitTargetWG && nst / (S * 2) >= 4) S *= 2;
+  const int sps = (nst + S - 1) / S;
+  return (nst + sps - 1) / sps;
 }
 
-// Small E (<= 32, bf16): scoring, softmax and top-k in one launch, no
-// workspace.  A workgroup takes TPW = 64 / EP tokens (EP = E rounded up to
-// 8, 16 or 32) and its four waves split the d axis; a lane accumulates the
-// bf16 dot products (v_dot2c_f32_bf16) of every (token, expert) pair over
-// its 16-byte column chunks, with the token and weight chunks of a step all
-// loaded before use.  A butterfly reduce-scatter over the wave (each value
-// added in exactly one lane, fixed pairing) leaves lane l with value l =
-// token l / EP, expert l % EP; the four waves' values are added in wave
-// order through LDS, and wave 0 finishes like the select kernel with one
-// token per EP-lane segment.  Measured on the Mixtral shapes: 13.9 us;
-// eight waves 17.6 us (each wave pays the reduce-scatter); two chunks per
-// step 15.1 us (201 registers, lower occupancy).
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-template <int EP>
-__global__ __launch_bounds__(kThreads) void route_fused_small(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
-    const float *__restrict__ bias, int T, int d, int E, int k, int renorm,
-    float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w) {
-  constexpr int TPW = kWave / EP;  // tokens per workgroup
-  __shared__ float s_red[kThreads / kWave][kWave];
+__global__ __launch_bounds__(LTH, 1) void route_logits_split(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, int T, int d, int E, int sps,
+    float *__restrict__ part) {
+  __shared__ u32x4 sA0[LSA], sA1[LSA], sA2[LSA];
+  __shared__ u32x4 sB0[LSB], sB1[LSB], sB2[LSB];
+  const int t0 = blockIdx.x * LT, e0 = blockIdx.y * LE, sl = blockIdx.z;
+  const int kb = sl * sps;
+  const int ns = min(d / LK, kb + sps) - kb;  // stages of this slice (>= 1)
   const int lane = lane_id(), wv = threadIdx.x / kWave;
-  const int t0 = blockIdx.x * TPW;
-  const int nch = d / 8;  // 16-byte chunks per row
-  const int c_lo = wv * nch / 4, c_hi = (wv + 1) * nch / 4;
-  float a[kWave];  // [t][e] partial dot products
+  const int wm = wv / LWE, wn = wv % LWE;
+  // LDS-direct sources: wave wv fills slots [wv * S / LNW, +S / LNW) of each
+  // stage, 64 per instruction; slot q holds piece lswz(q / 8, q % 8) of row q / 8
+  const uint16_t *ga[LIA];
+  const uint16_t *gb[LIB];
 #pragma unroll
-  for (int i = 0; i < kWave; ++i) a[i] = 0.f;
-  for (int c = c_lo + lane; c < c_hi; c += kWave) {
-    // the 16-byte chunks go through plain arrays of dwords: bit-casting a
-    // subscripted vector element (v[j]) to bf16x2 compiles to element 0
-    // for every j with this toolchain
-    unsigned xs[TPW][4], ws[EP][4];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const u32x4 v = t0 + t < T ? *reinterpret_cast<const u32x4 *>(x + (size_t)(t0 + t) * d + c * 8)
-                                 : u32x4{0u, 0u, 0u, 0u};
-      xs[t][0] = v.x; xs[t][1] = v.y; xs[t][2] = v.z; xs[t][3] = v.w;
-    }
-#pragma unroll
-    for (int e = 0; e < EP; ++e) {
-      const u32x4 v = e < E ? *reinterpret_cast<const u32x4 *>(wr + (size_t)e * d + c * 8)
-                            : u32x4{0u, 0u, 0u, 0u};
-      ws[e][0] = v.x; ws[e][1] = v.y; ws[e][2] = v.z; ws[e][3] = v.w;
-    }
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int e = 0; e < EP; ++e)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          a[t * EP + e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xs[t][j]),
-                                                          __builtin_bit_cast(bf16x2, ws[e][j]),
-                                                          a[t * EP + e], false);
+  for (int i = 0; i < LIA; ++i) {
+    const int q = wv * (LSA / LNW) + i * kWave + lane, r = q / 8;
+    ga[i] = x + (size_t)min(t0 + r, T - 1) * d + (size_t)kb * LK + lswz(r, q % 8) * 8;
   }
-  // reduce-scatter: at offset o a lane keeps the half of its values whose
-  // index has bit o equal to its own and adds the partner's copy of them
 #pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const bool hi = (lane & o) != 0;
+  for (int i = 0; i < LIB; ++i) {
+    const int q = wv * (LSB / LNW) + i * kWave + lane, r = q / 8;
+    gb[i] = wr + (size_t)min(e0 + r, E - 1) * d + (size_t)kb * LK + lswz(r, q % 8) * 8;
+  }
+  const int da = wv * (LSA / LNW), db = wv * (LSB / LNW);
+  f32x16 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < o; ++i) {
-      const float send = hi ? a[i] : a[o + i];
-      const float keep = hi ? a[o + i] : a[i];
-      a[i] = keep + __shfl_xor(send, o, kWave);
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  const int fr = lane & 31, fh = lane >> 5;
+
+#define MOE_RISSUE(SA, SB, ST)                                                                 \
+  _Pragma("unroll") for (int i = 0; i < LIA; ++i)                                             \
+    __builtin_amdgcn_global_load_lds((const void *)(ga[i] + (size_t)(ST) * LK),               \
+                                     (lds_void *)((SA) + da + i * kWave), 16, 0, 0);          \
+  _Pragma("unroll") for (int i = 0; i < LIB; ++i)                                             \
+    __builtin_amdgcn_global_load_lds((const void *)(gb[i] + (size_t)(ST) * LK),               \
+                                     (lds_void *)((SB) + db + i * kWave), 16, 0, 0);
+#define MOE_RCOMPUTE(SA, SB)                                                                   \
+  _Pragma("unroll") for (int ks = 0; ks < LK / 16; ++ks) {                                    \
+    const int pc = ks * 2 + fh;                                                               \
+    bf16x8 a[2], b[2];                                                                        \
+    _Pragma("unroll") for (int mi = 0; mi < 2; ++mi) {                                        \
+      const int r = wm * 64 + mi * 32 + fr;                                                   \
+      a[mi] = __builtin_bit_cast(bf16x8, (SA)[r * 8 + lswz(r, pc)]);                          \
+    }                                                                                         \
+    _Pragma("unroll") for (int nb = 0; nb < 2; ++nb) {                                        \
+      const int r = wn * 64 + nb * 32 + fr;                                                   \
+      b[nb] = __builtin_bit_cast(bf16x8, (SB)[r * 8 + lswz(r, pc)]);                          \
+    }                                                                                         \
+    _Pragma("unroll") for (int mi = 0; mi < 2; ++mi)                                          \
+      _Pragma("unroll") for (int nb = 0; nb < 2; ++nb)                                        \
+        acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[nb], acc[mi][nb], 0, 0, 0); \
+  }
+// stage s in slot s % 3: wait for this wave's loads of stage s (those of
+// stage s + 1 may stay in flight), meet (every wave is then past stage s - 1,
+// whose slot is free), refill that slot with stage s + 2 (past the end the
+// last stage again, into a slot nobody reads, so the counts never change),
+// multiply
+#define MOE_RSTAGE(CA, CB, NA, NB, S)                                                          \
+  wait_vmcnt<LIA + LIB>();                                                                    \
+  stage_barrier();                                                                            \
+  MOE_RISSUE(NA, NB, min((S) + 2, ns - 1))                                                    \
+  MOE_RCOMPUTE(CA, CB)
+
+  MOE_RISSUE(sA0, sB0, 0)
+  MOE_RISSUE(sA1, sB1, min(1, ns - 1))
+  int s = 0;
+  for (; s + 3 <= ns; s += 3) {
+    MOE_RSTAGE(sA0, sB0, sA2, sB2, s)
+    MOE_RSTAGE(sA1, sB1, sA0, sB0, s + 1)
+    MOE_RSTAGE(sA2, sB2, sA1, sB1, s + 2)
+  }
+  if (s < ns) {
+    MOE_RSTAGE(sA0, sB0, sA2, sB2, s)
+  }
+  if (s + 1 < ns) {
+    MOE_RSTAGE(sA1, sB1, sA0, sB0, s + 1)
+  }
+  wait_vmcnt<0>();  // no LDS-direct load may still be landing when the workgroup ends
+#undef MOE_RSTAGE
+#undef MOE_RCOMPUTE
+#undef MOE_RISSUE
+
+  // 32x32 accumulator layout: lane holds column (expert) lane % 32, register
+  // r holds row (token) 8 (r / 4) + 4 (lane / 32) + r % 4
+  float *out = part + (size_t)sl * T * E;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int e = e0 + wn * 64 + nb * 32 + fr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
+        if (t < T && e < E) out[(size_t)t * E + e] = acc[mi][nb][r];
+      }
     }
-  }
-  s_red[wv][lane] = a[0];
-  __syncthreads();
-  if (wv != 0) return;
-  float v = ((s_red[0][lane] + s_red[1][lane]) + s_red[2][lane]) + s_red[3][lane];
-  const int e = lane % EP, t = t0 + lane / EP;
-  const bool ok = t < T && e < E;
-  if (ok) {
-    if (bias) v += bias[e];
-    if (logits_out) logits_out[(size_t)t * E + e] = v;
-  } else {
-    v = -INFINITY;
-  }
-  float mx = v;
-  mx = seg_max<EP>(mx);
-  float z = ok ? expf(v - mx) : 0.f;
-  z = seg_sum<EP>(z);
+}
+
+
+// Softmax and top-k of one token held by a segment of W lanes, segment
+// lane e holding the logit v of expert e (ok: a real expert of a real
+// token).  Max-subtracted softmax over the segment, then k rounds of argmax
+// on (logit descending, index ascending); segment lane j < k keeps the j-th
+// choice in *idx / *w (renormalised over the k choices with renorm).
+// Returns the lane's own softmax probability (0 when !ok).
+template <int W>
+__device__ __forceinline__ float select_segment(float v, bool ok, int e, int k, int renorm,
+                                                int *idx, float *w) {
+  v = ok ? v : -INFINITY;
+  const float mx = seg_max<W>(v);
+  const float ex = ok ? expf(v - mx) : 0.f;
+  const float z = seg_sum<W>(ex);
   bool taken = false;
   float my_w = 0.f;
   int my_idx = 0;
   for (int j = 0; j < k; ++j) {
     float bv = (ok && !taken) ? v : -INFINITY;
     int be = (ok && !taken) ? e : 0x7fffffff;
-    seg_argmax<EP>(bv, be);
+    seg_argmax<W>(bv, be);
     if (be == e) taken = true;
     if (e == j) {
       my_idx = be;
@@ -389,89 +368,399 @@ __global__ __launch_bounds__(kThreads) void route_fused_small(
   }
   if (renorm) {
     float sw = e < k ? my_w : 0.f;
-    sw = seg_sum<EP>(sw);
+    sw = seg_sum<W>(sw);
     my_w = my_w / sw;
   }
+  *idx = my_idx;
+  *w = my_w;
+  return ok ? ex / z : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// E <= 32, bf16: one launch.  A workgroup (8 waves) owns 16 tokens.  The
+// logits are a 16 x EC matrix product on the matrix cores
+// (v_mfma_f32_16x16x32_bf16, tokens as rows, NB blocks of 16 experts as
+// columns, EC = 16 NB): the waves split the d axis in 32-column steps (wave
+// w takes steps w, w + 8, ...) and load both operands straight into
+// registers (lane l: row l % 16, columns 8 (l / 16) .. + 8 of the step, 16
+// bytes), eight steps' loads issued before their MFMAs, with clamped
+// addresses (so none waits on a condition) and masked values; the matrix
+// cores do the reduction over d that a lane-parallel dot product would need
+// shuffles for.  The eight waves' partial products are added in wave order
+// through LDS; then one token per ES-lane segment (ES = E rounded up to 8,
+// 16 or 32) takes the softmax and top-k, and the probability sums of the
+// 16 tokens are written per expert.  Measured on the Mixtral shapes against
+// the previous one-launch kernel (bf16 dot products per lane and a 63-step
+// butterfly reduce-scatter per wave, 8 tokens per workgroup):
+// see the design notes.
+template <int NB, int ES>
+__global__ __launch_bounds__(512) void route_small_bf16(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+    const float *__restrict__ bias, int T, int d, int E, int k, int renorm,
+    float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    float *__restrict__ prob_sums) {
+  constexpr int NW = 8, EC = NB * 16, U = 8;
+  static_assert(ES <= EC, "segment wider than the computed columns");
+  __shared__ float s_acc[NW][kSumBlock][EC + 1];
+  __shared__ float s_p[kSumBlock][EC + 1];
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  const int t0 = blockIdx.x * kSumBlock;
+  const int r = lane & 15, q = lane >> 4;
+  const int nsteps = (d + 31) / 32;
+  const bool a_ok = t0 + r < T;
+  const uint16_t *xa = x + (size_t)min(t0 + r, T - 1) * d;
+  const uint16_t *wb[NB];
+  bool b_ok[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int e = b * 16 + r;
+    b_ok[b] = e < E;
+    wb[b] = wr + (size_t)min(e, E - 1) * d;
+  }
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  for (int s0 = wv; s0 < nsteps; s0 += NW * U) {
+    u32x4 av[U], bv[U][NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int cc = min((s0 + u * NW) * 32 + q * 8, d - 8);
+      av[u] = *reinterpret_cast<const u32x4 *>(xa + cc);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) bv[u][b] = *reinterpret_cast<const u32x4 *>(wb[b] + cc);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = (s0 + u * NW) * 32 + q * 8 < d;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, (in && a_ok) ? av[u] : zero4);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const bf16x8 w = __builtin_bit_cast(bf16x8, (in && b_ok[b]) ? bv[u][b] : zero4);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[b], 0, 0, 0);
+      }
+    }
+  }
+  // 16x16 accumulator layout: lane holds column (expert) lane % 16 and rows
+  // (tokens) 4 (lane / 16) + i in register i
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_acc[wv][4 * q + i][b * 16 + r] = acc[b][i];
+  __syncthreads();
+  {
+    const int tt = threadIdx.x / 32, e = threadIdx.x % 32;  // 512 threads = 16 tokens x 32
+    if (e < EC) {
+      float v = s_acc[0][tt][e];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v += s_acc[w][tt][e];
+      s_acc[0][tt][e] = v;
+    }
+  }
+  __syncthreads();
+  constexpr int TPW = kWave / ES;          // tokens per wave in the selection
+  constexpr int SW = kSumBlock / TPW;      // waves that select
+  if (wv < SW) {
+    const int i = wv * TPW + lane / ES, e = lane % ES, t = t0 + i;
+    const bool ok = t < T && e < E;
+    float v = 0.f;
+    if (ok) {
+      v = s_acc[0][i][e];
+      if (bias) v += bias[e];
+      if (logits_out) logits_out[(size_t)t * E + e] = v;
+    }
+    int my_idx;
+    float my_w;
+    const float p = select_segment<ES>(v, ok, e, k, renorm, &my_idx, &my_w);
+    if (t < T && e < k) {
+      topk_idx[(size_t)t * k + e] = my_idx;
+      topk_w[(size_t)t * k + e] = my_w;
+    }
+    s_p[i][e] = p;
+  }
+  if (prob_sums) {
+    __syncthreads();
+    if ((int)threadIdx.x < E) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < kSumBlock; ++i) sum += s_p[i][threadIdx.x];
+      prob_sums[(size_t)blockIdx.x * E + threadIdx.x] = sum;
+    }
+  }
+}
+
+// E <= 32, fp32: one launch.  A workgroup of 16 ES threads owns 16 tokens;
+// thread (i, e) = (tid / ES, tid % ES) accumulates the dot product of token
+// i and expert e over d in order (16-byte loads), then the ES lanes of a
+// token select as above.
+template <int ES>
+__global__ __launch_bounds__(kSumBlock * ES) void route_small_f32(
+    const float *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
+    int T, int d, int E, int k, int renorm, float *__restrict__ logits_out,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ prob_sums) {
+  __shared__ float s_p[kSumBlock][ES + 1];
+  const int i = threadIdx.x / ES, e = threadIdx.x % ES;
+  const int t = blockIdx.x * kSumBlock + i;
+  const bool ok = t < T && e < E;
+  const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)min(t, T - 1) * d);
+  const float4 *wrow = reinterpret_cast<const float4 *>(wr + (size_t)min(e, E - 1) * d);
+  float acc = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < d / 4; ++c) {
+    const float4 a = xr[c], b = wrow[c];
+    acc = fmaf(a.x, b.x, acc);
+    acc = fmaf(a.y, b.y, acc);
+    acc = fmaf(a.z, b.z, acc);
+    acc = fmaf(a.w, b.w, acc);
+  }
+  float v = acc;
+  if (ok) {
+    if (bias) v += bias[e];
+    if (logits_out) logits_out[(size_t)t * E + e] = v;
+  }
+  int my_idx;
+  float my_w;
+  const float p = select_segment<ES>(v, ok, e, k, renorm, &my_idx, &my_w);
   if (t < T && e < k) {
     topk_idx[(size_t)t * k + e] = my_idx;
     topk_w[(size_t)t * k + e] = my_w;
   }
+  if (prob_sums) {
+    s_p[i][e] = p;
+    __syncthreads();
+    if ((int)threadIdx.x < E) {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < kSumBlock; ++j) sum += s_p[j][threadIdx.x];
+      prob_sums[(size_t)blockIdx.x * E + threadIdx.x] = sum;
+    }
+  }
 }
 
-template <int W, int NPER>
-void launch_select_t(const float *part, int S, const float *bias, int T, int E, int k, int renorm,
-                     float *logits_out, int32_t *topk_idx, float *topk_w, hipStream_t s) {
-  constexpr int TPB = (kThreads / kWave) * (kWave / W);  // tokens per workgroup
-  hipLaunchKernelGGL((route_select<W, NPER>), dim3((T + TPB - 1) / TPB), dim3(kThreads), 0, s,
-                     part, S, bias, T, E, k, renorm, logits_out, topk_idx, topk_w);
+// ---------------------------------------------------------------------------
+// Selection from S slices of partial logits (or from given logits, S = 1):
+// 16 tokens per workgroup of 16 waves, a wave per token (8 waves of two
+// tokens each when NPER = 16), lane l holding the
+// NPER consecutive experts l NPER .. l NPER + NPER - 1 (16-byte loads when
+// VEC).  A wave issues the loads of up to 8 slices (32 values a lane)
+// together, adds them
+// in slice order (deterministic), adds the bias, exports, and selects with
+// wave-wide reductions.  The probability sums of the 16 tokens are added
+// over the waves in token order.  (Four waves of four tokens each, loads of
+// four tokens in flight per wave: 32 us on the DeepSeek shapes, 4 waves per
+// CU; a wave per token: see the design notes.)
+// tokens a wave takes one after the other (two when a lane holds 16 experts,
+// so that 256 registers are left to a lane)
+__host__ __device__ constexpr int sel_tpw(int nper) { return nper >= 16 ? 2 : 1; }
+
+template <int NPER, bool VEC>
+__global__ __launch_bounds__(kSumBlock / sel_tpw(NPER) * kWave) void route_select_wave(
+    const float *__restrict__ part, int S, const float *__restrict__ bias, int T, int E, int k,
+    int renorm, float *__restrict__ logits_out, int32_t *__restrict__ topk_idx,
+    float *__restrict__ topk_w, float *__restrict__ prob_sums) {
+  constexpr int CH = NPER <= 4 ? 8 : 32 / NPER;  // slices loaded together (<= 32 values)
+  extern __shared__ float s_ps[];  // [16][E] when prob_sums is given
+  constexpr int TPW = sel_tpw(NPER), NWV = kSumBlock / TPW;
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  const int e0 = lane * NPER;
+  for (int tw = 0; tw < TPW; ++tw) {
+  const int ti = wv * TPW + tw;  // token of the block
+  const int t = blockIdx.x * kSumBlock + ti;
+  const bool tok = t < T;  // no early exit: the reductions need every lane
+  const size_t tcl = (size_t)min(t, T - 1);
+  float v[NPER];
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    float q[CH][NPER];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const size_t rowb = ((size_t)min(s0 + j, S - 1) * T + tcl) * E;
+      if constexpr (VEC) {
+#pragma unroll
+        for (int m = 0; m < NPER / 4; ++m) {
+          const float4 f4 = *reinterpret_cast<const float4 *>(part + rowb + min(e0 + 4 * m, E - 4));
+          q[j][4 * m] = f4.x;
+          q[j][4 * m + 1] = f4.y;
+          q[j][4 * m + 2] = f4.z;
+          q[j][4 * m + 3] = f4.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) q[j][i] = part[rowb + min(e0 + i, E - 1)];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if (s0 + j < S) v[i] = (s0 + j == 0) ? q[j][i] : v[i] + q[j][i];
+  }
+  bool ok[NPER];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = e0 + i;
+    ok[i] = tok && e < E;
+    if (ok[i]) {
+      if (bias) v[i] += bias[e];
+      if (logits_out) logits_out[(size_t)t * E + e] = v[i];
+    } else {
+      v[i] = -INFINITY;
+    }
+    mx = fmaxf(mx, v[i]);
+  }
+  mx = seg_max<kWave>(mx);
+  float z = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i)
+    if (ok[i]) z += expf(v[i] - mx);
+  z = seg_sum<kWave>(z);
+  uint32_t taken = 0;
+  float my_w = 0.f;
+  int my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {  // ascending e: a tie keeps the lower index
+      if (ok[i] && !((taken >> i) & 1u) && v[i] > bv) {
+        bv = v[i];
+        be = e0 + i;
+      }
+    }
+    seg_argmax<kWave>(bv, be);
+    if (be >= e0 && be < e0 + NPER) taken |= 1u << (be - e0);
+    if (lane == j) {
+      my_idx = be;
+      my_w = expf(bv - mx) / z;
+    }
+  }
+  if (renorm) {
+    float sw = lane < k ? my_w : 0.f;
+    sw = seg_sum<kWave>(sw);
+    my_w = my_w / sw;
+  }
+  if (tok && lane < k) {
+    topk_idx[(size_t)t * k + lane] = my_idx;
+    topk_w[(size_t)t * k + lane] = my_w;
+  }
+  if (prob_sums) {
+#pragma unroll
+    for (int i = 0; i < NPER; ++i)
+      if (e0 + i < E) s_ps[ti * E + e0 + i] = ok[i] ? expf(v[i] - mx) / z : 0.f;
+  }
+  }  // tokens of the wave
+  if (prob_sums) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += NWV * kWave) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < kSumBlock; ++i) sum += s_ps[i * E + e];
+      prob_sums[(size_t)blockIdx.x * E + e] = sum;
+    }
+  }
 }
 
-// segment width: the next power of two >= E up to 64, then NPER = E / 64
+template <int NPER>
+void launch_select_n(const float *part, int S, const float *bias, int T, int E, int k,
+                     int renorm, float *logits_out, int32_t *topk_idx, float *topk_w,
+                     float *prob_sums, hipStream_t s) {
+  const dim3 grid((T + kSumBlock - 1) / kSumBlock), block(kSumBlock / sel_tpw(NPER) * kWave);
+  const size_t lds = prob_sums ? sizeof(float) * kSumBlock * (size_t)E : 0;
+  if constexpr (NPER % 4 == 0) {
+    if (E % 4 == 0) {
+      hipLaunchKernelGGL((route_select_wave<NPER, true>), grid, block, lds, s, part, S, bias, T,
+                         E, k, renorm, logits_out, topk_idx, topk_w, prob_sums);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((route_select_wave<NPER, false>), grid, block, lds, s, part, S, bias, T, E,
+                     k, renorm, logits_out, topk_idx, topk_w, prob_sums);
+}
+
 void launch_select(const float *part, int S, const float *bias, int T, int E, int k, int renorm,
-                   float *logits_out, int32_t *topk_idx, float *topk_w, hipStream_t s) {
-#define MOE_SEL(W, NP) \
-  launch_select_t<W, NP>(part, S, bias, T, E, k, renorm, logits_out, topk_idx, topk_w, s)
-  if (E <= 8) MOE_SEL(8, 1);
-  else if (E <= 16) MOE_SEL(16, 1);
-  else if (E <= 32) MOE_SEL(32, 1);
-  else if (E <= 64) MOE_SEL(64, 1);
-  else if (E <= 128) MOE_SEL(64, 2);
-  else if (E <= 256) MOE_SEL(64, 4);
-  else if (E <= 512) MOE_SEL(64, 8);
-  else MOE_SEL(64, 16);
+                   float *logits_out, int32_t *topk_idx, float *topk_w, float *prob_sums,
+                   hipStream_t s) {
+#define MOE_SEL(NP) \
+  launch_select_n<NP>(part, S, bias, T, E, k, renorm, logits_out, topk_idx, topk_w, prob_sums, s)
+  if (E <= 64) MOE_SEL(1);
+  else if (E <= 128) MOE_SEL(2);
+  else if (E <= 256) MOE_SEL(4);
+  else if (E <= 512) MOE_SEL(8);
+  else MOE_SEL(16);
 #undef MOE_SEL
 }
 
 }  // namespace
 
 size_t route_ws_bytes(int T, int d, int E) {
-  return sizeof(float) * (size_t)route_splits(T, d, E) * (size_t)T * (size_t)E;
+  if (E <= 32) return 0;  // one-launch paths
+  const int S = d % LK == 0 ? route_split_slices(T, d, E) : route_splits(T, d, E);
+  return sizeof(float) * (size_t)S * (size_t)T * (size_t)E;
 }
 
 hipError_t launch_route(const void *x, const void *w_router, int dt, const float *bias, int T,
                         int d, int E, int k, unsigned flags, float *logits, int32_t *topk_idx,
-                        float *topk_w, float *ws, hipStream_t s) {
+                        float *topk_w, float *prob_sums, float *ws, hipStream_t s) {
   const int renorm = (flags & MOE_ROUTE_RENORM) ? 1 : 0;
-  const dim3 block(kThreads);
   if (flags & MOE_ROUTE_FROM_LOGITS) {
-    launch_select(logits, 1, nullptr, T, E, k, renorm, nullptr, topk_idx, topk_w, s);
+    launch_select(logits, 1, nullptr, T, E, k, renorm, nullptr, topk_idx, topk_w, prob_sums, s);
     return hipGetLastError();
   }
-  if (dt == MOE_BF16 && E <= 32) {
-    const uint16_t *xb = static_cast<const uint16_t *>(x);
-    const uint16_t *wb = static_cast<const uint16_t *>(w_router);
-    if (E <= 8)
-      hipLaunchKernelGGL(route_fused_small<8>, dim3((T + 7) / 8), block, 0, s, xb, wb, bias, T, d,
-                         E, k, renorm, logits, topk_idx, topk_w);
-    else if (E <= 16)
-      hipLaunchKernelGGL(route_fused_small<16>, dim3((T + 3) / 4), block, 0, s, xb, wb, bias, T, d,
-                         E, k, renorm, logits, topk_idx, topk_w);
-    else
-      hipLaunchKernelGGL(route_fused_small<32>, dim3((T + 1) / 2), block, 0, s, xb, wb, bias, T, d,
-                         E, k, renorm, logits, topk_idx, topk_w);
+  const unsigned nblk = (unsigned)((T + kSumBlock - 1) / kSumBlock);
+  if (E <= 32) {
+    const int es = E <= 8 ? 8 : (E <= 16 ? 16 : 32);
+    if (dt == MOE_BF16) {
+      const uint16_t *xb = static_cast<const uint16_t *>(x);
+      const uint16_t *wb = static_cast<const uint16_t *>(w_router);
+#define MOE_SMALL(NB, ES)                                                                    \
+  hipLaunchKernelGGL((route_small_bf16<NB, ES>), dim3(nblk), dim3(512), 0, s, xb, wb, bias, T, \
+                     d, E, k, renorm, logits, topk_idx, topk_w, prob_sums)
+      if (es == 8) MOE_SMALL(1, 8);
+      else if (es == 16) MOE_SMALL(1, 16);
+      else MOE_SMALL(2, 32);
+#undef MOE_SMALL
+    } else {
+      const float *xf = static_cast<const float *>(x);
+      const float *wf = static_cast<const float *>(w_router);
+#define MOE_SMALL(ES)                                                                          \
+  hipLaunchKernelGGL((route_small_f32<ES>), dim3(nblk), dim3(kSumBlock * ES), 0, s, xf, wf, bias, \
+                     T, d, E, k, renorm, logits, topk_idx, topk_w, prob_sums)
+      if (es == 8) MOE_SMALL(8);
+      else if (es == 16) MOE_SMALL(16);
+      else MOE_SMALL(32);
+#undef MOE_SMALL
+    }
     return hipGetLastError();
   }
   int S = 1;
+  const dim3 block(kThreads);
   if (dt == MOE_BF16) {
-    S = route_splits(T, d, E);
-    const int eb = route_eb(E);
-    const int kt = (d + RK - 1) / RK;
-    const dim3 grid((T + RT - 1) / RT, (E + eb - 1) / eb, S);
-    const int ks = (kt + S - 1) / S;
     const uint16_t *xb = static_cast<const uint16_t *>(x);
     const uint16_t *wb = static_cast<const uint16_t *>(w_router);
-    if (eb == 32)
-      hipLaunchKernelGGL(route_logits_bf16<32>, grid, block, 0, s, xb, wb, T, d, E, ks, ws);
-    else if (eb == 64)
-      hipLaunchKernelGGL(route_logits_bf16<64>, grid, block, 0, s, xb, wb, T, d, E, ks, ws);
-    else
-      hipLaunchKernelGGL(route_logits_bf16<128>, grid, block, 0, s, xb, wb, T, d, E, ks, ws);
+    if (d % LK == 0) {
+      S = route_split_slices(T, d, E);
+      const int nst = d / LK, sps = (nst + S - 1) / S;
+      const dim3 grid((T + LT - 1) / LT, (E + LE - 1) / LE, S);
+      hipLaunchKernelGGL(route_logits_split, grid, dim3(LTH), 0, s, xb, wb, T, d, E, sps, ws);
+    } else {
+      S = route_splits(T, d, E);
+      const int eb = route_eb(E);
+      const int kt = (d + RK - 1) / RK;
+      const dim3 grid((T + RT - 1) / RT, (E + eb - 1) / eb, S);
+      const int ks = (kt + S - 1) / S;
+      if (eb == 32)
+        hipLaunchKernelGGL(route_logits_bf16<32>, grid, block, 0, s, xb, wb, T, d, E, ks, ws);
+      else if (eb == 64)
+        hipLaunchKernelGGL(route_logits_bf16<64>, grid, block, 0, s, xb, wb, T, d, E, ks, ws);
+      else
+        hipLaunchKernelGGL(route_logits_bf16<128>, grid, block, 0, s, xb, wb, T, d, E, ks, ws);
+    }
   } else {
     const long long n = (long long)T * E;
     hipLaunchKernelGGL(route_logits_f32, dim3((unsigned)((n + kThreads - 1) / kThreads)), block,
                        0, s, static_cast<const float *>(x), static_cast<const float *>(w_router),
                        T, d, E, ws);
   }
-  launch_select(ws, S, bias, T, E, k, renorm, logits, topk_idx, topk_w, s);
+  launch_select(ws, S, bias, T, E, k, renorm, logits, topk_idx, topk_w, prob_sums, s);
   return hipGetLastError();
 }

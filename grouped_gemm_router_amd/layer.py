@@ -27,7 +27,7 @@ class MoELayer:
     """
 
     def __init__(self, w_router, w_gate, w_up, w_down, k, *, n_shared=0, bias=None, fp8=False,
-                 renorm=False, keep_logits=True, capacity_factor=None):
+                 renorm=False, keep_logits=True, keep_prob_sums=True, capacity_factor=None):
         self.E, self.d = w_router.shape
         self.G, self.dff, d2 = w_gate.shape
         assert d2 == self.d and self.G == self.E + n_shared
@@ -37,6 +37,9 @@ class MoELayer:
         self.bias = None if bias is None else bias.to(torch.float32).contiguous()
         self.flags = api.MOE_ROUTE_RENORM if renorm else 0
         self.keep_logits = keep_logits
+        # per-16-token sums of the gate probabilities, written by the route
+        # for router_stats
+        self.keep_prob_sums = keep_prob_sums
         # capacity factor cf: each expert keeps at most ceil(cf * T * k / E)
         # routed rows (1.0 = a perfectly even share); None = drop-less
         self.capacity_factor = capacity_factor
@@ -78,6 +81,8 @@ class MoELayer:
         rows = T * k + ns * T
         i32, f32 = torch.int32, torch.float32
         self.logits = torch.empty((T, E), dtype=f32, device=dev) if self.keep_logits else None
+        self.prob_sums = (torch.empty((api.prob_sum_blocks(T), E), dtype=f32, device=dev)
+                          if self.keep_prob_sums else None)
         self.topk_idx = torch.empty((T, k), dtype=i32, device=dev)
         self.topk_w = torch.empty((T, k), dtype=f32, device=dev)
         self.counts = torch.empty((E,), dtype=i32, device=dev)
@@ -120,7 +125,8 @@ class MoELayer:
         E, ns = self.E, self.n_shared
         s = [("route", lambda: api.moe_route(x, self.w_router, self.topk_idx, self.topk_w,
                                              logits=self.logits, logit_bias=self.bias,
-                                             flags=self.flags, ws=self.ws)),
+                                             flags=self.flags, prob_sums=self.prob_sums,
+                                             ws=self.ws)),
              ("permute", self._permute_fn(x))]
         if self.fp8:
             s.append(("gemm_gate_up", lambda: api.moe_grouped_gemm_fp8(
@@ -153,22 +159,18 @@ class MoELayer:
                                               x_perm_scale=self.x_scale)
 
     def router_stats(self, alpha: float = 0.01):
-        """Load-balance statistics of the last forward (needs keep_logits):
+        """Load-balance statistics of the last forward (needs keep_prob_sums):
         f [E], P [E] and summary [3] = (aux loss, max/mean, entropy bits),
-        as device tensors, enqueued on the current stream."""
-        if self.logits is None:
-            raise RuntimeError("router_stats needs the logits: build the layer with "
-                               "keep_logits=True")
-        T = self.logits.shape[0]
+        as device tensors, enqueued on the current stream (one launch over
+        the route's probability sums and the permute's counts)."""
+        if self.prob_sums is None:
+            raise RuntimeError("router_stats needs the route's probability sums: build the "
+                               "layer with keep_prob_sums=True")
+        T = self._T
         f = torch.empty((self.E,), dtype=torch.float32, device=self.device)
         P = torch.empty_like(f)
         summary = torch.empty((3,), dtype=torch.float32, device=self.device)
-        if getattr(self, "_stats_ws", None) is None or self._stats_ws_T != T:
-            self._stats_ws = torch.empty((max(api.moe_router_stats_workspace_size(T, self.E), 4),),
-                                         dtype=torch.uint8, device=self.device)
-            self._stats_ws_T = T
-        api.moe_router_stats(self.logits, self.counts, self.k, alpha, f, P, summary,
-                             ws=self._stats_ws)
+        api.moe_router_stats(self.prob_sums, self.counts, T, self.k, alpha, f, P, summary)
         return {"f": f, "P": P, "aux_loss": summary[0], "max_over_mean": summary[1],
                 "entropy_bits": summary[2]}
 

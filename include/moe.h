@@ -102,6 +102,10 @@ int moe_abi_version(void);
  * logit_bias [E] fp32 or NULL.  logits [T][E] fp32: written if non-NULL; with
  * MOE_ROUTE_FROM_LOGITS it is read instead (and must be non-NULL).
  * topk_idx [T][k] int32, topk_w [T][k] fp32 are written.
+ * prob_sums [ceil(T/16)][E] fp32 or NULL: if given, prob_sums[b][e] = the sum
+ * over tokens t = 16 b .. min(16 b + 15, T - 1) of p_t[e] (the softmax over
+ * all E, before any renormalisation), summed in a fixed order; it feeds
+ * moe_router_stats.
  * ws (device, 4-byte aligned) holds the fp32 partial logits of the d-axis
  * slices; it must hold moe_route_workspace_size(T, d, E) bytes (else
  * MOE_ERR_WORKSPACE).  With MOE_ROUTE_FROM_LOGITS it is unused (may be NULL,
@@ -112,10 +116,12 @@ int moe_abi_version(void);
 moe_status_t moe_route(const void *x, const void *w_router, moe_dtype_t dt,
                        const float *logit_bias, int T, int d, int E, int k,
                        unsigned flags, float *logits, int32_t *topk_idx,
-                       float *topk_w, void *ws, size_t ws_bytes, moe_stream_t stream);
+                       float *topk_w, float *prob_sums, void *ws, size_t ws_bytes,
+                       moe_stream_t stream);
 
 /* Bytes of device workspace moe_route needs for these sizes (the router's
- * split-K partial logits: at most a small multiple of T * E * 4). */
+ * split-K partial logits: at most a small multiple of T * E * 4; 0 for
+ * E <= 32, which routes in one launch). */
 size_t moe_route_workspace_size(int T, int d, int E);
 
 /* Bytes of device workspace moe_permute needs for these sizes. */
@@ -211,10 +217,6 @@ moe_status_t moe_permute_capped(const void *x, moe_dtype_t x_dt, int T, int d,
                                 int32_t *n_overflow, void *ws, size_t ws_bytes,
                                 moe_stream_t stream);
 
-/* Bytes of device workspace moe_router_stats needs ((T/64 rounded up) x E
- * floats). */
-size_t moe_router_stats_workspace_size(int T, int E);
-
 /*
  * Load-balance statistics of one routing decision, forward only.
  *   P[e] = (1/T) sum_t softmax(logits[t][.])[e]   mean gate probability [E]
@@ -225,15 +227,15 @@ size_t moe_router_stats_workspace_size(int T, int E);
  *                ("Dense GEMM to TP MoE" §5.1: above 3 is severe)
  *   summary[2] = -sum_e q[e] log2(q[e] + 1e-8), q = counts / sum counts
  *                (routing entropy in bits, "DeepSeek MoE evolution" §2.3)
- * logits [T][E] fp32 (moe_route's output), counts [E] int32 (moe_permute's),
- * all fp32 outputs on the device.  Softmax as in moe_route (max-subtracted
- * fp32); sums in a fixed order (deterministic).  Counts are exact up to
- * 2^24 in the fp32 arithmetic.  ws must hold
- * moe_router_stats_workspace_size(T, E) bytes (else MOE_ERR_WORKSPACE).
+ * prob_sums [ceil(T/16)][E] fp32 is moe_route's per-block sums of the
+ * softmax probabilities (the router computes every p_t already, so no pass
+ * over the logits is needed), counts [E] int32 is moe_permute's; all fp32
+ * outputs on the device.  One launch; sums in a fixed order
+ * (deterministic).  Counts are exact up to 2^24 in the fp32 arithmetic.
  */
-moe_status_t moe_router_stats(const float *logits, const int32_t *counts, int T, int E,
+moe_status_t moe_router_stats(const float *prob_sums, const int32_t *counts, int T, int E,
                               int k, float alpha, float *f, float *P, float *summary,
-                              void *ws, size_t ws_bytes, moe_stream_t stream);
+                              moe_stream_t stream);
 
 /*
  * Grouped GEMM over ragged groups in one launch ("DeepGEMM walkthrough"

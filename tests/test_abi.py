@@ -29,7 +29,7 @@ def lib():
         build.build()
     L = C.CDLL(LIB)
     vp, i32, u32, sz = C.c_void_p, C.c_int, C.c_uint, C.c_size_t
-    L.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp, sz, vp]
+    L.moe_route.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, u32, vp, vp, vp, vp, vp, sz, vp]
     L.moe_route_workspace_size.restype = sz
     L.moe_route_workspace_size.argtypes = [i32, i32, i32]
     L.moe_permute_workspace_size.restype = sz
@@ -46,9 +46,7 @@ def lib():
     L.moe_quantize_fp8.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
     L.moe_permute_capped.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, i32, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp, sz, vp]
-    L.moe_router_stats_workspace_size.restype = sz
-    L.moe_router_stats_workspace_size.argtypes = [i32, i32]
-    L.moe_router_stats.argtypes = [vp, vp, i32, i32, i32, C.c_float, vp, vp, vp, vp, sz, vp]
+    L.moe_router_stats.argtypes = [vp, vp, i32, i32, i32, C.c_float, vp, vp, vp, vp]
     L.moe_status_string.restype = C.c_char_p
     L.moe_status_string.argtypes = [i32]
     return L
@@ -62,7 +60,7 @@ NUL = C.c_void_p(0)
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), "libmoe.so does not export %s" % n
 
@@ -70,36 +68,39 @@ def test_every_declared_function_is_exported(lib):
 def test_status_strings_and_version(lib):
     for s in range(5):
         assert lib.moe_status_string(s)
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
 
 
 def test_route_validation(lib):
     big = 1 << 40
-    r = lambda *a: lib.moe_route(*a[:-1], P2, big, a[-1])  # noqa: E731  (ample workspace)
+    # (..., topk_w, prob_sums, stream) with an ample workspace
+    r = lambda *a: lib.moe_route(*a[:-2], a[-2], P2, big, a[-1])  # noqa: E731
     # k > E, k < 1, E > max, d % 8, dtype, null outputs, misaligned x
-    assert r(P, P, BF16, NUL, 16, 64, 4, 5, 0, NUL, P, P, NUL) == INVALID
-    assert r(P, P, BF16, NUL, 16, 64, 4, 0, 0, NUL, P, P, NUL) == INVALID
-    assert r(P, P, BF16, NUL, 16, 64, 2000, 2, 0, NUL, P, P, NUL) == UNSUPPORTED
-    assert r(P, P, BF16, NUL, 16, 60, 8, 2, 0, NUL, P, P, NUL) == UNSUPPORTED
-    assert r(P, P, E4M3, NUL, 16, 64, 8, 2, 0, NUL, P, P, NUL) == UNSUPPORTED
-    assert r(P, P, BF16, NUL, 16, 64, 8, 2, 0, NUL, NUL, P, NUL) == INVALID
-    assert r(MIS, P, BF16, NUL, 16, 64, 8, 2, 0, NUL, P, P, NUL) == INVALID
-    assert r(P, P, BF16, NUL, 16, 64, 8, 2, 8, NUL, P, P, NUL) == INVALID  # unknown flag
-    assert r(NUL, NUL, BF16, NUL, 16, 64, 8, 2, 2, NUL, P, P, NUL) == INVALID  # from-logits, no logits
-    assert r(P, P, BF16, NUL, -1, 64, 8, 2, 0, NUL, P, P, NUL) == INVALID
-    assert r(P, P, BF16, NUL, 0, 64, 8, 2, 0, NUL, P, P, NUL) == OK  # T == 0: no-op
+    assert r(P, P, BF16, NUL, 16, 64, 4, 5, 0, NUL, P, P, NUL, NUL) == INVALID
+    assert r(P, P, BF16, NUL, 16, 64, 4, 0, 0, NUL, P, P, NUL, NUL) == INVALID
+    assert r(P, P, BF16, NUL, 16, 64, 2000, 2, 0, NUL, P, P, NUL, NUL) == UNSUPPORTED
+    assert r(P, P, BF16, NUL, 16, 60, 8, 2, 0, NUL, P, P, NUL, NUL) == UNSUPPORTED
+    assert r(P, P, E4M3, NUL, 16, 64, 8, 2, 0, NUL, P, P, NUL, NUL) == UNSUPPORTED
+    assert r(P, P, BF16, NUL, 16, 64, 8, 2, 0, NUL, NUL, P, NUL, NUL) == INVALID
+    assert r(MIS, P, BF16, NUL, 16, 64, 8, 2, 0, NUL, P, P, NUL, NUL) == INVALID
+    assert r(P, P, BF16, NUL, 16, 64, 8, 2, 0, NUL, P, P, MIS, NUL) == INVALID  # prob_sums
+    assert r(P, P, BF16, NUL, 16, 64, 8, 2, 8, NUL, P, P, NUL, NUL) == INVALID  # unknown flag
+    assert r(NUL, NUL, BF16, NUL, 16, 64, 8, 2, 2, NUL, P, P, NUL, NUL) == INVALID  # no logits
+    assert r(P, P, BF16, NUL, -1, 64, 8, 2, 0, NUL, P, P, NUL, NUL) == INVALID
+    assert r(P, P, BF16, NUL, 0, 64, 8, 2, 0, NUL, P, P, NUL, NUL) == OK  # T == 0: no-op
 
 
 def test_route_workspace(lib):
     need = lib.moe_route_workspace_size(4096, 7168, 256)
     assert need >= 4096 * 256 * 4 and need % (4096 * 256 * 4) == 0
     assert lib.moe_route_workspace_size(-1, 64, 8) == 0
-    args = (P, P, BF16, NUL, 4096, 7168, 256, 8, 0, NUL, P, P)
+    assert lib.moe_route_workspace_size(4096, 4096, 8) == 0   # E <= 32: one launch, no workspace
+    args = (P, P, BF16, NUL, 4096, 7168, 256, 8, 0, NUL, P, P, NUL)
     assert lib.moe_route(*args, P2, need - 1, NUL) == WORKSPACE
     assert lib.moe_route(*args, NUL, 0, NUL) == WORKSPACE
     assert lib.moe_route(*args, MIS, need, NUL) == INVALID
     # from-logits needs no workspace; with T == 0 nothing is launched
-    assert lib.moe_route(NUL, NUL, BF16, NUL, 0, 8, 256, 8, 2, P, P, P, NUL, 0, NUL) == OK
+    assert lib.moe_route(NUL, NUL, BF16, NUL, 0, 8, 256, 8, 2, P, P, P, NUL, NUL, 0, NUL) == OK
 
 
 def test_permute_validation_and_workspace(lib):
@@ -214,10 +215,9 @@ def test_permute_capped_validation(lib):
 
 
 def test_router_stats_validation(lib):
-    need = lib.moe_router_stats_workspace_size(4096, 256)
-    assert need == (4096 // 16) * 256 * 4   # one fp32 row of E per 16-token block
-    s = lambda T, E, k, wsb: lib.moe_router_stats(P, P, T, E, k, 0.01, P, P, P, P2, wsb, NUL)  # noqa: E731
-    assert s(4096, 256, 0, need) == INVALID     # k < 1
-    assert s(4096, 2000, 8, 1 << 30) == UNSUPPORTED
-    assert s(4096, 256, 8, need - 1) == WORKSPACE
-    assert lib.moe_router_stats(P, P, 0, 256, 8, 0.01, P, P, P, NUL, 0, NUL) == OK
+    s = lambda T, E, k, ps=P: lib.moe_router_stats(ps, P, T, E, k, 0.01, P, P, P, NUL)  # noqa: E731
+    assert s(4096, 256, 0) == INVALID     # k < 1
+    assert s(4096, 2000, 8) == UNSUPPORTED
+    assert s(4096, 256, 8, MIS) == INVALID
+    assert s(4096, 256, 8, NUL) == INVALID
+    assert s(0, 256, 8) == OK             # T == 0: nothing launched

@@ -32,8 +32,10 @@ def run_from_logits(lg: np.ndarray, k: int, renorm=False):
     idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
     w = torch.empty((T, k), dtype=torch.float32, device=DEV)
     flags = a.MOE_ROUTE_FROM_LOGITS | (a.MOE_ROUTE_RENORM if renorm else 0)
-    a.moe_route(None, None, idx, w, logits=logits, flags=flags)
+    ps = torch.full((a.prob_sum_blocks(T), E), float("nan"), dtype=torch.float32, device=DEV)
+    a.moe_route(None, None, idx, w, logits=logits, flags=flags, prob_sums=ps)
     torch.cuda.synchronize()
+    check_prob_sums(ps, lg)
     return idx.cpu().numpy(), w.cpu().numpy()
 
 
@@ -61,6 +63,25 @@ def test_from_logits_exact_ties(orc, E, k):
     ridx, rw = orc.topk(lg, k)
     np.testing.assert_array_equal(idx, ridx)
     np.testing.assert_allclose(w, rw, atol=1e-6, rtol=0)
+
+
+def check_prob_sums(ps, lg32):
+    """Per-16-token sums of the softmax probabilities against fp64 sums of the
+    softmax of the same fp32 logits: each term within ~(E + 30) u relative
+    (exp, the normaliser over E terms, one division), 16 more roundings of
+    the positive partial sums."""
+    T, E = lg32.shape
+    l64 = lg32.astype(np.float64)
+    p = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    nb = (T + 15) // 16
+    pad = np.zeros((nb * 16, E))
+    pad[:T] = p
+    ref = pad.reshape(nb, 16, E).sum(axis=1)
+    got = ps.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert (np.abs(got - ref) <= (E + 50) * 2.0 ** -24 * ref + 1e-30).all(), \
+        np.abs(got / np.maximum(ref, 1e-300) - 1).max()
 
 
 def check_selection(idx, lg_ref, bound, k):
@@ -103,6 +124,13 @@ def check_selection(idx, lg_ref, bound, k):
     ("bf16", 65, 512, 30, 5, False),
     # E < 8 in 8-lane segments, d = 2048 (one chunk per lane and wave)
     ("bf16", 9, 2048, 5, 2, True),
+    # split-K MFMA logits (d % 64 == 0): 48 experts of a 256-wide tile, three
+    # token tiles with a ragged tail; two expert tiles, the second ragged
+    ("bf16", 257, 2048, 48, 4, False),
+    ("bf16", 200, 512, 300, 6, True),
+    # one-launch fp32 path with 16- and 32-lane segments
+    ("f32", 100, 64, 16, 3, True),
+    ("f32", 33, 256, 20, 4, False),
 ])
 def test_scoring_and_selection(orc, dt, T, d, E, k, bias):
     a = api()
@@ -113,8 +141,10 @@ def test_scoring_and_selection(orc, dt, T, d, E, k, bias):
     logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
     idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
     w = torch.empty((T, k), dtype=torch.float32, device=DEV)
-    a.moe_route(x, wr, idx, w, logits=logits, logit_bias=b)
+    ps = torch.full((a.prob_sum_blocks(T), E), float("nan"), dtype=torch.float32, device=DEV)
+    a.moe_route(x, wr, idx, w, logits=logits, logit_bias=b, prob_sums=ps)
     torch.cuda.synchronize()
+    check_prob_sums(ps, logits.cpu().numpy())
     lg_ref, absdot = orc.router_logits(np_of(x), np_of(wr), None if b is None else np_of(b))
     got = logits.cpu().numpy().astype(np.float64)
     # fp32 accumulation of exact products: |err| <= d * 2^-24 * sum|x w| (+ bias rounding)
