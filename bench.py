@@ -4,11 +4,18 @@ libmoe.so on one MI355X, over seeded synthetic inputs already resident in
 HBM.  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+                    [--no-configs] [--no-extras]
 
-Default workload: the Mixtral-shape bf16 layer (T=4096, d=4096, E=8, top-2,
-SwiGLU d_ff=14336).  `value` is layer tokens/s; the grouped-GEMM TFLOP/s and
-fraction of bf16 MFMA peak ride along.  Per-kernel times come from HIP events
-recorded on the launch stream around every call of every timed step.
+Headline workload: the Mixtral-shape bf16 layer (T=4096, d=4096, E=8, top-2,
+SwiGLU d_ff=14336).  `value` is layer tokens/s over K timed steps (HIP events
+around the whole loop, nothing else recorded inside it), after W warm-up
+steps.  Per-kernel times come from a pass of K steps before those, with HIP
+events on the launch stream around every call.  The grouped-GEMM TFLOP/s and fraction of the bf16 MFMA
+peak ride along, and `configs` repeats the measurement (fewer steps) for the
+other workloads.  HBM fractions divide the algorithmic bytes of each step
+(bf16 expert outputs Y, as the method stores them) by the kernel time; the
+bf16 layers keep Y in fp32, whose extra bytes are reported next to them as
+`impl_bytes` / `hbm_frac_impl_bytes`.
 """
 from __future__ import annotations
 
@@ -25,6 +32,9 @@ METRIC = "grouped-GEMM TFLOP/s (% MFMA peak) + MoE-layer tokens/s per config"
 PEAK = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}  # dense MFMA TFLOP/s, MI355X
 HBM_PEAK_GBS = 8000.0
 STEP_NAMES = ["route", "permute", "gemm_gate_up", "gemm_down", "combine"]
+# the workloads of the `configs` block, in this order
+CONFIG_ORDER = ["tiny_f32", "mixtral_bf16", "skew_bf16", "skew_decode_bf16", "deepseek_bf16",
+                "deepseek_fp8"]
 
 
 
@@ -35,6 +45,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="mixtral_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="measure only --config (no `configs` block)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the routing variants timed outside the layer step")
+    p.add_argument("--config-steps", type=int, default=10,
+                   help="timed steps of each workload of the `configs` block")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--calib-copy", action="store_true",
@@ -42,25 +58,40 @@ def parse():
     return p.parse_args()
 
 
-def step_bytes_flops(cfg, counts):
-    """Algorithmic bytes and flops per launch of each step."""
+def step_bytes_flops(cfg, counts, logits_exported=False):
+    """Per step: (algorithmic bytes, implementation bytes, flops) of one
+    launch.  Algorithmic bytes count every input once, every output once and
+    each active expert's weights once, with the method's own storage types
+    (bf16 H and Y; E4M3 + fp32 scales in the FP8 layer); the bf16 copy of the
+    shared expert's rows is not algorithmic (the rows are x itself).
+    Implementation bytes differ where this implementation moves more: the
+    bf16 layers store Y in fp32, and the permutation writes the shared rows."""
     es = 4 if cfg.dtype == "f32" else 2
     T, d, E, k, dff, ns = cfg.T, cfg.d, cfg.E, cfg.k, cfg.dff, cfg.n_shared
     rows = cfg.rows
+    routed = T * k
     active = int((counts > 0).sum()) + ns
-    w_es = 1 if cfg.dtype == "fp8" else es
-    act_es = 1 if cfg.dtype == "fp8" else es
+    fp8 = cfg.dtype == "fp8"
+    w_es = 1 if fp8 else es
+    act_es = 1 if fp8 else es
+    maps = T * k * 4 * 4  # topk ids read, perm_src / flat_to_row written, ranks
     out = {}
-    out["route"] = (T * d * es + E * d * es + T * E * 4 + T * k * 8, 2.0 * T * E * d)
-    out["permute"] = (T * d * es + rows * d * act_es + T * k * 4 * 4
-                      + (rows * (d // 128) * 4 if cfg.dtype == "fp8" else 0), 0.0)
-    wsc = (active * 2 * (dff // 128) * (d // 128) * 4) if cfg.dtype == "fp8" else 0
-    out["gemm_gate_up"] = (rows * d * act_es + active * 2 * dff * d * w_es + wsc
-                           + rows * dff * act_es, 2.0 * rows * d * 2 * dff)
-    y_es = 2 if cfg.dtype == "fp8" else 4  # Y is fp32 except in the FP8 layer
-    out["gemm_down"] = (rows * dff * act_es + active * d * dff * w_es + wsc // 2
-                        + rows * d * y_es, 2.0 * rows * dff * d)
-    out["combine"] = (rows * d * y_es + T * d * es + T * k * 8, 0.0)
+    rb = T * d * es + E * d * es + T * k * 8 + (T * E * 4 if logits_exported else 0)
+    out["route"] = (rb, rb, 2.0 * T * E * d)
+    perm_rows = rows if fp8 else routed  # shared rows: quantised (FP8) or x itself
+    pb = T * d * es + perm_rows * d * act_es + maps + (rows * (d // 128) * 4 if fp8 else 0)
+    out["permute"] = (pb, T * d * es + rows * d * act_es + maps
+                      + (rows * (d // 128) * 4 if fp8 else 0), 0.0)
+    wsc = (active * 2 * (dff // 128) * (d // 128) * 4) if fp8 else 0
+    hsc = rows * (dff // 128) * 4 if fp8 else 0
+    gb = rows * d * act_es + active * 2 * dff * d * w_es + wsc + rows * dff * act_es + hsc
+    out["gemm_gate_up"] = (gb, gb, 2.0 * rows * d * 2 * dff)
+    y_alg = es                       # Y as the method stores it (bf16; fp32 layer: fp32)
+    y_impl = es if fp8 or es == 4 else 4   # the bf16 layers keep Y in fp32
+    db = rows * dff * act_es + hsc + active * d * dff * w_es + wsc // 2
+    out["gemm_down"] = (db + rows * d * y_alg, db + rows * d * y_impl, 2.0 * rows * dff * d)
+    cb = T * d * es + T * k * 8 + (T * k + ns * T) * 4
+    out["combine"] = (rows * d * y_alg + cb, rows * d * y_impl + cb, 0.0)
     return out
 
 
@@ -186,6 +217,87 @@ def cpu_baseline(cfg, layer, x, wr, bias, weights, target_s):
                       % (cfg.T, t_route, ntok, t_first + t_more)}
 
 
+def build_layer(cfg, dev):
+    import torch
+
+    from grouped_gemm_router_amd import synth
+    from grouped_gemm_router_amd.layer import MoELayer
+    x = synth.gen_x(cfg, dev)
+    wr = synth.gen_router(cfg, dev)
+    bias = synth.gen_bias(cfg, dev)
+    weights = synth.gen_experts(cfg, dev)
+    layer = MoELayer(wr, *weights, cfg.k, n_shared=cfg.n_shared, bias=bias,
+                     fp8=cfg.dtype == "fp8", keep_logits=False, keep_prob_sums=False)
+    layer.alloc(cfg.T)
+    out = torch.empty((cfg.T, cfg.d), dtype=layer.out_dtype, device=dev)
+    return layer, x, wr, bias, weights, out
+
+
+def measure(cfg, layer, x, out, warmup, K, stream):
+    """(ms per layer step, {step: ms per call}): K steps with events around
+    every call (on the stream the library launches on), then `warmup` untimed
+    steps, then the K timed steps with events only around the whole loop."""
+    import numpy as np
+    import torch
+    steps = layer.steps(x, out)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in steps] for _ in range(K)]
+    for i in range(K):
+        for j, (_, fn) in enumerate(steps):
+            ev[i][j][0].record(stream)
+            fn()
+            ev[i][j][1].record(stream)
+    torch.cuda.synchronize()
+    per = {name: float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(K)]))
+           for j, (name, _) in enumerate(steps)}
+    for _ in range(warmup):
+        for _, fn in steps:
+            fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(K):
+        for _, fn in steps:
+            fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    return ms_step, per
+
+
+def kernel_table(cfg, per, counts):
+    bf = step_bytes_flops(cfg, counts)
+    peak = PEAK[cfg.dtype]
+    kernels = {}
+    for name in STEP_NAMES:
+        alg, impl, fl = bf[name]
+        t = per[name] * 1e-3
+        kr = {"ms": round(per[name], 5), "alg_bytes": alg, "GB/s": round(alg / t / 1e9, 1),
+              "hbm_frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4)}
+        if impl != alg:
+            kr["impl_bytes"] = impl
+            kr["hbm_frac_impl_bytes"] = round(impl / t / 1e9 / HBM_PEAK_GBS, 4)
+        if fl:
+            kr["TFLOP/s"] = round(fl / t / 1e12, 2)
+            kr["mfma_frac"] = round(fl / t / 1e12 / peak, 4)
+        kernels[name] = kr
+    return kernels, bf
+
+
+def config_summary(cfg, ms_step, per, counts):
+    kernels, _ = kernel_table(cfg, per, counts)
+    gemm_ms = per["gemm_gate_up"] + per["gemm_down"]
+    tf = cfg.gemm_flops() / (gemm_ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms_step, 5), "tokens_per_s": round(cfg.T / (ms_step * 1e-3), 1),
+            "grouped_gemm_tflops": round(tf, 2),
+            "grouped_gemm_frac_mfma_peak": round(tf / PEAK[cfg.dtype], 4),
+            "peak_tflops": PEAK[cfg.dtype],
+            "rows_per_expert_max_over_mean": round(float(counts.max() / counts.mean()), 3),
+            "kernels": {n: {kk: v for kk, v in r.items()
+                            if kk in ("ms", "hbm_frac", "hbm_frac_impl_bytes", "mfma_frac")}
+                        for n, r in kernels.items()}}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -195,46 +307,17 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from grouped_gemm_router_amd import synth
-    from grouped_gemm_router_amd.layer import MoELayer
 
     cfg = synth.CONFIGS[args.config]
     dev = "cuda"
-    x = synth.gen_x(cfg, dev)
-    wr = synth.gen_router(cfg, dev)
-    bias = synth.gen_bias(cfg, dev)
-    weights = synth.gen_experts(cfg, dev)
-    layer = MoELayer(wr, *weights, cfg.k, n_shared=cfg.n_shared, bias=bias,
-                     fp8=cfg.dtype == "fp8", keep_logits=False)
-    layer.alloc(cfg.T)
-    out = torch.empty((cfg.T, cfg.d), dtype=layer.out_dtype, device=dev)
-    steps = layer.steps(x, out)
     stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
-        for _, fn in steps:
-            fn()
-    torch.cuda.synchronize()
-
+    layer, x, wr, bias, weights, out = build_layer(cfg, dev)
     K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in steps] for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        for j, (_, fn) in enumerate(steps):
-            ev[i][j][0].record(stream)
-            fn()
-            ev[i][j][1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / K
-    per = {name: float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(K)]))
-           for j, (name, _) in enumerate(steps)}
+    extra = None if args.no_extras else extras(cfg, layer, x, K, stream)
+    ms_step, per = measure(cfg, layer, x, out, args.warmup, K, stream)
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -245,22 +328,13 @@ def main():
         del a, b
 
     counts = layer.counts.cpu().numpy()
-    bf = step_bytes_flops(cfg, counts)
+    kernels, bf = kernel_table(cfg, per, counts)
     gemm_ms = per["gemm_gate_up"] + per["gemm_down"]
     gemm_tflops = cfg.gemm_flops() / (gemm_ms * 1e-3) / 1e12
     peak = PEAK[cfg.dtype]
-    kernels = {}
-    for name in STEP_NAMES:
-        by, fl = bf[name]
-        t = per[name] * 1e-3
-        kernels[name] = {"ms": round(per[name], 5), "GB/s": round(by / t / 1e9, 1),
-                         "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
-        if fl:
-            kernels[name]["TFLOP/s"] = round(fl / t / 1e12, 2)
-            kernels[name]["mfma_frac"] = round(fl / t / 1e12 / peak, 4)
     # dominant kernel: gate/up GEMM.  MFMA-bound when its flops need longer at
     # peak than its bytes at HBM peak, else HBM-bound.
-    by, fl = bf["gemm_gate_up"]
+    by, _, fl = bf["gemm_gate_up"]
     t = per["gemm_gate_up"] * 1e-3
     mfma_bound = fl / (peak * 1e12) >= by / (HBM_PEAK_GBS * 1e9)
     traffic = load_traffic("gemm_gate_up", cfg.name)
@@ -273,11 +347,24 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4), "traffic": traffic}
 
-    extra = extras(cfg, layer, x, K, stream)
-
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, layer, x, wr, bias, weights, args.cpu_seconds)
+
+    configs = None
+    if not args.no_configs:
+        configs = {cfg.name: config_summary(cfg, ms_step, per, counts)}
+        del layer, x, wr, bias, weights, out
+        torch.cuda.empty_cache()
+        for name in CONFIG_ORDER:
+            if name == cfg.name:
+                continue
+            c = synth.CONFIGS[name]
+            L, xx, _, _, _, oo = build_layer(c, dev)
+            ms_c, per_c = measure(c, L, xx, oo, 3, args.config_steps, stream)
+            configs[name] = config_summary(c, ms_c, per_c, L.counts.cpu().numpy())
+            del L, xx, oo
+            torch.cuda.empty_cache()
 
     line = {
         "metric": METRIC,
@@ -298,9 +385,10 @@ def main():
         "grouped_gemm_tflops": round(gemm_tflops, 2),
         "grouped_gemm_frac_mfma_peak": round(gemm_tflops / peak, 4),
         "kernels": kernels,
-        "extras": extra,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "configs": configs,
+        "extras": extra,
     }
     print(json.dumps(line))
 

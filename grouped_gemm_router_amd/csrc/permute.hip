@@ -109,15 +109,16 @@ __device__ __forceinline__ int block_excl_scan(int v, int *s_wave, int *total) {
 // offsets = exclusive prefix of the kept counts; ovf_start = exclusive
 // prefix of the dropped counts (where each expert's dropped entries start
 // in the overflow list); *n_overflow (if given) = all dropped entries.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_shared, int nblk,
-                                                         int cap, int32_t *__restrict__ blk,
-                                                         int32_t *__restrict__ counts,
-                                                         int32_t *__restrict__ offsets,
-                                                         int32_t *__restrict__ ovf_start,
-                                                         int32_t *__restrict__ n_overflow) {
-  __shared__ int s_wave[16];
-  __shared__ int s_part[1024];  // [r][E]: count of expert e over thread r's blocks
-  __shared__ int s_tot[MOE_MAX_EXPERTS];
+// cnt [nblk][E] holds the block counts; blk [nblk][E] receives each block's
+// exclusive prefix per expert (blk may be cnt itself).  Called by all 1024
+// threads of the workgroup.
+__device__ __forceinline__ void scan_blocks(int T, int E, int n_shared, int nblk, int cap,
+                                            const int32_t *cnt, int32_t *__restrict__ blk,
+                                            int32_t *__restrict__ counts,
+                                            int32_t *__restrict__ offsets,
+                                            int32_t *__restrict__ ovf_start,
+                                            int32_t *__restrict__ n_overflow, int *s_wave,
+                                            int *s_part, int *s_tot) {
   const int tid = threadIdx.x;
   // R threads per expert (thread r of expert e takes a contiguous run of
   // token blocks), so the per-block counts are read with many loads in
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_sha
     for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
       int c[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = (b0 + i < b_hi) ? blk[(size_t)(b0 + i) * E + e] : 0;
+      for (int i = 0; i < 16; ++i) c[i] = (b0 + i < b_hi) ? cnt[(size_t)(b0 + i) * E + e] : 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) mine += c[i];
     }
@@ -141,13 +142,13 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_sha
   __syncthreads();
   if (act) {
     // exclusive prefix of expert e over the runs before r, then the run's
-    // blocks in order (the counts are re-read from cache)
+    // blocks in order (the counts are read again)
     int run = 0;
     for (int q = 0; q < r; ++q) run += s_part[q * E + e];
     for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
       int c[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = (b0 + i < b_hi) ? blk[(size_t)(b0 + i) * E + e] : 0;
+      for (int i = 0; i < 16; ++i) c[i] = (b0 + i < b_hi) ? cnt[(size_t)(b0 + i) * E + e] : 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (b0 + i < b_hi) blk[(size_t)(b0 + i) * E + e] = run;
@@ -175,6 +176,19 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_sha
     for (int s = 0; s < n_shared; ++s) offsets[E + s + 1] = routed + (s + 1) * T;
     if (n_overflow) *n_overflow = dropped;
   }
+}
+
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int T, int E, int n_shared, int nblk,
+                                                         int cap, int32_t *__restrict__ blk,
+                                                         int32_t *__restrict__ counts,
+                                                         int32_t *__restrict__ offsets,
+                                                         int32_t *__restrict__ ovf_start,
+                                                         int32_t *__restrict__ n_overflow) {
+  __shared__ int s_wave[16];
+  __shared__ int s_part[1024];  // [r][E]: count of expert e over thread r's blocks
+  __shared__ int s_tot[MOE_MAX_EXPERTS];
+  scan_blocks(T, E, n_shared, nblk, cap, blk, blk, counts, offsets, ovf_start, n_overflow, s_wave,
+              s_part, s_tot);
 }
 
 // ---- 3. scatter + row copy ----------------------------------------------------
@@ -383,6 +397,14 @@ size_t permute_ws_bytes(int T, int k, int E) {
   return (nblk + 1) * (size_t)E * sizeof(int32_t);  // block counts, then overflow starts
 }
 
+namespace {
+hipError_t launch_scatter(const void *x, int x_dt, int T, int d, const int32_t *topk_idx, int k,
+                          int E, int n_shared, int capacity, int out_dt, void *x_perm,
+                          float *x_perm_scale, int32_t *offsets, int32_t *perm_src,
+                          int32_t *flat_to_row, int32_t *overflow, int32_t *blk,
+                          int32_t *ovf_start, hipStream_t s);
+}  // namespace
+
 hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *topk_idx, int k,
                           int E, int n_shared, int capacity, int out_dt, void *x_perm,
                           float *x_perm_scale, int32_t *counts, int32_t *offsets,
@@ -407,6 +429,17 @@ hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *
                      blk, counts, offsets, ovf_start, n_overflow);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  return launch_scatter(x, x_dt, T, d, topk_idx, k, E, n_shared, capacity, out_dt, x_perm,
+                        x_perm_scale, offsets, perm_src, flat_to_row, overflow, blk, ovf_start, s);
+}
+
+namespace {
+
+hipError_t launch_scatter(const void *x, int x_dt, int T, int d, const int32_t *topk_idx, int k,
+                          int E, int n_shared, int capacity, int out_dt, void *x_perm,
+                          float *x_perm_scale, int32_t *offsets, int32_t *perm_src,
+                          int32_t *flat_to_row, int32_t *overflow, int32_t *blk,
+                          int32_t *ovf_start, hipStream_t s) {
   const int tpb = T >= 1024 ? 4 : 1;  // tokens per scatter workgroup
   const dim3 grid((T + tpb - 1) / tpb), block(256);
   const size_t lds = sizeof(int) * (size_t)tpb * k;
@@ -425,3 +458,6 @@ hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *
 #undef MOE_SCATTER
   return hipGetLastError();
 }
+
+}  // namespace
+

@@ -38,18 +38,34 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "grouped_gemm_router_amd", "csrc")
 
 # kernel sources whose change invalidates a traffic record
+_GEMM_SOURCES = ["gemm_bf16.hip", "gemm_fp8.hip", "gemm_fp8_ring.hip", "gemm_simple.hip",
+                 "moe_internal.h"]
 KERNEL_SOURCES = {
-    "gemm_gate_up": ["gemm_bf16.hip", "gemm_fp8.hip", "gemm_fp8_ring.hip", "gemm_simple.hip",
-                     "moe_internal.h"],
-    "gemm_down": ["gemm_bf16.hip", "gemm_fp8.hip", "gemm_fp8_ring.hip", "gemm_simple.hip",
-                  "moe_internal.h"],
+    "gemm_gate_up": _GEMM_SOURCES,
+    "gemm_down": _GEMM_SOURCES,
+    "route": ["route.hip", "moe_internal.h"],
+    "permute": ["permute.hip", "moe_internal.h"],
+    "combine": ["combine.hip", "moe_internal.h"],
 }
 
-# device kernel names: the grouped GEMMs take the epilogue (SwiGLU = gate/up)
-# as their first template argument
+# device kernel names of each layer step: the grouped GEMMs take the
+# epilogue (SwiGLU = gate/up) as their first template argument; the split
+# tail's reduce kernel belongs to its GEMM; route and permute are one to
+# three kernels per call, whose counters add up per call
 KERNEL_PATTERNS = {
+    "gemm_gate_up": re.compile(r"(gemm_(bf16|fp8_ring|fp8|simple)_kernel|split_reduce_kernel)<true"),
+    "gemm_down": re.compile(r"(gemm_(bf16|fp8_ring|fp8|simple)_kernel|split_reduce_kernel)<false"),
+    "route": re.compile(r"route_"),
+    "permute": re.compile(r"perm_"),
+    "combine": re.compile(r"combine_kernel"),
+}
+# the first kernel of each call of a step (one dispatch per call)
+CALL_PATTERNS = {
     "gemm_gate_up": re.compile(r"gemm_(bf16|fp8_ring|fp8|simple)_kernel<true"),
     "gemm_down": re.compile(r"gemm_(bf16|fp8_ring|fp8|simple)_kernel<false"),
+    "route": re.compile(r"route_(small|logits)"),
+    "permute": re.compile(r"perm_rank"),
+    "combine": re.compile(r"combine_kernel"),
 }
 COPY_PATTERN = re.compile(r"copyBuffer")
 COPY_BYTES = 1 << 30
@@ -75,10 +91,29 @@ def per_dispatch(csv_path: str, counter: str, pattern) -> list[float]:
     return [vals[k] for k in sorted(vals, key=int)]
 
 
+def per_call(csv_path: str, counter: str, kernel: str) -> list[float]:
+    """Counter value of every call of a layer step: the dispatches of the
+    step's kernels (KERNEL_PATTERNS), summed over their instances and over
+    the kernels of one call; a call starts at its first kernel
+    (CALL_PATTERNS) and takes the step's dispatches up to the next start."""
+    by_disp: dict[int, list] = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and KERNEL_PATTERNS[kernel].search(row["Kernel_Name"]):
+                e = by_disp.setdefault(int(row["Dispatch_Id"]), [row["Kernel_Name"], 0.0])
+                e[1] += float(row["Counter_Value"])
+    calls = []
+    for d in sorted(by_disp):
+        name, v = by_disp[d]
+        if CALL_PATTERNS[kernel].search(name) or not calls:
+            calls.append(0.0)
+        calls[-1] += v
+    return calls
+
+
 def traffic_record(fetch_csv: str, write_csv: str, kernel: str, config: str) -> dict:
-    pat = KERNEL_PATTERNS[kernel]
-    fk = per_dispatch(fetch_csv, "FETCH_SIZE", pat)
-    wk = per_dispatch(write_csv, "WRITE_SIZE", pat)
+    fk = per_call(fetch_csv, "FETCH_SIZE", kernel)
+    wk = per_call(write_csv, "WRITE_SIZE", kernel)
     fc = per_dispatch(fetch_csv, "FETCH_SIZE", COPY_PATTERN)
     wc = per_dispatch(write_csv, "WRITE_SIZE", COPY_PATTERN)
     if not (fk and wk and fc and wc):
@@ -109,10 +144,56 @@ def traffic_record(fetch_csv: str, write_csv: str, kernel: str, config: str) -> 
 LIBRARY_KERNELS = re.compile(r"route_|perm_|gemm_|split_reduce|combine_|stats_|quantize")
 
 
+def mfma_record(pmc_csv: str, trace_csv: str, kernel: str, config: str, xcds: int = 8,
+                simds: int = 1024) -> dict:
+    """Matrix-core utilisation of one GEMM step from a counter run with
+    GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_*
+    (plus its kernel trace for the durations): per call, the median of
+      clock   = GRBM_GUI_ACTIVE (summed over the XCDs) / xcds / duration,
+      util    = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / xcds * simds),
+      flops   = SQ_INSTS_VALU_MFMA_MOPS_* * 512 (the MFMA work done, padding
+                rows included) / duration."""
+    pat = CALL_PATTERNS[kernel]
+    grbm = per_dispatch(pmc_csv, "GRBM_GUI_ACTIVE", pat)
+    busy = per_dispatch(pmc_csv, "SQ_VALU_MFMA_BUSY_CYCLES", pat)
+    mops = []
+    for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+              "SQ_INSTS_VALU_MFMA_MOPS_F32"):
+        v = per_dispatch(pmc_csv, c, pat)
+        if v:
+            mops = v
+            break
+    durs = []
+    for r in csv.DictReader(open(trace_csv)):
+        if pat.search(r["Kernel_Name"]):
+            durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    if not (grbm and busy and durs) or len(grbm) != len(durs):
+        raise ValueError("missing or unmatched dispatches: %d counters, %d durations"
+                         % (len(grbm), len(durs)))
+    clk = [g / xcds / (t * 1e-9) / 1e9 for g, t in zip(grbm, durs)]
+    util = [b / (g / xcds * simds) for b, g in zip(busy, grbm)]
+    rec = {
+        "kernel": kernel, "config": config, "source_hash": source_hash(kernel),
+        "dispatches": len(durs),
+        "duration_us_median": statistics.median(durs) / 1e3,
+        "clock_ghz_median": round(statistics.median(clk), 4),
+        "mfma_busy_fraction_median": round(statistics.median(util), 4),
+        "grbm_gui_active_median": statistics.median(grbm),
+        "mfma_busy_cycles_median": statistics.median(busy),
+    }
+    if mops and len(mops) == len(durs):
+        tf = [m * 512 / (t * 1e-9) / 1e12 for m, t in zip(mops, durs)]
+        rec["mfma_mops_median"] = statistics.median(mops)
+        rec["mfma_tflops_median"] = round(statistics.median(tf), 2)
+    return rec
+
+
 def timed_averages(trace_csv: str, last: int) -> dict:
     """Average duration (ns) of the last `last` dispatches of every kernel in
-    a rocprofv3 kernel_trace.csv (in dispatch order): the timed steps of a
-    bench run, without its warm-up calls."""
+    a rocprofv3 kernel_trace.csv (in dispatch order).  With bench.py run as
+    `--no-configs --no-extras` and `last` = its --steps these are the timed
+    loop's calls (after the per-call pass and the warm-up; the extras, when
+    run, come before all of them)."""
     per = {}
     for r in csv.DictReader(open(trace_csv)):
         per.setdefault(r["Kernel_Name"], []).append(
@@ -173,10 +254,20 @@ def main() -> None:
     p.add_argument("--trace", help="kernel_trace.csv of the same run (per dispatch)")
     p.add_argument("--timed", type=int, default=0,
                    help="with --trace: average the last this many calls of each kernel")
+    p.add_argument("--mfma", help="counter_collection.csv of a run with the MFMA counters")
     p.add_argument("--config", required=True)
     p.add_argument("--out", required=True,
                    help="traffic: output path without extension (.json); trace: the .md path")
     a = p.parse_args()
+    if a.mfma:
+        if not (a.trace and a.kernel):
+            p.error("--mfma needs --trace and --kernel")
+        rec = mfma_record(a.mfma, a.trace, a.kernel, a.config)
+        rec["command"] = a.command or ""
+        with open(a.out + ".json", "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec, indent=1))
+        return
     if a.stats:
         text = trace_summary(a.stats, a.config, a.command or "", a.trace, a.timed)
         with open(a.out, "w") as f:

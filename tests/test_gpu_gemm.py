@@ -84,9 +84,12 @@ def test_bf16_all_rows(orc, sizes, N, K, swiglu, out):
     assert_within(C.float().cpu().numpy(), ref, bound)
 
 
-@pytest.mark.parametrize("sizes", [[0, 5, 64, 65, 1], [200]])
+# fp32 operands: N % 32 == 0 takes the fp32 matrix cores (32 x 32 tiles, K
+# in chunks of 64 with a zero-padded tail: K = 40, 128, 200, 256), other N the
+# vector-ALU kernel (N = 100, 72)
+@pytest.mark.parametrize("sizes", [[0, 5, 64, 65, 1], [200], [31, 32, 33]])
 @pytest.mark.parametrize("N,K,swiglu", [(256, 128, True), (128, 256, False), (100, 40, False),
-                                        (72, 24, True)])
+                                        (72, 24, True), (64, 40, False), (96, 200, True)])
 def test_fp32_vector_path(orc, sizes, N, K, swiglu):
     A, B, B2, offs = make(sizes, N, K, torch.float32, 200 + N, swiglu)
     C = gpu_gemm(A, B, B2, offs, torch.float32, swiglu)

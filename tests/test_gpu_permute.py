@@ -48,6 +48,9 @@ CASES = [  # T, E, k, ns, d, weights
     (300, 64, 4, 2, 64, "skew"),
     (130, 32, 2, 0, 64, "empty"),
     (5000, 1024, 32, 0, 8, None),
+    # the DeepSeek routing shape; a ragged 65th block of tokens
+    (4096, 256, 8, 1, 64, None),
+    (4097, 8, 2, 0, 64, None),
 ]
 
 

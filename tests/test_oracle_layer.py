@@ -223,3 +223,53 @@ def test_fp8_layer_matches_torch_quantised_reference(orc, x_dt):
         for s in range(ns):
             ref[t] += ffn(E + s)
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-11)
+
+
+def test_bf16_expert_outputs_cannot_meet_the_bf16_bar(orc):
+    """Why the bf16 layers keep the expert outputs Y in fp32 until the
+    combine.  On the small Mixtral-shape layer of the GPU layer tests
+    (T 512, d 512, d_ff 1024, 8 experts top-2, the synthetic recipe), the
+    roundings alone -- no GEMM error at all -- cost, against the fp64 layer:
+      * Y rounded to bf16, combined in fp32 in j order, out rounded to bf16:
+        more than the 2e-2 x RMS bar;
+      * Y kept in fp32, the same combine and final rounding: well inside it.
+    The outputs are heavy-tailed (max |y| ~ 6 RMS), and one bf16 rounding of
+    an output near 6 RMS can already cost up to 2^-8 x 6 RMS ~ 0.023 RMS.
+    Rounding by torch's float32 -> bfloat16 cast (round to nearest even)."""
+    from grouped_gemm_router_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["mixtral_bf16"], name="mixtral_small", T=512, d=512,
+                       dff=1024)
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    def to_bf16(a):
+        return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).float().numpy()
+
+    x, wr = synth.gen_x(cfg, "cpu"), synth.gen_router(cfg, "cpu")
+    wg, wu, wd = synth.gen_experts(cfg, "cpu")
+    xs = bits(x)
+    idx, w, _, _ = orc.route(xs, bits(wr), cfg.k)
+    L = orc.Layer(xs, cfg.E, cfg.k, 0, [bits(a) for a in wg], [bits(a) for a in wu],
+                  [bits(a) for a in wd])
+    tok = np.arange(cfg.T)
+    Y = []   # each selected expert's output for every token, fp64
+    for j in range(cfg.k):
+        unit = np.zeros_like(w)
+        unit[:, j] = 1.0
+        Y.append(L.tokens(idx, unit, tok))
+    y = sum(w[:, j:j + 1] * Y[j] for j in range(cfg.k))
+    np.testing.assert_allclose(y, L.tokens(idx, w, tok), rtol=1e-12, atol=1e-12)
+    scale = np.sqrt(np.mean(y * y))
+
+    def combine(Ys):
+        acc = np.zeros(y.shape, np.float32)
+        for j in range(cfg.k):
+            acc = np.float32(acc + w[:, j:j + 1].astype(np.float32) * Ys[j])
+        return to_bf16(acc).astype(np.float64)
+
+    err_f32 = np.abs(combine([np.float32(v) for v in Y]) - y).max() / scale
+    err_bf16 = np.abs(combine([to_bf16(v) for v in Y]) - y).max() / scale
+    assert np.abs(y).max() / scale > 5.0
+    assert err_bf16 > 2e-2, err_bf16
+    assert err_f32 < 0.6 * 2e-2, err_f32

@@ -1,8 +1,10 @@
 """CPU checks of the profile summaries built from rocprofv3 CSVs.  Traffic
 record: the kernel and copy dispatches are told apart by name, counters are
-summed over their instances per dispatch, and the copy calibration scales
-KiB to bytes.  Trace summary: the timed column averages each kernel's last
-dispatches in dispatch order."""
+summed over their instances per dispatch and over the kernels of one call of
+a step, and the copy calibration scales KiB to bytes.  MFMA record: clock,
+busy fraction and MFMA rate from the counters and durations.  Trace summary:
+the timed column averages each kernel's last dispatches in dispatch
+order."""
 import csv
 import json
 
@@ -76,3 +78,57 @@ def test_trace_summary_timed_column(tmp_path):
     text = profiling.trace_summary(str(stats), "cfg", "cmd", str(trace), 2)
     assert "| Timed avg (us) |" in text
     assert "| `gemm_bf16_kernel<true>` | 3 | 2.00 | 1.00 | 1.00 | 4.00 |" in text
+
+
+def test_traffic_of_a_multi_kernel_step(tmp_path):
+    """A permutation call is three kernels (rank, scan, scatter) and a GEMM
+    call may add its split tail's reduce kernel: the counters of one call add
+    up, other steps' kernels in between are left out."""
+    rank, scan = "perm_rank_kernel<2>(...)", "perm_scan_kernel(...)"
+    scat, route = "perm_scatter_kernel<2, false>(...)", "route_small_bf16<1, 8>(...)"
+    gate, red = "gemm_bf16_kernel<true, false, 8>(...)", "split_reduce_kernel<true, false>(...)"
+    copy = "__amd_rocclr_copyBuffer"
+    rows = []
+    d = 0
+    for call in range(3):
+        for name, v in [(route, 7), (rank, 1), (scan, 2), (scat, 100 + call), (gate, 1000),
+                        (red, 10)]:
+            d += 1
+            rows.append((d, name, [v / 2, v / 2]))
+    rows.append((d + 1, copy, [2 ** 20]))
+    f = tmp_path / "f.csv"
+    w = tmp_path / "w.csv"
+    write_csv(f, "FETCH_SIZE", rows)
+    write_csv(w, "WRITE_SIZE", rows)
+    assert profiling.per_call(str(f), "FETCH_SIZE", "permute") == [103, 104, 105]
+    assert profiling.per_call(str(f), "FETCH_SIZE", "gemm_gate_up") == [1010] * 3
+    assert profiling.per_call(str(f), "FETCH_SIZE", "route") == [7] * 3
+    rec = profiling.traffic_record(str(f), str(w), "permute", "mixtral_bf16")
+    assert rec["fetch_bytes_per_launch"] == 104 * 1024 and rec["dispatches"] == [3, 3]
+
+
+def test_mfma_record(tmp_path):
+    """clock = GRBM_GUI_ACTIVE / XCDs / duration; busy fraction = MFMA busy
+    cycles / (cycles x SIMDs); rate = MOPS x 512 / duration."""
+    gate = "gemm_bf16_kernel<true, false, 8>(...)"
+    pmc = tmp_path / "p.csv"
+    with open(pmc, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=FIELDS)
+        wr.writeheader()
+        for disp in (1, 2):
+            for counter, vals in [("GRBM_GUI_ACTIVE", [2.0e6] * 8),
+                                  ("SQ_VALU_MFMA_BUSY_CYCLES", [0.7 * 2.0e6 * 1024]),
+                                  ("SQ_INSTS_VALU_MFMA_MOPS_BF16", [1.0e9])]:
+                for v in vals:
+                    wr.writerow({"Dispatch_Id": disp, "Kernel_Name": gate,
+                                 "Counter_Name": counter, "Counter_Value": v})
+    trace = tmp_path / "t.csv"
+    with open(trace, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Dispatch_Id", "Start_Timestamp", "End_Timestamp"])
+        for disp in (1, 2):
+            w.writerow([gate, disp, 0, 1_000_000])   # 1 ms
+    rec = profiling.mfma_record(str(pmc), str(trace), "gemm_gate_up", "mixtral_bf16")
+    assert rec["clock_ghz_median"] == pytest.approx(2.0)
+    assert rec["mfma_busy_fraction_median"] == pytest.approx(0.7)
+    assert rec["mfma_tflops_median"] == pytest.approx(512.0)
