@@ -12,7 +12,10 @@ around the whole loop, nothing else recorded inside it), after W warm-up
 steps.  Per-kernel times come from a pass of K steps before those, with HIP
 events on the launch stream around every call.  The grouped-GEMM TFLOP/s and fraction of the bf16 MFMA
 peak ride along, and `configs` repeats the measurement (fewer steps) for the
-other workloads.  HBM fractions divide the algorithmic bytes of each step
+other workloads, each also as HIP-graph replays of the five calls
+(`ms_per_step_graph`: the launch-bound workloads are set by the host-side
+cost of five calls, which a replay removes).  HBM fractions divide the
+algorithmic bytes of each step
 (bf16 expert outputs Y, as the method stores them) by the kernel time; the
 bf16 layers keep Y in fp32, whose extra bytes are reported next to them as
 `impl_bytes` / `hbm_frac_impl_bytes`.
@@ -284,7 +287,24 @@ def kernel_table(cfg, per, counts):
     return kernels, bf
 
 
-def config_summary(cfg, ms_step, per, counts):
+def measure_graph(layer, x, out, K, stream):
+    """ms per layer step when the five calls replay as one HIP graph."""
+    import torch
+    g = layer.capture(x, out)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(K):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return start.elapsed_time(end) / K
+
+
+def config_summary(cfg, ms_step, per, counts, ms_graph=None):
     kernels, _ = kernel_table(cfg, per, counts)
     gemm_ms = per["gemm_gate_up"] + per["gemm_down"]
     tf = cfg.gemm_flops() / (gemm_ms * 1e-3) / 1e12
@@ -293,6 +313,8 @@ def config_summary(cfg, ms_step, per, counts):
             "grouped_gemm_frac_mfma_peak": round(tf / PEAK[cfg.dtype], 4),
             "peak_tflops": PEAK[cfg.dtype],
             "rows_per_expert_max_over_mean": round(float(counts.max() / counts.mean()), 3),
+            "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
+            "tokens_per_s_graph": None if ms_graph is None else round(cfg.T / (ms_graph * 1e-3), 1),
             "kernels": {n: {kk: v for kk, v in r.items()
                             if kk in ("ms", "hbm_frac", "hbm_frac_impl_bytes", "mfma_frac")}
                         for n, r in kernels.items()}}
@@ -353,7 +375,8 @@ def main():
 
     configs = None
     if not args.no_configs:
-        configs = {cfg.name: config_summary(cfg, ms_step, per, counts)}
+        ms_g = measure_graph(layer, x, out, args.config_steps, stream)
+        configs = {cfg.name: config_summary(cfg, ms_step, per, counts, ms_g)}
         del layer, x, wr, bias, weights, out
         torch.cuda.empty_cache()
         for name in CONFIG_ORDER:
@@ -362,7 +385,8 @@ def main():
             c = synth.CONFIGS[name]
             L, xx, _, _, _, oo = build_layer(c, dev)
             ms_c, per_c = measure(c, L, xx, oo, 3, args.config_steps, stream)
-            configs[name] = config_summary(c, ms_c, per_c, L.counts.cpu().numpy())
+            ms_g = measure_graph(L, xx, oo, args.config_steps, stream)
+            configs[name] = config_summary(c, ms_c, per_c, L.counts.cpu().numpy(), ms_g)
             del L, xx, oo
             torch.cuda.empty_cache()
 

@@ -192,3 +192,28 @@ def test_layer_with_capacity_factor(orc, cfg_name, cf):
     if dropped.any():
         assert err[dropped].max() <= 2e-2 * scale, \
             "tokens with drops: max err %.3e vs 2e-2 x RMS %.3e" % (err[dropped].max(), scale)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "deepseek_small"])
+def test_graph_replays_match_eager(name):
+    """The five library calls captured in a HIP graph: every replay, with
+    the program's own eager work and synchronisations in between (another
+    eager forward into a second buffer, a torch op on x's copy), gives
+    bit-identical outputs to the eager forward."""
+    cfg = synth.CONFIGS[name] if name in synth.CONFIGS else \
+        next(c for c in SMALL if c.name == name)
+    layer, x, *_ = build_layer(cfg)
+    eager = layer(x).clone()
+    out = torch.empty_like(eager)
+    g = layer.capture(x, out)
+    torch.cuda.synchronize()
+    bits = torch.int32 if eager.dtype == torch.float32 else torch.int16
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(bits), eager.view(bits)), "replay %d differs" % rep
+        other = layer(x)                      # eager work between replays
+        y = (x.float() * 2.0).sum()
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(bits), eager.view(bits)) and torch.isfinite(y)
