@@ -244,6 +244,61 @@ def trace_summary(stats_csv: str, config: str, command: str, trace_csv: str = No
     return "\n".join(lines)
 
 
+TRAFFIC_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"route_|perm_|gemm_|split_reduce|combine_|"
+    "stats_|copyBuffer\" --kernel-trace --output-format csv -d $OUT/FETCH_SIZE_<cfg> -o p -- "
+    "python3 $REPO/bench.py --no-cpu-baseline --no-configs --no-extras --config <cfg> --steps 3 "
+    "--warmup 1 --calib-copy",
+    "(the same with WRITE_SIZE into $OUT/WRITE_SIZE_<cfg>)",
+    "python -m grouped_gemm_router_amd.profiling --fetch $OUT/FETCH_SIZE_<cfg>/p_counter_collection.csv "
+    "--write $OUT/WRITE_SIZE_<cfg>/p_counter_collection.csv --kernel <step> --config <cfg> "
+    "--out profiles/traffic_<step>_<cfg>",
+]
+
+
+def summary(profiles_dir: str) -> str:
+    """Markdown tables of every traffic_*.json and mfma_*.json record."""
+    import glob
+    steps = ["route", "permute", "gemm_gate_up", "gemm_down", "combine"]
+    lines = ["# Counter records of the MoE layer steps", "",
+             "## HBM traffic (FETCH_SIZE + WRITE_SIZE, per launch)", "",
+             "Two counter runs per workload (from /tmp, `$REPO` = repository root, `$OUT` a "
+             "scratch folder), then one record per step:", "", "```"] + TRAFFIC_COMMANDS + [
+             "```", "",
+             "Counters are KiB per dispatch, scaled by what they read for the plain 1 GiB copy "
+             "that `--calib-copy` runs in the same process; the median over the 7 calls of the "
+             "run (3 of the per-call timing pass, 1 warm-up, 3 timed).  A step of several "
+             "kernels (route, permute, a GEMM with its split-tail reduce) is summed per call.  "
+             "FETCH_SIZE counts L2 misses to the memory fabric: reads served by the 256 MB MALL "
+             "count too.  A record whose `source_hash` no longer matches the sources is stale.",
+             "", "| Workload | Step | Fetch MB | Write MB | Total MB | source hash current |",
+             "|---|---|---|---|---|---|"]
+    recs = [json.load(open(f)) for f in sorted(glob.glob(os.path.join(profiles_dir, "traffic_*.json")))]
+    recs.sort(key=lambda r: (r["config"], steps.index(r["kernel"])))
+    for r in recs:
+        lines.append("| %s | %s | %.1f | %.1f | %.1f | %s |" % (
+            r["config"], r["kernel"], r["fetch_bytes_per_launch"] / 1e6,
+            r["write_bytes_per_launch"] / 1e6, r["bytes_per_launch"] / 1e6,
+            "yes" if r["source_hash"] == source_hash(r["kernel"]) else "no"))
+    m = [json.load(open(f)) for f in sorted(glob.glob(os.path.join(profiles_dir, "mfma_*.json")))]
+    if m:
+        lines += ["", "## Matrix-core utilisation of the grouped GEMMs", "",
+                  "One counter run per workload (command in each record), "
+                  "GRBM_GUI_ACTIVE + SQ_VALU_MFMA_BUSY_CYCLES + the MFMA ops counter of the "
+                  "GEMM's type; median over the run's 7 calls.  Clock = GRBM_GUI_ACTIVE / 8 XCDs "
+                  "/ duration; busy = MFMA-busy cycles / (1024 SIMDs x those cycles); "
+                  "TFLOP/s = MFMA ops x 512 / duration (the work the matrix cores did, "
+                  "padding rows included).", "",
+                  "| Workload | GEMM | Duration (us) | Clock (GHz) | MFMA busy | MFMA TFLOP/s |",
+                  "|---|---|---|---|---|---|"]
+        m.sort(key=lambda r: (r["config"], r["kernel"]))
+        for r in m:
+            lines.append("| %s | %s | %.1f | %.3f | %.3f | %s |" % (
+                r["config"], r["kernel"], r["duration_us_median"], r["clock_ghz_median"],
+                r["mfma_busy_fraction_median"], r.get("mfma_tflops_median", "-")))
+    return "\n".join(lines) + "\n"
+
+
 def main() -> None:
     p = argparse.ArgumentParser()
     p.add_argument("--fetch", help="counter_collection.csv of the FETCH_SIZE pass")
@@ -255,10 +310,19 @@ def main() -> None:
     p.add_argument("--timed", type=int, default=0,
                    help="with --trace: average the last this many calls of each kernel")
     p.add_argument("--mfma", help="counter_collection.csv of a run with the MFMA counters")
-    p.add_argument("--config", required=True)
+    p.add_argument("--summary", help="write the markdown summary of a profiles folder")
+    p.add_argument("--config")
     p.add_argument("--out", required=True,
                    help="traffic: output path without extension (.json); trace: the .md path")
     a = p.parse_args()
+    if a.summary:
+        text = summary(a.summary)
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text)
+        return
+    if not a.config:
+        p.error("--config is required")
     if a.mfma:
         if not (a.trace and a.kernel):
             p.error("--mfma needs --trace and --kernel")

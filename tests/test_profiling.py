@@ -132,3 +132,25 @@ def test_mfma_record(tmp_path):
     assert rec["clock_ghz_median"] == pytest.approx(2.0)
     assert rec["mfma_busy_fraction_median"] == pytest.approx(0.7)
     assert rec["mfma_tflops_median"] == pytest.approx(512.0)
+
+
+def test_summary_tables(tmp_path):
+    """The summary lists every traffic and MFMA record, in MB, steps in layer
+    order, and marks a record whose source hash no longer matches."""
+    rec = {"kernel": "combine", "config": "mixtral_bf16", "source_hash": "stale",
+           "fetch_bytes_per_launch": 134_800_000, "write_bytes_per_launch": 33_600_000,
+           "bytes_per_launch": 168_400_000}
+    (tmp_path / "traffic_combine_mixtral_bf16.json").write_text(json.dumps(rec))
+    rec2 = dict(rec, kernel="route", source_hash=profiling.source_hash("route"),
+                fetch_bytes_per_launch=34_100_000, write_bytes_per_launch=100_000,
+                bytes_per_launch=34_200_000)
+    (tmp_path / "traffic_route_mixtral_bf16.json").write_text(json.dumps(rec2))
+    m = {"kernel": "gemm_gate_up", "config": "mixtral_bf16", "duration_us_median": 1587.9,
+         "clock_ghz_median": 1.703, "mfma_busy_fraction_median": 0.691,
+         "mfma_tflops_median": 1225.94}
+    (tmp_path / "mfma_gemm_gate_up_mixtral_bf16.json").write_text(json.dumps(m))
+    text = profiling.summary(str(tmp_path))
+    rows = [l for l in text.splitlines() if l.startswith("| mixtral_bf16")]
+    assert rows[0] == "| mixtral_bf16 | route | 34.1 | 0.1 | 34.2 | yes |"
+    assert rows[1] == "| mixtral_bf16 | combine | 134.8 | 33.6 | 168.4 | no |"
+    assert rows[2] == "| mixtral_bf16 | gemm_gate_up | 1587.9 | 1.703 | 0.691 | 1225.94 |"
