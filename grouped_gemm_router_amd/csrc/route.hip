@@ -537,6 +537,36 @@ __global__ __launch_bounds__(kSumBlock * ES) void route_small_f32(
   }
 }
 
+// Whole-wave maximum and sum, returned to every lane: an inclusive DPP scan
+// (row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast15 and
+// row_bcast31 across the rows) leaves the total in lane 63, which is read
+// back as a scalar -- no LDS round trip.  A lane without a source in a step
+// contributes the identity.  Must be called by a whole wave.
+#define MOE_DPP_F(v, id, ctrl, rmask)                                                   \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, (id)),  \
+                                                        __builtin_bit_cast(int, (v)),   \
+                                                        ctrl, rmask, 0xf, false))
+__device__ __forceinline__ float wave_allmax(float v) {
+  const float n = -INFINITY;
+  v = fmaxf(v, MOE_DPP_F(v, n, 0x111, 0xf));  // row_shr:1
+  v = fmaxf(v, MOE_DPP_F(v, n, 0x112, 0xf));  // row_shr:2
+  v = fmaxf(v, MOE_DPP_F(v, n, 0x114, 0xf));  // row_shr:4
+  v = fmaxf(v, MOE_DPP_F(v, n, 0x118, 0xf));  // row_shr:8
+  v = fmaxf(v, MOE_DPP_F(v, n, 0x142, 0xa));  // row_bcast:15
+  v = fmaxf(v, MOE_DPP_F(v, n, 0x143, 0xc));  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+}
+__device__ __forceinline__ float wave_allsum(float v) {
+  v += MOE_DPP_F(v, 0.f, 0x111, 0xf);
+  v += MOE_DPP_F(v, 0.f, 0x112, 0xf);
+  v += MOE_DPP_F(v, 0.f, 0x114, 0xf);
+  v += MOE_DPP_F(v, 0.f, 0x118, 0xf);
+  v += MOE_DPP_F(v, 0.f, 0x142, 0xa);
+  v += MOE_DPP_F(v, 0.f, 0x143, 0xc);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+}
+#undef MOE_DPP_F
+
 // ---------------------------------------------------------------------------
 // Selection from S slices of partial logits (or from given logits, S = 1):
 // 16 tokens per workgroup of 16 waves, a wave per token (8 waves of two
@@ -608,37 +638,43 @@ __global__ __launch_bounds__(kSumBlock / sel_tpw(NPER) * kWave) void route_selec
     }
     mx = fmaxf(mx, v[i]);
   }
-  mx = seg_max<kWave>(mx);
+  mx = wave_allmax(mx);
   float z = 0.f;
 #pragma unroll
   for (int i = 0; i < NPER; ++i)
     if (ok[i]) z += expf(v[i] - mx);
-  z = seg_sum<kWave>(z);
+  z = wave_allsum(z);
+  // k rounds: every lane offers its best expert not yet taken (ascending
+  // index with a strict >, so its lowest index among equal logits), the
+  // wave takes the largest offer and, among equal offers, the lowest lane:
+  // a lane's experts are contiguous, so that is the lowest expert index.
+  // Round j's logit and expert end up in lane j.
   uint32_t taken = 0;
-  float my_w = 0.f;
+  float my_v = -INFINITY;
   int my_idx = 0;
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
-    int be = 0x7fffffff;
+    int bi = -1;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) {  // ascending e: a tie keeps the lower index
-      if (ok[i] && !((taken >> i) & 1u) && v[i] > bv) {
+    for (int i = 0; i < NPER; ++i) {
+      if (ok[i] && !((taken >> i) & 1u) && (bi < 0 || v[i] > bv)) {
         bv = v[i];
-        be = e0 + i;
+        bi = i;
       }
     }
-    seg_argmax<kWave>(bv, be);
-    if (be >= e0 && be < e0 + NPER) taken |= 1u << (be - e0);
+    const float m = wave_allmax(bv);
+    const unsigned long long offers = __ballot(bi >= 0 && bv == m);
+    // no offer at all only in a wave past the last token (nothing is stored)
+    const int wl = offers ? __builtin_ctzll(offers) : 0;
+    const int we = __builtin_amdgcn_readlane(e0 + bi, wl);
+    if (offers && lane == wl) taken |= 1u << bi;
     if (lane == j) {
-      my_idx = be;
-      my_w = expf(bv - mx) / z;
+      my_v = m;
+      my_idx = we;
     }
   }
-  if (renorm) {
-    float sw = lane < k ? my_w : 0.f;
-    sw = seg_sum<kWave>(sw);
-    my_w = my_w / sw;
-  }
+  float my_w = lane < k ? expf(my_v - mx) / z : 0.f;
+  if (renorm) my_w = my_w / wave_allsum(my_w);
   if (tok && lane < k) {
     topk_idx[(size_t)t * k + lane] = my_idx;
     topk_w[(size_t)t * k + lane] = my_w;
