@@ -7,7 +7,12 @@
 // "DeepGEMM walkthrough" §4.3: tokens of one expert laid out contiguously
 // turn expert compute into a list of contiguous GEMMs.
 //
-// Three launches, all deterministic (no order-dependent atomics):
+// Up to T*k = 16384 entries with bf16 / fp32 rows, one launch
+// (perm_fused_kernel below: every workgroup histograms all entries itself,
+// so none waits for another); beyond that, and for E4M3 rows (whose
+// quantising copy needs more registers than a 1024-thread workgroup
+// leaves), three launches.  All deterministic (counts are sums, ranks
+// come from flat order, never from the order of atomics):
 //   1. rank     one wave per block of 64 tokens: each lane (token) ORs its
 //               k experts into a per-expert 64-bit LDS bitmap; the rank of
 //               (t, j) inside the block is popcount(bitmap & lanes-below);
@@ -205,43 +210,18 @@ __device__ __forceinline__ float group_max8(float v) {
   return v;
 }
 
+// Row copy of tokens [t0, t1): every source row is read once and stored to
+// the rows in s_row ([(t1 - t0) * k], -1 = dropped) and to its shared-expert
+// rows (shared_base + s*T + t), in 16-byte pieces; with E4M3 output each
+// 1 x 128 group is quantised on the way.  Called by the whole workgroup
+// after s_row is complete.
 template <int ESIZE, bool QUANT>
-__global__ __launch_bounds__(256) void perm_scatter_kernel(
-    const void *__restrict__ xv, int T, int d, const int32_t *__restrict__ idx, int k, int E,
-    int n_shared, int tpb, const int32_t *__restrict__ blk_base,
-    const int32_t *__restrict__ offsets, int32_t *__restrict__ perm_src,
-    int32_t *__restrict__ flat_to_row, void *__restrict__ x_perm, float *__restrict__ x_scale,
-    int cap, const int32_t *__restrict__ ovf_start, int32_t *__restrict__ overflow) {
-  extern __shared__ int s_row[];  // [tpb * k]
-  const int t0 = blockIdx.x * tpb;
-  const int t1 = min(t0 + tpb, T);
-  const int nent = (t1 - t0) * k;
-  // shared-expert rows follow the routed rows: row = offsets[E] + s*T + t
-  const size_t shared_base = (size_t)offsets[E];
+__device__ __forceinline__ void copy_rows(const void *__restrict__ xv, int T, int d, int k,
+                                          int n_shared, int t0, int t1, const int *s_row,
+                                          size_t shared_base, void *__restrict__ x_perm,
+                                          float *__restrict__ x_scale) {
   // scales are stored group-major, [d/128][rows], rows = T*k + n_shared*T
   const size_t srows = (size_t)T * (k + n_shared);
-  for (int i = threadIdx.x; i < (t1 - t0) * n_shared; i += blockDim.x) {
-    const int s = i / (t1 - t0), t = t0 + i % (t1 - t0);
-    flat_to_row[(size_t)T * k + (size_t)s * T + t] = (int32_t)(shared_base + (size_t)s * T + t);
-  }
-  for (int i = threadIdx.x; i < nent; i += blockDim.x) {
-    const size_t f = (size_t)t0 * k + i;
-    const int e = idx[f];
-    int row = -1;
-    if (e >= 0 && e < E) {
-      const int t = (int)(f / k);
-      const int r = blk_base[(size_t)(t / kBlk) * E + e] + flat_to_row[f];  // rank in expert
-      if (r < cap) {
-        row = offsets[e] + r;
-        perm_src[row] = (int32_t)f;
-      } else if (overflow) {
-        overflow[ovf_start[e] + (r - cap)] = (int32_t)f;
-      }
-    }
-    flat_to_row[f] = row;
-    s_row[i] = row;
-  }
-  __syncthreads();
   const char *x = static_cast<const char *>(xv);
   if (!QUANT) {
     // 16-byte pieces; d * ESIZE is a multiple of 16
@@ -355,6 +335,207 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
   }
 }
 
+template <int ESIZE, bool QUANT>
+__global__ __launch_bounds__(256) void perm_scatter_kernel(
+    const void *__restrict__ xv, int T, int d, const int32_t *__restrict__ idx, int k, int E,
+    int n_shared, int tpb, const int32_t *__restrict__ blk_base,
+    const int32_t *__restrict__ offsets, int32_t *__restrict__ perm_src,
+    int32_t *__restrict__ flat_to_row, void *__restrict__ x_perm, float *__restrict__ x_scale,
+    int cap, const int32_t *__restrict__ ovf_start, int32_t *__restrict__ overflow) {
+  extern __shared__ int s_row[];  // [tpb * k]
+  const int t0 = blockIdx.x * tpb;
+  const int t1 = min(t0 + tpb, T);
+  const int nent = (t1 - t0) * k;
+  // shared-expert rows follow the routed rows: row = offsets[E] + s*T + t
+  const size_t shared_base = (size_t)offsets[E];
+  for (int i = threadIdx.x; i < (t1 - t0) * n_shared; i += blockDim.x) {
+    const int s = i / (t1 - t0), t = t0 + i % (t1 - t0);
+    flat_to_row[(size_t)T * k + (size_t)s * T + t] = (int32_t)(shared_base + (size_t)s * T + t);
+  }
+  for (int i = threadIdx.x; i < nent; i += blockDim.x) {
+    const size_t f = (size_t)t0 * k + i;
+    const int e = idx[f];
+    int row = -1;
+    if (e >= 0 && e < E) {
+      const int t = (int)(f / k);
+      const int r = blk_base[(size_t)(t / kBlk) * E + e] + flat_to_row[f];  // rank in expert
+      if (r < cap) {
+        row = offsets[e] + r;
+        perm_src[row] = (int32_t)f;
+      } else if (overflow) {
+        overflow[ovf_start[e] + (r - cap)] = (int32_t)f;
+      }
+    }
+    flat_to_row[f] = row;
+    s_row[i] = row;
+  }
+  __syncthreads();
+  copy_rows<ESIZE, QUANT>(xv, T, d, k, n_shared, t0, t1, s_row, shared_base, x_perm, x_scale);
+}
+
+
+// ---- one launch: histogram + prefix + scatter (T k <= kFusedMaxEntries) ----
+// Every workgroup counts all T*k entries itself (per-wave LDS bins, so no
+// workgroup waits for another): the entries before its first token give each
+// expert's rank base for its own tokens, all of them give the counts, and
+// the exclusive prefix over experts of the kept counts gives the offsets
+// (of the dropped counts, the overflow starts).  It then ranks its own
+// entries in flat order, places them like the scatter kernel and copies its
+// rows.  Workgroup 0 writes counts, offsets and n_overflow.  Each workgroup
+// reads all of topk_idx (at most 64 KB, from L2), which is why the three
+// launches above take over for larger T*k (measured on the DeepSeek shapes,
+// T k = 32768: one launch 142 us against 130 us for the three).
+constexpr int kFusedMaxEntries = 16384;
+constexpr int kFusedThreads = 1024;  // 16 waves: the row copy needs loads in flight
+// copies of the histogram bins per workgroup (thread i counts into copy
+// i % copies): with few experts the LDS atomics of one instruction would
+// otherwise meet on a handful of addresses; [copies][2][E] stays 8 KB
+__host__ __device__ inline int fused_copies(int E) { return E <= 16 ? 64 : (E <= 256 ? 4 : 1); }
+
+// exclusive prefix of v over the workgroup's kFusedThreads threads (fixed
+// order); *total gets the sum
+__device__ __forceinline__ int fused_excl_scan(int v, int *s_wave, int *total) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  int wt;
+  const int ex = wave_exclusive_scan(v, &wt);
+  if (lane == 0) s_wave[wv] = wt;
+  __syncthreads();
+  int base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kFusedThreads / kWave; ++w) {
+    if (w < wv) base += s_wave[w];
+    all += s_wave[w];
+  }
+  __syncthreads();  // s_wave is reused by the next scan
+  *total = all;
+  return base + ex;
+}
+
+template <int ESIZE, bool QUANT>
+__global__ __launch_bounds__(kFusedThreads) void perm_fused_kernel(
+    const void *__restrict__ xv, int T, int d, const int32_t *__restrict__ idx, int k, int E,
+    int n_shared, int tpb, int cap, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ perm_src, int32_t *__restrict__ flat_to_row, void *__restrict__ x_perm,
+    float *__restrict__ x_scale, int32_t *__restrict__ overflow,
+    int32_t *__restrict__ n_overflow) {
+  constexpr int NW = kFusedThreads / kWave;
+  extern __shared__ int s_mem[];
+  // bins: cp copies of [2][E] (entries before t0, entries from t0 on)
+  const int cp = fused_copies(E);
+  int *bins = s_mem;
+  int *s_base = bins + cp * 2 * E;       // [E] entries of expert e before t0
+  int *s_off = s_base + E;               // [E] offsets
+  int *s_ovf = s_off + E;                // [E] overflow starts
+  int *s_e = s_ovf + E;                  // [tpb * k] the workgroup's expert ids
+  int *s_row = s_e + tpb * k;            // [tpb * k] their rows
+  __shared__ int s_wave[NW];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * tpb;
+  const int t1 = min(t0 + tpb, T);
+  const int nent = (t1 - t0) * k;
+  const int nall = T * k, nbefore = t0 * k;
+  for (int i = tid; i < cp * 2 * E; i += kFusedThreads) bins[i] = 0;
+  for (int i = tid; i < nent; i += kFusedThreads) s_e[i] = idx[(size_t)nbefore + i];
+  __syncthreads();
+  int *mb = bins + (tid % cp) * 2 * E;
+  auto count = [&](int f, int e) {
+    if (e >= 0 && e < E) atomicAdd(&mb[(f < nbefore ? 0 : E) + e], 1);
+  };
+  // histogram of all entries: 16-byte loads (four entries) when idx is
+  // 16-byte aligned, up to sixteen of them in flight per thread
+  int done = 0;
+  if ((reinterpret_cast<uintptr_t>(idx) & 15) == 0) {
+    const int ng = nall / 4;
+    const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
+    for (int g0 = tid; g0 < ng; g0 += 16 * kFusedThreads) {
+      int4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = idx4[min(g0 + u * kFusedThreads, ng - 1)];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int g = g0 + u * kFusedThreads;
+        if (g < ng) {
+          count(4 * g, v[u].x);
+          count(4 * g + 1, v[u].y);
+          count(4 * g + 2, v[u].z);
+          count(4 * g + 3, v[u].w);
+        }
+      }
+    }
+    done = 4 * ng;
+  }
+  for (int f0 = done + tid; f0 < nall; f0 += 8 * kFusedThreads) {
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ev[u] = idx[min(f0 + u * kFusedThreads, nall - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (f0 + u * kFusedThreads < nall) count(f0 + u * kFusedThreads, ev[u]);
+  }
+  __syncthreads();
+  // thread i owns experts [i * per, i * per + per): totals, kept and dropped
+  const int per = (E + kFusedThreads - 1) / kFusedThreads;
+  const int e_lo = min(E, tid * per), e_hi = min(E, e_lo + per);
+  int kept_sum = 0, drop_sum = 0;
+  for (int e = e_lo; e < e_hi; ++e) {
+    int before = 0, after = 0;
+    for (int w = 0; w < cp; ++w) {
+      before += bins[w * 2 * E + e];
+      after += bins[w * 2 * E + E + e];
+    }
+    const int total = before + after;
+    s_base[e] = before;
+    s_off[e] = total;  // the total, until the prefix below replaces it
+    kept_sum += min(total, cap);
+    drop_sum += total - min(total, cap);
+  }
+  int routed, dropped;
+  int ko = fused_excl_scan(kept_sum, s_wave, &routed);
+  int dro = fused_excl_scan(drop_sum, s_wave, &dropped);
+  for (int e = e_lo; e < e_hi; ++e) {
+    const int total = s_off[e], kept = min(total, cap);
+    if (blockIdx.x == 0) {
+      counts[e] = total;
+      offsets[e] = ko;
+    }
+    s_off[e] = ko;
+    s_ovf[e] = dro;
+    ko += kept;
+    dro += total - kept;
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    offsets[E] = routed;
+    for (int sh = 0; sh < n_shared; ++sh) offsets[E + sh + 1] = routed + (sh + 1) * T;
+    if (n_overflow) *n_overflow = dropped;
+  }
+  __syncthreads();
+  // the workgroup's own entries: rank = entries of the same expert before
+  // t0, plus those before it in flat order inside the workgroup
+  const size_t shared_base = (size_t)routed;
+  for (int i = tid; i < (t1 - t0) * n_shared; i += kFusedThreads) {
+    const int sh = i / (t1 - t0), t = t0 + i % (t1 - t0);
+    flat_to_row[(size_t)T * k + (size_t)sh * T + t] = (int32_t)(shared_base + (size_t)sh * T + t);
+  }
+  for (int i = tid; i < nent; i += kFusedThreads) {
+    const int e = s_e[i];
+    const size_t f = (size_t)nbefore + i;
+    int row = -1;
+    if (e >= 0 && e < E) {
+      int r = s_base[e];
+      for (int j = 0; j < i; ++j) r += s_e[j] == e;
+      if (r < cap) {
+        row = s_off[e] + r;
+        perm_src[row] = (int32_t)f;
+      } else if (overflow) {
+        overflow[s_ovf[e] + (r - cap)] = (int32_t)f;
+      }
+    }
+    flat_to_row[f] = row;
+    s_row[i] = row;
+  }
+  __syncthreads();
+  copy_rows<ESIZE, QUANT>(xv, T, d, k, n_shared, t0, t1, s_row, shared_base, x_perm, x_scale);
+}
 
 // Library-owned scratch of moe_permute_noalloc (the per-block counts and
 // overflow starts that moe_permute keeps in its workspace), one copy per GPU
@@ -410,6 +591,22 @@ hipError_t launch_permute(const void *x, int x_dt, int T, int d, const int32_t *
                           float *x_perm_scale, int32_t *counts, int32_t *offsets,
                           int32_t *perm_src, int32_t *flat_to_row, int32_t *overflow,
                           int32_t *n_overflow, void *ws, hipStream_t s) {
+  if ((long long)T * k <= kFusedMaxEntries && out_dt != MOE_E4M3) {
+    // tokens per workgroup: 16 once there are 256 workgroups' worth, fewer
+    // below (one per workgroup under 512 tokens)
+    const int tpb = max(1, min(16, T / 256));
+    const dim3 grid((T + tpb - 1) / tpb), block(kFusedThreads);
+    const size_t lds = sizeof(int) * ((size_t)fused_copies(E) * 2 * E + 3 * (size_t)E +
+                                      2 * (size_t)tpb * k);
+#define MOE_FUSED(ES)                                                                        \
+  hipLaunchKernelGGL((perm_fused_kernel<ES, false>), grid, block, lds, s, x, T, d, topk_idx, k, \
+                     E, n_shared, tpb, capacity, counts, offsets, perm_src, flat_to_row, x_perm, \
+                     x_perm_scale, overflow, n_overflow)
+    if (x_dt == MOE_BF16) MOE_FUSED(2);
+    else MOE_FUSED(4);
+#undef MOE_FUSED
+    return hipGetLastError();
+  }
   const int nblk = (T + kBlk - 1) / kBlk;
   int32_t *blk = static_cast<int32_t *>(ws);
   int32_t *ovf_start = blk + (size_t)nblk * E;

@@ -48,9 +48,15 @@ CASES = [  # T, E, k, ns, d, weights
     (300, 64, 4, 2, 64, "skew"),
     (130, 32, 2, 0, 64, "empty"),
     (5000, 1024, 32, 0, 8, None),
-    # the DeepSeek routing shape; a ragged 65th block of tokens
-    (4096, 256, 8, 1, 64, None),
+    # one launch up to T k = 16384 entries: a ragged last workgroup; the limit
     (4097, 8, 2, 0, 64, None),
+    (2048, 64, 8, 1, 64, None),
+    # past the limit, three launches (rank, scan, scatter): one entry past
+    # it, the DeepSeek routing shape, a ragged 65th block of tokens
+    (2049, 64, 8, 0, 64, None),
+    (4096, 256, 8, 1, 64, None),
+    (4097, 256, 8, 1, 64, None),
+    (20000, 8, 2, 0, 64, "skew"),
 ]
 
 
@@ -90,7 +96,8 @@ def test_permute_bit_exact(orc, T, E, k, ns, d, kind, dt):
 
 
 @pytest.mark.parametrize("T,E,k,ns,d", [(70, 8, 2, 0, 256), (300, 256, 8, 1, 512),
-                                        (4096, 8, 2, 0, 128), (5, 3, 3, 2, 1024)])
+                                        (4096, 8, 2, 0, 128), (5, 3, 3, 2, 1024),
+                                        (9000, 8, 4, 1, 128)])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_permute_fp8_quantisation_bit_exact(orc, T, E, k, ns, d, dt):
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
@@ -106,6 +113,24 @@ def test_permute_fp8_quantisation_bit_exact(orc, T, E, k, ns, d, dt):
     src_tok = np.concatenate([rp // k, np.tile(np.arange(T), ns)])
     np.testing.assert_array_equal(x_perm.cpu().numpy(), qref[src_tok])
     np.testing.assert_array_equal(scale.cpu().numpy(), sref[src_tok])
+
+
+@pytest.mark.parametrize("T,E,k", [(300, 8, 2), (999, 64, 8), (4097, 256, 8)])
+def test_index_array_without_16_byte_alignment(T, E, k):
+    """topk_idx at a 4-byte but not 16-byte aligned address (the one-launch
+    path then reads it entry by entry) gives the same result as an aligned
+    copy, bit for bit."""
+    x = synth.randn((T, 128), 1.0, 5 + T, DEV, torch.bfloat16)
+    idx = synth.random_selection(T, E, k, s=6 + T).to(DEV)
+    buf = torch.empty((T * k + 4,), dtype=torch.int32, device=DEV)
+    odd = buf[1: 1 + T * k].view(T, k)
+    odd.copy_(idx)
+    assert odd.data_ptr() % 16 == 4
+    ref = run_permute(x, idx, E, 1)
+    got = run_permute(x, odd, E, 1)
+    for u, v in zip(ref, got):
+        if u is not None:
+            assert torch.equal(u, v)
 
 
 def test_dropped_entries_stay_in_bounds(orc):
@@ -175,6 +200,8 @@ CAPPED = [  # T, E, k, ns, d, kind, capacity
     (777, 16, 16, 0, 64, None, 0),            # everything routed is dropped
     (130, 32, 2, 2, 64, "empty", 5),
     (200, 8, 2, 0, 64, None, 200),            # cap >= T: the drop-less result
+    (20000, 8, 2, 0, 64, "skew", 4000),       # three launches
+    (4097, 256, 8, 1, 64, None, 100),         # three launches, ragged last block
 ]
 
 

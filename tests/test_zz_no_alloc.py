@@ -4,7 +4,9 @@ instead of a caller workspace.  Called through the C ABI, its outputs must be
 bit-identical to moe_permute's (same inputs, a caller workspace) -- rows,
 E4M3 codes and scales, counts, offsets and both index maps -- on calls in a
 row that reuse the scratch, each later one smaller than the one before, up to
-the largest size the scratch allows."""
+the largest size the scratch allows.  The scratch holds the block counts of
+the three-launch path (T k above the one-launch limit of 32768 entries);
+the last calls take the one-launch path, which needs no scratch."""
 import pytest
 import torch
 
@@ -64,6 +66,8 @@ def test_noalloc_matches_permute_on_calls_in_a_row(fp8):
     # ((T/64 + 1) * E * 4 bytes of block counts and overflow starts)
     assert api.moe_permute_workspace_size(65472, 8, 256) <= api.PERMUTE_NOALLOC_SCRATCH_BYTES
     call_pair(65472, 128, 256, 8, 1, fp8, 11)
+    # smaller, still three launches: the scratch left by the first call is reused
+    call_pair(20000, 128, 64, 4, 0, fp8, 14)
     call_pair(4096, 7168 if fp8 else 4096, 256 if fp8 else 8, 8 if fp8 else 2, 1 if fp8 else 0,
               fp8, 12)
     call_pair(300, 1024, 64, 4, 1, fp8, 13)
