@@ -157,7 +157,10 @@ size_t moe_permute_workspace_size(int T, int k, int E);
  * flat_to_row is -1 and no row is written for it; the rows stay compact
  * (offsets[E] is then below T*k).  Requires d % 8 == 0.
  * ws must hold moe_permute_workspace_size(T, k, E) bytes (else
- * MOE_ERR_WORKSPACE).
+ * MOE_ERR_WORKSPACE).  It holds per-block counts when the call runs as
+ * three launches (T*k above 16384 entries, or E4M3 rows); a call of at most
+ * 16384 entries with bf16 / fp32 rows runs as one launch and leaves ws
+ * untouched.  Either way the results are the same, bit for bit.
  */
 moe_status_t moe_permute(const void *x, moe_dtype_t x_dt, int T, int d,
                          const int32_t *topk_idx, int k, int E, int n_shared,
@@ -174,10 +177,10 @@ moe_status_t moe_permute(const void *x, moe_dtype_t x_dt, int T, int d,
  * allocate device memory at call time: code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation.  Same arguments (minus
  * ws / ws_bytes), same results, same kernels as moe_permute.
- * The per-block counts that moe_permute keeps in its workspace live instead
- * in a library-owned static device array of MOE_PERMUTE_NOALLOC_SCRATCH_BYTES
- * bytes, one per GPU, held until the process ends; this call itself calls
- * no allocator.  Sizes whose moe_permute_workspace_size(T, k, E) exceeds that
+ * The per-block counts that moe_permute keeps in its workspace (three-launch
+ * sizes) live instead in a library-owned static device array of
+ * MOE_PERMUTE_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held until the
+ * process ends; this call itself calls no allocator.  Sizes whose moe_permute_workspace_size(T, k, E) exceeds that
  * limit return MOE_ERR_WORKSPACE and launch nothing (the limit allows, e.g.,
  * T up to 65472 at E = 256 and T up to 16320 at E = 1024).
  * Every call on one GPU shares that GPU's array, which keeps the last call's
