@@ -64,7 +64,7 @@ CALL_PATTERNS = {
     "gemm_gate_up": re.compile(r"gemm_(bf16|fp8_ring|fp8|simple)_kernel<true"),
     "gemm_down": re.compile(r"gemm_(bf16|fp8_ring|fp8|simple)_kernel<false"),
     "route": re.compile(r"route_(small|logits)"),
-    "permute": re.compile(r"perm_rank"),
+    "permute": re.compile(r"perm_(rank|fused)"),
     "combine": re.compile(r"combine_kernel"),
 }
 COPY_PATTERN = re.compile(r"copyBuffer")
@@ -266,8 +266,8 @@ def summary(profiles_dir: str) -> str:
              "scratch folder), then one record per step:", "", "```"] + TRAFFIC_COMMANDS + [
              "```", "",
              "Counters are KiB per dispatch, scaled by what they read for the plain 1 GiB copy "
-             "that `--calib-copy` runs in the same process; the median over the 7 calls of the "
-             "run (3 of the per-call timing pass, 1 warm-up, 3 timed).  A step of several "
+             "that `--calib-copy` runs in the same process; the median over the 8 calls of the "
+             "run (1 untimed, 3 of the per-call timing pass, 1 warm-up, 3 timed).  A step of several "
              "kernels (route, permute, a GEMM with its split-tail reduce) is summed per call.  "
              "FETCH_SIZE counts L2 misses to the memory fabric: reads served by the 256 MB MALL "
              "count too.  A record whose `source_hash` no longer matches the sources is stale.",
@@ -285,7 +285,7 @@ def summary(profiles_dir: str) -> str:
         lines += ["", "## Matrix-core utilisation of the grouped GEMMs", "",
                   "One counter run per workload (command in each record), "
                   "GRBM_GUI_ACTIVE + SQ_VALU_MFMA_BUSY_CYCLES + the MFMA ops counter of the "
-                  "GEMM's type; median over the run's 7 calls.  Clock = GRBM_GUI_ACTIVE / 8 XCDs "
+                  "GEMM's type; median over the run's 8 calls.  Clock = GRBM_GUI_ACTIVE / 8 XCDs "
                   "/ duration; busy = MFMA-busy cycles / (1024 SIMDs x those cycles); "
                   "TFLOP/s = MFMA ops x 512 / duration (the work the matrix cores did, "
                   "padding rows included).", "",

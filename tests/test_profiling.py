@@ -154,3 +154,13 @@ def test_summary_tables(tmp_path):
     assert rows[0] == "| mixtral_bf16 | route | 34.1 | 0.1 | 34.2 | yes |"
     assert rows[1] == "| mixtral_bf16 | combine | 134.8 | 33.6 | 168.4 | no |"
     assert rows[2] == "| mixtral_bf16 | gemm_gate_up | 1587.9 | 1.703 | 0.691 | 1225.94 |"
+
+
+def test_one_launch_permute_calls_are_counted_apart(tmp_path):
+    """The one-launch permutation kernel starts a call of its own, so its
+    dispatches are not summed into one."""
+    fused = "perm_fused_kernel<2, false>(...)"
+    rows = [(d + 1, fused, [50.0 + d, 50.0]) for d in range(4)]
+    f = tmp_path / "f.csv"
+    write_csv(f, "FETCH_SIZE", rows)
+    assert profiling.per_call(str(f), "FETCH_SIZE", "permute") == [100, 101, 102, 103]
