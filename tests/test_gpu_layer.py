@@ -114,6 +114,23 @@ def test_layer_small_every_token(orc, cfg):
     compare_layer(orc, cfg, np.arange(cfg.T))
 
 
+DEGENERATE = [
+    # one token; seven tokens (a ragged 16-token routing block) with every
+    # expert taking every token (k = E) and a shared expert; one expert
+    synth.scaled(synth.CONFIGS["mixtral_bf16"], name="one_token", T=1, d=256, dff=512),
+    synth.scaled(synth.CONFIGS["deepseek_bf16"], name="k_equals_e", T=7, d=256, dff=256, E=4,
+                 k=4),
+    synth.scaled(synth.CONFIGS["mixtral_bf16"], name="one_expert", T=33, d=256, dff=512, E=1,
+                 k=1),
+    synth.scaled(synth.CONFIGS["tiny_f32"], name="f32_one_token", T=1),
+]
+
+
+@pytest.mark.parametrize("cfg", DEGENERATE, ids=[c.name for c in DEGENERATE])
+def test_layer_degenerate_shapes(orc, cfg):
+    compare_layer(orc, cfg, np.arange(cfg.T))
+
+
 def test_layer_renormalised_gate(orc):
     cfg = synth.scaled(synth.CONFIGS["mixtral_bf16"], name="renorm", T=256, d=256, dff=512)
     compare_layer(orc, cfg, np.arange(cfg.T), renorm=True)
