@@ -184,7 +184,10 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
   constexpr int NR = MI + NB;                 // fragment reads per 16-deep step
   static_assert(IA >= 1 && IB >= 1, "tile too small for the wave count");
 
-  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  // the wave index is uniform: scalar, so LDS destinations (M0) and block
+  // bases need no per-use readfirstlane
+  const int tid = threadIdx.x, lane = lane_id(),
+            wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wv / NWN, wn = wv % NWN;
   int live = MI;
   if (SKIP) {
