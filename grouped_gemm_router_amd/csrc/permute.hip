@@ -7,7 +7,7 @@
 // "DeepGEMM walkthrough" §4.3: tokens of one expert laid out contiguously
 // turn expert compute into a list of contiguous GEMMs.
 //
-// Up to T*k = 16384 entries with bf16 / fp32 rows, one launch
+// Up to T*k = 32768 entries with bf16 / fp32 rows, one launch
 // (perm_fused_kernel below: every workgroup histograms all entries itself,
 // so none waits for another); beyond that, and for E4M3 rows (whose
 // quantising copy needs more registers than a 1024-thread workgroup
@@ -382,10 +382,10 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
 // (of the dropped counts, the overflow starts).  It then ranks its own
 // entries in flat order, places them like the scatter kernel and copies its
 // rows.  Workgroup 0 writes counts, offsets and n_overflow.  Each workgroup
-// reads all of topk_idx (at most 64 KB, from L2), which is why the three
+// reads all of topk_idx (at most 128 KB, from L2), which is why the three
 // launches above take over for larger T*k (measured on the DeepSeek shapes,
-// T k = 32768: one launch 142 us against 130 us for the three).
-constexpr int kFusedMaxEntries = 16384;
+// T k = 32768: one launch 128 us against 130 us for the three).
+constexpr int kFusedMaxEntries = 32768;
 constexpr int kFusedThreads = 1024;  // 16 waves: the row copy needs loads in flight
 // copies of the histogram bins per workgroup (thread i counts into copy
 // i % copies): with few experts the LDS atomics of one instruction would

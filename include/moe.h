@@ -158,8 +158,8 @@ size_t moe_permute_workspace_size(int T, int k, int E);
  * (offsets[E] is then below T*k).  Requires d % 8 == 0.
  * ws must hold moe_permute_workspace_size(T, k, E) bytes (else
  * MOE_ERR_WORKSPACE).  It holds per-block counts when the call runs as
- * three launches (T*k above 16384 entries, or E4M3 rows); a call of at most
- * 16384 entries with bf16 / fp32 rows runs as one launch and leaves ws
+ * three launches (T*k above 32768 entries, or E4M3 rows); a call of at most
+ * 32768 entries with bf16 / fp32 rows runs as one launch and leaves ws
  * untouched.  Either way the results are the same, bit for bit.
  */
 moe_status_t moe_permute(const void *x, moe_dtype_t x_dt, int T, int d,

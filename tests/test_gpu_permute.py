@@ -48,14 +48,14 @@ CASES = [  # T, E, k, ns, d, weights
     (300, 64, 4, 2, 64, "skew"),
     (130, 32, 2, 0, 64, "empty"),
     (5000, 1024, 32, 0, 8, None),
-    # one launch up to T k = 16384 entries: a ragged last workgroup; the limit
+    # one launch up to T k = 32768 entries: a ragged last workgroup; the
+    # limit (the DeepSeek routing shape)
     (4097, 8, 2, 0, 64, None),
-    (2048, 64, 8, 1, 64, None),
-    # past the limit, three launches (rank, scan, scatter): one entry past
-    # it, the DeepSeek routing shape, a ragged 65th block of tokens
-    (2049, 64, 8, 0, 64, None),
     (4096, 256, 8, 1, 64, None),
+    # past the limit, three launches (rank, scan, scatter): one entry past
+    # it, with a ragged 65th block of tokens
     (4097, 256, 8, 1, 64, None),
+    (2049, 64, 16, 0, 64, None),
     (20000, 8, 2, 0, 64, "skew"),
 ]
 
