@@ -19,7 +19,7 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH 
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_ROUTE_RENORM, MOE_ROUTE_FROM_LOGITS = 1, 2
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 EXPORTS = ["moe_status_string", "moe_abi_version", "moe_route_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute_capped", "moe_router_stats",
@@ -66,11 +66,11 @@ def _load():
     lib.moe_grouped_gemm_workspace_size.restype = sz
     lib.moe_grouped_gemm_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.moe_grouped_gemm.restype = i32
-    lib.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, vp, sz,
-                                     vp]
+    lib.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                     vp, sz, vp]
     lib.moe_grouped_gemm_fp8.restype = i32
     lib.moe_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
-                                         i32, i32, vp]
+                                         i32, i32, i32, vp]
     lib.moe_combine.restype = i32
     lib.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp]
     lib.moe_quantize_fp8.restype = i32
@@ -101,6 +101,22 @@ def _ptr(t) -> C.c_void_p:
     if not t.is_contiguous():
         raise ValueError("tensors passed to libmoe must be contiguous")
     return C.c_void_p(t.data_ptr())
+
+
+def _weights(B, B2=None):
+    """(pointer of B, pointer of B2, row pitch in elements) of [G][N][K]
+    weights whose rows may sit further apart than K (a view of [G][N][ldb]
+    storage, ldb >= K); B2, when given, must have the same shape and strides."""
+    if not isinstance(B, torch.Tensor) or B.dim() != 3:
+        raise TypeError("weights must be a [G][N][K] torch.Tensor")
+    G, N, K = B.shape
+    ldb = B.stride(1)
+    if B.stride(2) != 1 or ldb < K or B.stride(0) != N * ldb:
+        raise ValueError("weights must be [G][N][K] rows of unit stride, %s given" % (B.stride(),))
+    if B2 is not None and (B2.shape != B.shape or B2.stride() != B.stride()):
+        raise ValueError("B2 must have B's shape and strides")
+    p2 = C.c_void_p(0) if B2 is None else C.c_void_p(B2.data_ptr())
+    return C.c_void_p(B.data_ptr()), p2, ldb
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -245,10 +261,11 @@ def moe_grouped_gemm(A, B, C_out, offsets, *, B2=None, epi=MOE_EPI_NONE, ws=None
         raise ValueError("A is [rows][%d] but B is [G][N][%d]" % (K, K2))
     if offsets.numel() != G + 1:
         raise ValueError("offsets must have G + 1 = %d entries" % (G + 1))
+    pb, pb2, ldb = _weights(B, B2)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check("moe_grouped_gemm", lib.moe_grouped_gemm(_ptr(A), _ptr(B), _ptr(B2), _dt(A),
-                                                    _ptr(C_out), _dt(C_out), _ptr(offsets), G,
-                                                    rows, N, K, epi, _ptr(ws), ws_bytes,
+    _check("moe_grouped_gemm", lib.moe_grouped_gemm(_ptr(A), pb, pb2, _dt(A), _ptr(C_out),
+                                                    _dt(C_out), _ptr(offsets), G, rows, N, K,
+                                                    ldb, epi, _ptr(ws), ws_bytes,
                                                     _stream(stream)))
 
 
@@ -260,12 +277,12 @@ def moe_grouped_gemm_fp8(A_q, A_scale, B_q, B_scale, C_out, offsets, *, B2_q=Non
         raise ValueError("A_q is [rows][%d] but B_q is [G][N][%d]" % (K, K2))
     if offsets.numel() != G + 1:
         raise ValueError("offsets must have G + 1 = %d entries" % (G + 1))
+    pb, pb2, ldb = _weights(B_q, B2_q)
     c_dt = MOE_E4M3 if C_out.dtype in (torch.uint8, torch.float8_e4m3fn) else _dt(C_out)
     _check("moe_grouped_gemm_fp8",
-           lib.moe_grouped_gemm_fp8(_ptr(A_q), _ptr(A_scale), _ptr(B_q), _ptr(B_scale),
-                                    _ptr(B2_q), _ptr(B2_scale), _ptr(C_out), c_dt,
-                                    _ptr(C_scale), _ptr(offsets), G, rows, N, K, epi,
-                                    _stream(stream)))
+           lib.moe_grouped_gemm_fp8(_ptr(A_q), _ptr(A_scale), pb, _ptr(B_scale), pb2,
+                                    _ptr(B2_scale), _ptr(C_out), c_dt, _ptr(C_scale),
+                                    _ptr(offsets), G, rows, N, K, ldb, epi, _stream(stream)))
 
 
 def moe_combine(Y, flat_to_row, topk_w, out, *, n_shared=0, stream=None):

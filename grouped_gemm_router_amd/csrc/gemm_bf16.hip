@@ -44,6 +44,13 @@
 //     one expert at a time (see tile_of_workgroup);
 //   * ragged tails: A rows past the group end are loaded (clamped to the
 //     buffer) and multiplied but never stored;
+//   * weight rows sit ldb >= K elements apart (B[g][n][k] at (g N + n) ldb
+//     + k): a power-of-two row pitch puts the 128-byte pieces that a tile
+//     reads at one K offset on few HBM channels, so callers streaming such
+//     weights from HBM pad them (measured alone: decode-size gate/up, 8 KB
+//     rows, 403 -> 321 us with 256 bytes of padding; DeepSeek-shape down,
+//     4 KB rows, 1852 -> 1709 us; the Mixtral-shape GEMMs, fed from L2 and
+//     the MALL, unchanged);
 //   * the last, partial round of tiles (fewer tiles than half the CUs) is
 //     cut along K into S slices when a workspace is given: each slice writes
 //     an fp32 partial tile to the workspace and a second small kernel adds the
@@ -171,7 +178,7 @@ template <int BM, bool SWIGLU, bool OUT_F32, int NW, bool SKIP>
 __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__restrict__ A,
                                          const uint16_t *__restrict__ B,
                                          const uint16_t *__restrict__ B2, void *__restrict__ C,
-                                         int rows, int N, int K, int kbeg, int KT,
+                                         int rows, int N, int K, int ldb, int kbeg, int KT,
                                          float *__restrict__ part, u32x4 *sA0, u32x4 *sA1,
                                          u32x4 *sB0, u32x4 *sB1, u32x4 *sB2) {
   constexpr int NWN = NW / 2;                 // wave columns (2 wave rows)
@@ -199,7 +206,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
   // operand double stage, 64 slots per instruction; slot s holds piece
   // swzb(row, s % 8) of row s / 8.
   const uint16_t *gb[IB];
-  const size_t goff = (size_t)tile.g * N * K + kbeg;
+  const size_t goff = (size_t)tile.g * N * ldb + kbeg;
   const uint16_t *ga[IA];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
@@ -215,9 +222,9 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
     const int p = swzb(r, sl % PIECES_B);
     if (SWIGLU) {
       const int n = tile.nt * 128 + (r & 127);
-      gb[i] = (r < 128 ? B : B2) + goff + (size_t)n * K + p * 8;
+      gb[i] = (r < 128 ? B : B2) + goff + (size_t)n * ldb + p * 8;
     } else {
-      gb[i] = B + goff + (size_t)(tile.nt * 256 + r) * K + p * 8;
+      gb[i] = B + goff + (size_t)(tile.nt * 256 + r) * ldb + p * 8;
     }
   }
   // LDS destinations of lane 0, in 16-byte units
@@ -457,7 +464,7 @@ template <bool SWIGLU, bool OUT_F32, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const uint16_t *__restrict__ B2, void *__restrict__ C, const int32_t *__restrict__ offsets,
-    int G, int rows, int N, int K, int nt_count, char *__restrict__ ws, int cus) {
+    int G, int rows, int N, int K, int ldb, int nt_count, char *__restrict__ ws, int cus) {
   // 2 A double stages (64 KB) and 3 B double stages (96 KB): all 160 KB of LDS.
   // The scheduler's result (8 ints) passes through the last B slot, which is
   // first loaded after every wave has passed the prologue barrier.
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   // Mixtral shapes.  Down-projection tiles never skip: the extra control
   // flow cost more than the saved MFMAs there.
 #define MOE_TILE(BMV, SKIPV)                                                                  \
-  run_tile<BMV, SWIGLU, OUT_F32, NW, SKIPV>(tile, A, B, B2, C, rows, N, K, kbeg, kt, part, sA0, \
+  run_tile<BMV, SWIGLU, OUT_F32, NW, SKIPV>(tile, A, B, B2, C, rows, N, K, ldb, kbeg, kt, part, sA0, \
                                             sA1, sB0, sB1, sB2)
   if (h > 128) {
     if (SWIGLU && h <= 224) MOE_TILE(256, SWIGLU); else MOE_TILE(256, false);
@@ -594,14 +601,14 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const char *__restric
 
 template <bool SWIGLU, bool OUT_F32, int NW>
 void launch_t(const void *A, const void *B, const void *B2, void *C, const int32_t *offsets,
-              int G, int rows, int N, int K, char *ws, int cus, hipStream_t s) {
+              int G, int rows, int N, int K, int ldb, char *ws, int cus, hipStream_t s) {
   const int nt = SWIGLU ? N / 128 : N / 256;
   // slices of split tiles add at most cus - 1 workgroups past the tile count
   const long long bound = (long long)host_row_tile_bound(rows, G, BM_MAX) * nt + (ws ? cus : 0);
   hipLaunchKernelGGL((gemm_bf16_kernel<SWIGLU, OUT_F32, NW>), dim3((unsigned)((bound + 7) / 8 * 8)),
                      dim3(NW * 64), 0, s, static_cast<const uint16_t *>(A),
                      static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(B2), C,
-                     offsets, G, rows, N, K, nt, ws, cus);
+                     offsets, G, rows, N, K, ldb, nt, ws, cus);
   if (ws == nullptr) return;
   hipLaunchKernelGGL((split_reduce_kernel<SWIGLU, OUT_F32>), dim3((unsigned)(kReduceWGPerCU * cus)),
                      dim3(256), 0, s,
@@ -628,16 +635,16 @@ size_t gemm_bf16_split_ws_bytes(int G, int rows, int N, int K, int epi, int cus)
 }
 
 hipError_t launch_gemm_bf16_mfma(const void *A, const void *B, const void *B2, void *C, int c_dt,
-                                 const int32_t *offsets, int G, int rows, int N, int K, int epi,
-                                 void *ws, int cus, hipStream_t s) {
+                                 const int32_t *offsets, int G, int rows, int N, int K, int ldb,
+                                 int epi, void *ws, int cus, hipStream_t s) {
   char *w = static_cast<char *>(ws);
   // wave counts measured on the Mixtral shapes: 8 for gate/up, 4 for down
   if (epi == MOE_EPI_SWIGLU) {
-    if (c_dt == MOE_F32) launch_t<true, true, 8>(A, B, B2, C, offsets, G, rows, N, K, w, cus, s);
-    else launch_t<true, false, 8>(A, B, B2, C, offsets, G, rows, N, K, w, cus, s);
+    if (c_dt == MOE_F32) launch_t<true, true, 8>(A, B, B2, C, offsets, G, rows, N, K, ldb, w, cus, s);
+    else launch_t<true, false, 8>(A, B, B2, C, offsets, G, rows, N, K, ldb, w, cus, s);
   } else {
-    if (c_dt == MOE_F32) launch_t<false, true, 4>(A, B, B2, C, offsets, G, rows, N, K, w, cus, s);
-    else launch_t<false, false, 4>(A, B, B2, C, offsets, G, rows, N, K, w, cus, s);
+    if (c_dt == MOE_F32) launch_t<false, true, 4>(A, B, B2, C, offsets, G, rows, N, K, ldb, w, cus, s);
+    else launch_t<false, false, 4>(A, B, B2, C, offsets, G, rows, N, K, ldb, w, cus, s);
   }
   return hipGetLastError();
 }

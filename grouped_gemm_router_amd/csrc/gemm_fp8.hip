@@ -47,7 +47,7 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
     const uint8_t *__restrict__ Aq, const float *__restrict__ As, const uint8_t *__restrict__ Bq,
     const float *__restrict__ Bs, const uint8_t *__restrict__ B2q,
     const float *__restrict__ B2s, void *__restrict__ C, float *__restrict__ Cs,
-    const int32_t *__restrict__ offsets, int G, int rows, int N, int K, int nt_count) {
+    const int32_t *__restrict__ offsets, int G, int rows, int N, int K, int ldb, int nt_count) {
   __shared__ u32x4 lA[2][A_PIECES];
   __shared__ u32x4 lB[2][B_PIECES];
   __shared__ __attribute__((aligned(16))) float lS[2][FBM];
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
     const int m = min(tile.m0 + lrow + 32 * i, rows - 1);
     pa[i] = Aq + (size_t)m * K + lpc * 16;
   }
-  const size_t goff = (size_t)tile.g * N * K;
+  const size_t goff = (size_t)tile.g * N * ldb;
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int r = lrow + 32 * i;
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
       n = min(tile.nt * 256 + r, N - 1);
       base = Bq;
     }
-    pb[i] = base + goff + (size_t)n * K + lpc * 16;
+    pb[i] = base + goff + (size_t)n * ldb + lpc * 16;
   }
   // activation scale row handled by this thread (threads < 128)
   const int srow = min(tile.m0 + tid, rows - 1);
@@ -277,8 +277,8 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
 
 hipError_t launch_gemm_fp8(const uint8_t *Aq, const float *As, const uint8_t *Bq, const float *Bs,
                            const uint8_t *B2q, const float *B2s, void *C, int c_dt, float *C_scale,
-                           const int32_t *offsets, int G, int rows, int N, int K, int epi,
-                           hipStream_t s) {
+                           const int32_t *offsets, int G, int rows, int N, int K, int ldb,
+                           int epi, hipStream_t s) {
   const bool swiglu = epi == MOE_EPI_SWIGLU;
   const int nt = swiglu ? N / 128 : (N + 255) / 256;
   const long long bound = (long long)host_row_tile_bound(rows, G, FBM) * nt;
@@ -287,17 +287,17 @@ hipError_t launch_gemm_fp8(const uint8_t *Aq, const float *As, const uint8_t *Bq
   if (swiglu) {
     if (f8)
       hipLaunchKernelGGL((gemm_fp8_kernel<true, true>), grid, block, 0, s, Aq, As, Bq, Bs, B2q,
-                         B2s, C, C_scale, offsets, G, rows, N, K, nt);
+                         B2s, C, C_scale, offsets, G, rows, N, K, ldb, nt);
     else
       hipLaunchKernelGGL((gemm_fp8_kernel<true, false>), grid, block, 0, s, Aq, As, Bq, Bs, B2q,
-                         B2s, C, C_scale, offsets, G, rows, N, K, nt);
+                         B2s, C, C_scale, offsets, G, rows, N, K, ldb, nt);
   } else {
     if (f8)
       hipLaunchKernelGGL((gemm_fp8_kernel<false, true>), grid, block, 0, s, Aq, As, Bq, Bs, B2q,
-                         B2s, C, C_scale, offsets, G, rows, N, K, nt);
+                         B2s, C, C_scale, offsets, G, rows, N, K, ldb, nt);
     else
       hipLaunchKernelGGL((gemm_fp8_kernel<false, false>), grid, block, 0, s, Aq, As, Bq, Bs, B2q,
-                         B2s, C, C_scale, offsets, G, rows, N, K, nt);
+                         B2s, C, C_scale, offsets, G, rows, N, K, ldb, nt);
   }
   return hipGetLastError();
 }

@@ -115,7 +115,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
                                          const uint8_t *__restrict__ B2q,
                                          const float *__restrict__ B2s, void *__restrict__ C,
                                          float *__restrict__ Cs, int rows, int N, int K,
-                                         const Ring &ring) {
+                                         int ldb, const Ring &ring) {
   constexpr int MI = BM / 64;            // 32-token blocks per wave
   constexpr int SLOTS_A2 = BM * PIECES2;
   constexpr int IA = SLOTS_A2 / NW / 64;  // A loads per wave and double step
@@ -153,14 +153,14 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
   }
   // the B tile of wave wv comes from one matrix: SwiGLU waves 0-3 fill the
   // 128 gate rows, waves 4-7 the 128 up rows
-  const uint8_t *bbase = ((SWIGLU && wvu >= NW / 2) ? B2q : Bq) + (size_t)gu * N * K;
+  const uint8_t *bbase = ((SWIGLU && wvu >= NW / 2) ? B2q : Bq) + (size_t)gu * N * ldb;
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
     const int sl = wv * (SLOTS_B2 / NW) + i * 64 + lane;
     const int r = sl / PIECES2;
     const int n = SWIGLU ? ntu * 128 + (r & 127)
                          : min(ntu * 256 + r, N - 1);  // N % 256 == 128: half tile
-    gb[i] = (uint32_t)n * (uint32_t)K + swz(r, sl % PIECES2) * 16;
+    gb[i] = (uint32_t)n * (uint32_t)ldb + swz(r, sl % PIECES2) * 16;
   }
   // activation scales [K/128][rows]: each A double step carries its block's
   // scales into the matching scale slot; wave wv loads tile rows [32 wv,
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_fp8_ring_kernel(
     const uint8_t *__restrict__ Aq, const float *__restrict__ As, const uint8_t *__restrict__ Bq,
     const float *__restrict__ Bs, const uint8_t *__restrict__ B2q,
     const float *__restrict__ B2s, void *__restrict__ C, float *__restrict__ Cs,
-    const int32_t *__restrict__ offsets, int G, int rows, int N, int K, int nt_count) {
+    const int32_t *__restrict__ offsets, int G, int rows, int N, int K, int ldb, int nt_count) {
   // 2 A and 3 B double steps and two scale slots (148 KB of LDS).  The
   // scheduler's result (8 ints) passes through B slot 2, first loaded after
   // every wave has passed the first barrier; the epilogue's row maxima live
@@ -452,28 +452,28 @@ __global__ __launch_bounds__(NTH, 1) void gemm_fp8_ring_kernel(
   const Ring ring{sA0, sA1, sB0, sB1, sB2, sS0, sS1, reinterpret_cast<float *>(sA0)};
   const int h = tile.mend - tile.m0;  // wave-uniform
   if (h == BM_MAX)
-    run_tile<BM_MAX, SWIGLU, OUT_FP8, false>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+    run_tile<BM_MAX, SWIGLU, OUT_FP8, false>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ldb, ring);
   else if (h > 128)
-    run_tile<BM_MAX, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+    run_tile<BM_MAX, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ldb, ring);
   else if (h > 64)
-    run_tile<128, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+    run_tile<128, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ldb, ring);
   else
-    run_tile<64, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ring);
+    run_tile<64, SWIGLU, OUT_FP8, true>(tile, Aq, As, Bq, Bs, B2q, B2s, C, Cs, rows, N, K, ldb, ring);
 }
 
 }  // namespace
 
-bool gemm_fp8_ring_supports(int rows, int N, int K) {
-  // per-lane source offsets are 32-bit: rows x K bytes of A and N x K bytes
+bool gemm_fp8_ring_supports(int rows, int N, int K, int ldb) {
+  // per-lane source offsets are 32-bit: rows x K bytes of A and N x ldb bytes
   // of one group's weights must stay below 4 GiB
   return K > 0 && K % (4 * BK) == 0 && N % 128 == 0 && (long long)rows * K < (1ll << 32) &&
-         (long long)N * K < (1ll << 32);
+         (long long)N * ldb < (1ll << 32);
 }
 
 hipError_t launch_gemm_fp8_ring(const uint8_t *Aq, const float *As, const uint8_t *Bq,
                                 const float *Bs, const uint8_t *B2q, const float *B2s, void *C,
                                 int c_dt, float *C_scale, const int32_t *offsets, int G,
-                                int rows, int N, int K, int epi, hipStream_t s) {
+                                int rows, int N, int K, int ldb, int epi, hipStream_t s) {
   const bool swiglu = epi == MOE_EPI_SWIGLU;
   const int nt = swiglu ? N / 128 : (N + 255) / 256;
   const long long bound = (long long)host_row_tile_bound(rows, G, BM_MAX) * nt;
@@ -482,17 +482,17 @@ hipError_t launch_gemm_fp8_ring(const uint8_t *Aq, const float *As, const uint8_
   if (swiglu) {
     if (f8)
       hipLaunchKernelGGL((gemm_fp8_ring_kernel<true, true>), grid, block, 0, s, Aq, As, Bq, Bs,
-                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, nt);
+                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, ldb, nt);
     else
       hipLaunchKernelGGL((gemm_fp8_ring_kernel<true, false>), grid, block, 0, s, Aq, As, Bq, Bs,
-                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, nt);
+                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, ldb, nt);
   } else {
     if (f8)
       hipLaunchKernelGGL((gemm_fp8_ring_kernel<false, true>), grid, block, 0, s, Aq, As, Bq, Bs,
-                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, nt);
+                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, ldb, nt);
     else
       hipLaunchKernelGGL((gemm_fp8_ring_kernel<false, false>), grid, block, 0, s, Aq, As, Bq, Bs,
-                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, nt);
+                         B2q, B2s, C, C_scale, offsets, G, rows, N, K, ldb, nt);
   }
   return hipGetLastError();
 }

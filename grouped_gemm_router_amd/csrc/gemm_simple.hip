@@ -40,7 +40,7 @@ template <int ESIZE, int OSIZE, bool SWIGLU>
 __global__ __launch_bounds__(256) void gemm_simple_kernel(
     const void *__restrict__ A, const void *__restrict__ B, const void *__restrict__ B2,
     void *__restrict__ C, const int32_t *__restrict__ offsets, int G, int rows, int N, int K,
-    int nt_count) {
+    int ldb, int nt_count) {
   __shared__ int s_x[8];
   __shared__ float As[SBK][SBM + 1];
   __shared__ float Bs[SBK][SBN + 1];
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(
   if (sc.L < 0) return;
   const Tile tile = sc.tile;
   const int n0 = tile.nt * SBN;
-  const size_t boff = (size_t)tile.g * N * K;
+  const size_t boff = (size_t)tile.g * N * ldb;
 
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   float acc[4][4], acc2[4][4];
@@ -68,8 +68,8 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(
       const int r = e / SBK, kk = e % SBK;
       const int m = tile.m0 + r, n = n0 + r, kg = k0 + kk;
       As[kk][r] = (m < tile.mend && kg < K) ? ld<ESIZE>(A, (size_t)m * K + kg) : 0.f;
-      Bs[kk][r] = (n < N && kg < K) ? ld<ESIZE>(B, boff + (size_t)n * K + kg) : 0.f;
-      if (SWIGLU) B2s[kk][r] = (n < N && kg < K) ? ld<ESIZE>(B2, boff + (size_t)n * K + kg) : 0.f;
+      Bs[kk][r] = (n < N && kg < K) ? ld<ESIZE>(B, boff + (size_t)n * ldb + kg) : 0.f;
+      if (SWIGLU) B2s[kk][r] = (n < N && kg < K) ? ld<ESIZE>(B2, boff + (size_t)n * ldb + kg) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -117,7 +117,7 @@ template <bool SWIGLU, int OSIZE>
 __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(
     const float *__restrict__ A, const float *__restrict__ B, const float *__restrict__ B2,
     void *__restrict__ C, const int32_t *__restrict__ offsets, int G, int rows, int N, int K,
-    int nt_count) {
+    int ldb, int nt_count) {
   constexpr int NB = SWIGLU ? 2 : 1;  // B operands (gate, up)
   __shared__ int s_x[8];
   __shared__ float As[FBM][FPAD];
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(
   if (sc.L < 0) return;
   const Tile tile = sc.tile;
   const int n0 = tile.nt * FBN;
-  const size_t boff = (size_t)tile.g * N * K;
+  const size_t boff = (size_t)tile.g * N * ldb;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
   f32x16 acc[NB];
 #pragma unroll
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(
       for (int b = 0; b < NB; ++b) {
         rb[b][i] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (kg < K)
-          rb[b][i] = *reinterpret_cast<const float4 *>((b ? B2 : B) + boff + (size_t)(n0 + r) * K + kg);
+          rb[b][i] = *reinterpret_cast<const float4 *>((b ? B2 : B) + boff + (size_t)(n0 + r) * ldb + kg);
       }
     }
   };
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(
 
 template <int OSIZE>
 hipError_t launch_f32_mfma(const void *A, const void *B, const void *B2, void *C,
-                           const int32_t *offsets, int G, int rows, int N, int K, int epi,
-                           hipStream_t s) {
+                           const int32_t *offsets, int G, int rows, int N, int K, int ldb,
+                           int epi, hipStream_t s) {
   const int nt = N / FBN;
   const long long bound = (long long)host_row_tile_bound(rows, G, FBM) * nt;
   const dim3 grid((unsigned)bound), block(256);
@@ -217,25 +217,25 @@ hipError_t launch_f32_mfma(const void *A, const void *B, const void *B2, void *C
               *b2 = static_cast<const float *>(B2);
   if (epi == MOE_EPI_SWIGLU)
     hipLaunchKernelGGL((gemm_f32_mfma_kernel<true, OSIZE>), grid, block, 0, s, a, b, b2, C,
-                       offsets, G, rows, N, K, nt);
+                       offsets, G, rows, N, K, ldb, nt);
   else
     hipLaunchKernelGGL((gemm_f32_mfma_kernel<false, OSIZE>), grid, block, 0, s, a, b, b2, C,
-                       offsets, G, rows, N, K, nt);
+                       offsets, G, rows, N, K, ldb, nt);
   return hipGetLastError();
 }
 
 template <int ESIZE, int OSIZE>
 hipError_t launch_t(const void *A, const void *B, const void *B2, void *C, const int32_t *offsets,
-                    int G, int rows, int N, int K, int epi, hipStream_t s) {
+                    int G, int rows, int N, int K, int ldb, int epi, hipStream_t s) {
   const int nt = (N + SBN - 1) / SBN;
   const long long bound = (long long)host_row_tile_bound(rows, G, SBM) * nt;
   const dim3 grid((unsigned)((bound + 7) / 8 * 8)), block(256);
   if (epi == MOE_EPI_SWIGLU)
     hipLaunchKernelGGL((gemm_simple_kernel<ESIZE, OSIZE, true>), grid, block, 0, s, A, B, B2, C,
-                       offsets, G, rows, N, K, nt);
+                       offsets, G, rows, N, K, ldb, nt);
   else
     hipLaunchKernelGGL((gemm_simple_kernel<ESIZE, OSIZE, false>), grid, block, 0, s, A, B, B2, C,
-                       offsets, G, rows, N, K, nt);
+                       offsets, G, rows, N, K, ldb, nt);
   return hipGetLastError();
 }
 
@@ -243,13 +243,13 @@ hipError_t launch_t(const void *A, const void *B, const void *B2, void *C, const
 
 hipError_t launch_gemm_simple(const void *A, const void *B, const void *B2, int ab_dt, void *C,
                               int c_dt, const int32_t *offsets, int G, int rows, int N, int K,
-                              int epi, hipStream_t s) {
+                              int ldb, int epi, hipStream_t s) {
   if (ab_dt == MOE_BF16)
-    return c_dt == MOE_BF16 ? launch_t<2, 2>(A, B, B2, C, offsets, G, rows, N, K, epi, s)
-                            : launch_t<2, 4>(A, B, B2, C, offsets, G, rows, N, K, epi, s);
+    return c_dt == MOE_BF16 ? launch_t<2, 2>(A, B, B2, C, offsets, G, rows, N, K, ldb, epi, s)
+                            : launch_t<2, 4>(A, B, B2, C, offsets, G, rows, N, K, ldb, epi, s);
   if (N % FBN == 0)
-    return c_dt == MOE_BF16 ? launch_f32_mfma<2>(A, B, B2, C, offsets, G, rows, N, K, epi, s)
-                            : launch_f32_mfma<4>(A, B, B2, C, offsets, G, rows, N, K, epi, s);
-  return c_dt == MOE_BF16 ? launch_t<4, 2>(A, B, B2, C, offsets, G, rows, N, K, epi, s)
-                          : launch_t<4, 4>(A, B, B2, C, offsets, G, rows, N, K, epi, s);
+    return c_dt == MOE_BF16 ? launch_f32_mfma<2>(A, B, B2, C, offsets, G, rows, N, K, ldb, epi, s)
+                            : launch_f32_mfma<4>(A, B, B2, C, offsets, G, rows, N, K, ldb, epi, s);
+  return c_dt == MOE_BF16 ? launch_t<4, 2>(A, B, B2, C, offsets, G, rows, N, K, ldb, epi, s)
+                          : launch_t<4, 4>(A, B, B2, C, offsets, G, rows, N, K, ldb, epi, s);
 }

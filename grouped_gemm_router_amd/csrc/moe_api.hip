@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 
 bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -192,16 +192,20 @@ size_t moe_grouped_gemm_workspace_size(int G, int rows, int N, int K, moe_dtype_
 
 moe_status_t moe_grouped_gemm(const void *A, const void *B, const void *B2, moe_dtype_t ab_dt,
                               void *C, moe_dtype_t c_dt, const int32_t *offsets, int G, int rows,
-                              int N, int K, moe_epilogue_t epi, void *ws, size_t ws_bytes,
-                              moe_stream_t stream) {
+                              int N, int K, int ldb, moe_epilogue_t epi, void *ws,
+                              size_t ws_bytes, moe_stream_t stream) {
   if (G < 1 || rows < 0 || N < 1 || K < 1) return MOE_ERR_INVALID;
+  if (ldb == 0) ldb = K;
+  if (ldb < K) return MOE_ERR_INVALID;
   if (G > MOE_MAX_GROUPS) return MOE_ERR_UNSUPPORTED;
   if (epi != MOE_EPI_NONE && epi != MOE_EPI_SWIGLU) return MOE_ERR_INVALID;
   if (!is_act(ab_dt) || !is_act(c_dt)) return MOE_ERR_UNSUPPORTED;
   if (K % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  // weight rows start on 16-byte boundaries like the matrices themselves
+  if ((long long)ldb * (ab_dt == MOE_BF16 ? 2 : 4) % 16 != 0) return MOE_ERR_INVALID;
   if (!aligned16(A) || !aligned16(B) || !aligned4(C) || !aligned4(offsets)) return MOE_ERR_INVALID;
   if (epi == MOE_EPI_SWIGLU ? !aligned16(B2) : B2 != nullptr) return MOE_ERR_INVALID;
-  if ((long long)G * N * K >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)G * N * ldb >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
   if (ws == nullptr && ws_bytes != 0) return MOE_ERR_INVALID;
   // the MFMA kernel writes C in 16-byte row pieces
   const bool mfma = ab_dt == MOE_BF16 && gemm_bf16_mfma_supports(N, K, epi) && aligned16(C);
@@ -219,20 +223,23 @@ moe_status_t moe_grouped_gemm(const void *A, const void *B, const void *B2, moe_
   if (rows == 0) return MOE_OK;
   const hipStream_t s = as_stream(stream);
   if (mfma)
-    return launched(launch_gemm_bf16_mfma(A, B, B2, C, c_dt, offsets, G, rows, N, K, epi,
+    return launched(launch_gemm_bf16_mfma(A, B, B2, C, c_dt, offsets, G, rows, N, K, ldb, epi,
                                           split_ws, cus, s));
-  return launched(launch_gemm_simple(A, B, B2, ab_dt, C, c_dt, offsets, G, rows, N, K, epi, s));
+  return launched(
+      launch_gemm_simple(A, B, B2, ab_dt, C, c_dt, offsets, G, rows, N, K, ldb, epi, s));
 }
 
 moe_status_t moe_grouped_gemm_fp8(const uint8_t *A_q, const float *A_scale, const uint8_t *B_q,
                                   const float *B_scale, const uint8_t *B2_q,
                                   const float *B2_scale, void *C, moe_dtype_t c_dt,
                                   float *C_scale, const int32_t *offsets, int G, int rows, int N,
-                                  int K, moe_epilogue_t epi, moe_stream_t stream) {
+                                  int K, int ldb, moe_epilogue_t epi, moe_stream_t stream) {
   if (G < 1 || rows < 0 || N < 1 || K < 1) return MOE_ERR_INVALID;
   if (G > MOE_MAX_GROUPS) return MOE_ERR_UNSUPPORTED;
   if (epi != MOE_EPI_NONE && epi != MOE_EPI_SWIGLU) return MOE_ERR_INVALID;
   if (N % 128 != 0 || K % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (ldb == 0) ldb = K;
+  if (ldb < K || ldb % 16 != 0) return MOE_ERR_INVALID;
   if (c_dt != MOE_BF16 && c_dt != MOE_E4M3) return MOE_ERR_UNSUPPORTED;
   if (!aligned16(A_q) || !aligned4(A_scale) || !aligned16(B_q) || !aligned4(B_scale) ||
       !aligned4(C) || !aligned4(offsets))
@@ -243,14 +250,14 @@ moe_status_t moe_grouped_gemm_fp8(const uint8_t *A_q, const float *A_scale, cons
     return MOE_ERR_INVALID;
   }
   if (c_dt == MOE_E4M3 ? !aligned4(C_scale) : C_scale != nullptr) return MOE_ERR_INVALID;
-  if ((long long)G * N * K >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)G * N * ldb >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
-  if (gemm_fp8_ring_supports(rows, N, K))
+  if (gemm_fp8_ring_supports(rows, N, K, ldb))
     return launched(launch_gemm_fp8_ring(A_q, A_scale, B_q, B_scale, B2_q, B2_scale, C, c_dt,
-                                         C_scale, offsets, G, rows, N, K, epi,
+                                         C_scale, offsets, G, rows, N, K, ldb, epi,
                                          as_stream(stream)));
   return launched(launch_gemm_fp8(A_q, A_scale, B_q, B_scale, B2_q, B2_scale, C, c_dt, C_scale,
-                                  offsets, G, rows, N, K, epi, as_stream(stream)));
+                                  offsets, G, rows, N, K, ldb, epi, as_stream(stream)));
 }
 
 moe_status_t moe_combine(const void *Y, moe_dtype_t y_dt, const int32_t *flat_to_row,

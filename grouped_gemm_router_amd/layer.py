@@ -16,6 +16,26 @@ import torch
 from . import api
 
 
+def padded_weights(w: torch.Tensor, pad_bytes: int = 256) -> torch.Tensor:
+    """A copy of [G][N][K] weights whose rows sit K + pad_bytes / element size
+    elements apart when a row is a power-of-two number of bytes of at least
+    4 KB (such rows stream from HBM through few memory channels), else a
+    contiguous copy.  The result is a [G][N][K] view that moe_grouped_gemm and
+    moe_grouped_gemm_fp8 take as they are.  Measured in the layer: decode-size
+    gate/up (8 KB rows) 0.35-0.36 -> 0.33 ms, DeepSeek-shape down (4 KB rows)
+    1.93-1.94 -> 1.91 ms, Mixtral shapes unchanged; the 2 KB rows of the
+    DeepSeek-shape FP8 down were 2 % slower padded, so they stay dense."""
+    G, N, K = w.shape
+    row = K * w.element_size()
+    if row < 4096 or row & (row - 1):
+        return w.contiguous()
+    ldb = K + pad_bytes // w.element_size()
+    store = torch.empty((G, N, ldb), dtype=w.dtype, device=w.device)
+    view = store[:, :, :K]
+    view.copy_(w)
+    return view
+
+
 class MoELayer:
     """Weights: w_router [E][d]; w_gate, w_up [G][dff][d]; w_down [G][d][dff]
     with G = E + n_shared (shared experts last), all on the GPU.
@@ -45,14 +65,16 @@ class MoELayer:
         self.capacity_factor = capacity_factor
         self.act_dtype = w_router.dtype
         self.device = w_router.device
+        # expert weights are stored with padded rows where that streams them
+        # faster (padded_weights); the GEMMs take the row pitch from the view
         if fp8:
             self.wg_q, self.wg_s = self._quant(w_gate)
             self.wu_q, self.wu_s = self._quant(w_up)
             self.wd_q, self.wd_s = self._quant(w_down)
         else:
-            self.w_gate = w_gate.contiguous()
-            self.w_up = w_up.contiguous()
-            self.w_down = w_down.contiguous()
+            self.w_gate = padded_weights(w_gate)
+            self.w_up = padded_weights(w_up)
+            self.w_down = padded_weights(w_down)
         self._T = None
 
     def _quant(self, w):
@@ -61,7 +83,7 @@ class MoELayer:
         s = torch.empty((G, R // 128, Cn // 128), dtype=torch.float32, device=self.device)
         api.moe_quantize_fp8(w.contiguous().view(G * R, Cn), q.view(G * R, Cn),
                              s.view(G * R // 128, Cn // 128), block_rows=128, block_cols=128)
-        return q, s
+        return padded_weights(q), s
 
     def capacity(self, T: int):
         """Rows per expert under the capacity factor (None when drop-less)."""

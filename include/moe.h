@@ -248,8 +248,16 @@ moe_status_t moe_router_stats(const float *prob_sums, const int32_t *counts, int
  *   C[r][n] = sum_k A[r][k] * B[g][n][k]                       (MOE_EPI_NONE)
  *   C[r][n] = silu(sum_k A[r][k] B[g][n][k]) * sum_k A[r][k] B2[g][n][k]
  *                                                             (MOE_EPI_SWIGLU)
- * A [rows][K], B and B2 [G][N][K] of type ab_dt (MOE_F32 or MOE_BF16),
- * accumulation in fp32, C [rows][N] of type c_dt (MOE_F32 or MOE_BF16).
+ * A [rows][K], B and B2 [G][N][ldb] of type ab_dt (MOE_F32 or MOE_BF16),
+ * of whose rows the first K elements are used (B[g][n][k] is element
+ * (g N + n) ldb + k), accumulation in fp32, C [rows][N] of type c_dt
+ * (MOE_F32 or MOE_BF16).  ldb == 0 means K; otherwise ldb >= K with ldb
+ * times the element size a multiple of 16 bytes, else MOE_ERR_INVALID.
+ * Padding matters when a weight row is a power-of-two number of bytes and
+ * the weights stream from HBM: the pieces a tile reads at one K offset then
+ * fall on few memory channels (measured with 256 bytes of padding, the GEMM
+ * alone: decode-size gate/up with 8 KB rows -20 %, DeepSeek-shape down with
+ * 4 KB rows -8 %).
  * B2 must be NULL unless epi == MOE_EPI_SWIGLU.  Rows of C outside every
  * group are not written.  offsets values are clamped to [0, rows] and read
  * as their running maximum (group g owns rows [o_g, o_{g+1}) with o_g the
@@ -270,7 +278,7 @@ moe_status_t moe_router_stats(const float *prob_sums, const int32_t *counts, int
 moe_status_t moe_grouped_gemm(const void *A, const void *B, const void *B2,
                               moe_dtype_t ab_dt, void *C, moe_dtype_t c_dt,
                               const int32_t *offsets, int G, int rows, int N,
-                              int K, moe_epilogue_t epi, void *ws,
+                              int K, int ldb, moe_epilogue_t epi, void *ws,
                               size_t ws_bytes, moe_stream_t stream);
 
 /* Workspace bytes moe_grouped_gemm may use for this shape on the current
@@ -295,6 +303,9 @@ size_t moe_grouped_gemm_workspace_size(int G, int rows, int N, int K,
  * from a division's in the last rounding), and writes C_scale
  * [N/128][rows] (group-major, like A_scale, so it feeds the next GEMM);
  * C_scale must be NULL otherwise.
+ * B_q and B2_q rows sit ldb bytes apart (B_q[g][n][k] at (g N + n) ldb + k;
+ * ldb == 0 means K; otherwise ldb >= K and ldb % 16 == 0, else
+ * MOE_ERR_INVALID; padding as for moe_grouped_gemm); the scales stay dense.
  * Requires N % 128 == 0 and K % 128 == 0.
  */
 moe_status_t moe_grouped_gemm_fp8(const uint8_t *A_q, const float *A_scale,
@@ -302,7 +313,7 @@ moe_status_t moe_grouped_gemm_fp8(const uint8_t *A_q, const float *A_scale,
                                   const uint8_t *B2_q, const float *B2_scale,
                                   void *C, moe_dtype_t c_dt, float *C_scale,
                                   const int32_t *offsets, int G, int rows,
-                                  int N, int K, moe_epilogue_t epi,
+                                  int N, int K, int ldb, moe_epilogue_t epi,
                                   moe_stream_t stream);
 
 /*

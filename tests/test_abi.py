@@ -38,10 +38,10 @@ def lib():
                               vp, sz, vp]
     L.moe_grouped_gemm_workspace_size.restype = sz
     L.moe_grouped_gemm_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
-    L.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, vp, sz,
-                                   vp]
+    L.moe_grouped_gemm.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                   vp, sz, vp]
     L.moe_grouped_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
-                                       i32, i32, vp]
+                                       i32, i32, i32, vp]
     L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp]
     L.moe_quantize_fp8.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
     L.moe_permute_capped.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, i32, i32, vp, vp, vp,
@@ -68,7 +68,7 @@ def test_every_declared_function_is_exported(lib):
 def test_status_strings_and_version(lib):
     for s in range(5):
         assert lib.moe_status_string(s)
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
 
 
 def test_route_validation(lib):
@@ -148,8 +148,8 @@ def test_permute_workspace_error_is_reported(lib):
 
 
 def test_gemm_validation(lib):
-    g = lambda A, B, B2, dt, cdt, G, rows, N, K, epi: lib.moe_grouped_gemm(  # noqa: E731
-        A, B, B2, dt, P, cdt, P, G, rows, N, K, epi, NUL, 0, NUL)
+    g = lambda A, B, B2, dt, cdt, G, rows, N, K, epi, ldb=0: lib.moe_grouped_gemm(  # noqa: E731
+        A, B, B2, dt, P, cdt, P, G, rows, N, K, ldb, epi, NUL, 0, NUL)
     assert g(P, P, NUL, BF16, BF16, 0, 10, 256, 64, 0) == INVALID        # G < 1
     assert g(P, P, NUL, BF16, BF16, 5000, 10, 256, 64, 0) == UNSUPPORTED  # G > max
     assert g(P, P, NUL, BF16, BF16, 2, 10, 256, 60, 0) == UNSUPPORTED    # K % 8
@@ -159,8 +159,15 @@ def test_gemm_validation(lib):
     assert g(P, P, NUL, BF16, BF16, 2, 10, 256, 64, 7) == INVALID        # bad epilogue
     assert g(MIS, P, NUL, BF16, BF16, 2, 10, 256, 64, 0) == INVALID
     assert g(P, P, NUL, BF16, BF16, 2, 0, 256, 64, 0) == OK              # no rows: no-op
+    # weight row pitch: at least K, rows 16-byte aligned
+    assert g(P, P, NUL, BF16, BF16, 2, 10, 256, 64, 0, 56) == INVALID    # ldb < K
+    assert g(P, P, NUL, BF16, BF16, 2, 10, 256, 64, 0, -8) == INVALID
+    assert g(P, P, NUL, BF16, BF16, 2, 10, 256, 64, 0, 68) == INVALID    # 136-byte rows
+    assert g(P, P, NUL, F32, F32, 2, 10, 256, 64, 0, 66) == INVALID      # 264-byte rows
+    assert g(P, P, NUL, BF16, BF16, 2, 0, 256, 64, 0, 72) == OK          # 144-byte rows
+    assert g(P, P, NUL, F32, F32, 2, 0, 256, 64, 0, 68) == OK            # 272-byte rows
     # a workspace size without a workspace
-    assert lib.moe_grouped_gemm(P, P, NUL, BF16, P, BF16, P, 2, 10, 256, 64, 0, NUL, 64,
+    assert lib.moe_grouped_gemm(P, P, NUL, BF16, P, BF16, P, 2, 10, 256, 64, 0, 0, NUL, 64,
                                 NUL) == INVALID
 
 
@@ -175,8 +182,8 @@ def test_gemm_workspace_size(lib):
 
 
 def test_gemm_fp8_validation(lib):
-    f = lambda N, K, cdt, cs, b2, b2s, epi: lib.moe_grouped_gemm_fp8(  # noqa: E731
-        P, P, P, P, b2, b2s, P, cdt, cs, P, 2, 10, N, K, epi, NUL)
+    f = lambda N, K, cdt, cs, b2, b2s, epi, ldb=0, rows=10: lib.moe_grouped_gemm_fp8(  # noqa: E731
+        P, P, P, P, b2, b2s, P, cdt, cs, P, 2, rows, N, K, ldb, epi, NUL)
     assert f(200, 256, BF16, NUL, NUL, NUL, 0) == UNSUPPORTED   # N % 128
     assert f(256, 200, BF16, NUL, NUL, NUL, 0) == UNSUPPORTED   # K % 128
     assert f(256, 256, F32, NUL, NUL, NUL, 0) == UNSUPPORTED    # output dtype
@@ -184,6 +191,9 @@ def test_gemm_fp8_validation(lib):
     assert f(256, 256, BF16, P, NUL, NUL, 0) == INVALID         # scales only for fp8 output
     assert f(256, 256, BF16, NUL, NUL, NUL, 1) == INVALID       # SwiGLU needs B2
     assert f(256, 256, BF16, NUL, P, P, 0) == INVALID           # B2 without SwiGLU
+    assert f(256, 256, BF16, NUL, NUL, NUL, 0, 128) == INVALID  # ldb < K
+    assert f(256, 256, BF16, NUL, NUL, NUL, 0, 264) == INVALID  # rows not 16-byte aligned
+    assert f(256, 256, BF16, NUL, NUL, NUL, 0, 512, 0) == OK    # padded rows, nothing to do
 
 
 def test_combine_and_quant_validation(lib):
@@ -221,3 +231,23 @@ def test_router_stats_validation(lib):
     assert s(4096, 256, 8, MIS) == INVALID
     assert s(4096, 256, 8, NUL) == INVALID
     assert s(0, 256, 8) == OK             # T == 0: nothing launched
+
+
+def test_padded_weights_layout():
+    """Host logic of the layer's weight storage: rows of a power-of-two size
+    of at least 4 KB get 256 bytes of padding (the GEMMs read the pitch from
+    the view's strides), other rows stay contiguous; values are unchanged."""
+    import torch
+    from grouped_gemm_router_amd.layer import padded_weights
+    cases = [((2, 3, 4096), torch.bfloat16, 4096 + 128),   # 8 KB rows
+             ((2, 3, 2048), torch.bfloat16, 2048 + 128),   # 4 KB rows
+             ((2, 3, 1024), torch.float32, 1024 + 64),     # 4 KB rows
+             ((2, 3, 2048), torch.uint8, 2048),            # 2 KB rows: dense
+             ((2, 3, 14336), torch.bfloat16, 14336),       # 28 KB: not a power of two
+             ((2, 3, 7168), torch.bfloat16, 7168)]
+    for shape, dt, ldb in cases:
+        n = shape[0] * shape[1] * shape[2]
+        w = torch.arange(n, dtype=torch.int32).remainder(251).to(dt).view(shape)
+        p = padded_weights(w)
+        assert p.shape == w.shape and p.stride() == (shape[1] * ldb, ldb, 1), (shape, dt)
+        assert torch.equal(p, w)

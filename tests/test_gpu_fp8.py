@@ -170,6 +170,48 @@ def test_fp8_gemm_bf16_out(orc, sizes, N, K, swiglu):
     assert_within(C.float().cpu().numpy(), ref, bound)
 
 
+def pad_rows_e4m3(Bq, pad):
+    """Bq [G][N][K] E4M3 codes as a view of [G][N][K + pad] storage whose pad
+    bytes hold the E4M3 NaN code 0x7F: a kernel that read past a row's first
+    K bytes would carry the NaN into its output."""
+    if Bq is None:
+        return None
+    G, N, K = Bq.shape
+    store = torch.full((G, N, K + pad), 0x7F, dtype=torch.uint8, device=Bq.device)
+    store[:, :, :K] = Bq
+    return store[:, :, :K]
+
+
+# Weight rows further apart than K bytes: the LDS-ring kernel (K % 256 == 0)
+# and the general one, pads of 16 to 256 bytes; the result must equal the one
+# with contiguous weights bit for bit.
+@pytest.mark.parametrize("N,K,swiglu,pad", [(256, 256, False, 16), (128, 512, True, 256),
+                                            (384, 1024, False, 128), (256, 128, True, 16),
+                                            (384, 384, False, 256)])
+def test_fp8_gemm_padded_weight_rows(orc, N, K, swiglu, pad):
+    sizes = [0, 1, 127, 129, 193, 64]
+    offs, Aq, As, Bq, Bs, B2q, B2s = make_fp8(sizes, N, K, 110 + N + pad, swiglu)
+    a = api()
+    rows = int(offs[-1])
+    dAq, dAs, dBq, dBs, dB2q, dB2s = dev_operands(Aq, As, Bq, Bs, B2q, B2s)
+    epi = a.MOE_EPI_SWIGLU if swiglu else a.MOE_EPI_NONE
+    C = torch.full((rows, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    a.moe_grouped_gemm_fp8(dAq, dAs, pad_rows_e4m3(dBq, pad), dBs, C,
+                           torch.from_numpy(offs).to(DEV), B2_q=pad_rows_e4m3(dB2q, pad),
+                           B2_scale=dB2s, epi=epi)
+    torch.cuda.synchronize()
+    ref, bound = fp8_ref_and_bound(orc, Aq.numpy(), As.numpy(), Bq.numpy(), Bs.numpy(),
+                                   None if B2q is None else B2q.numpy(),
+                                   None if B2s is None else B2s.numpy(), offs, np.arange(rows),
+                                   swiglu, 2.0 ** -8)
+    assert_within(C.float().cpu().numpy(), ref, bound)
+    C0 = torch.full((rows, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    a.moe_grouped_gemm_fp8(dAq, dAs, dBq, dBs, C0, torch.from_numpy(offs).to(DEV), B2_q=dB2q,
+                           B2_scale=dB2s, epi=epi)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C0.view(torch.int16))
+
+
 # The 1040-group limit (the scheduler's lanes hold runs of 17 groups), mostly
 # empty or tiny groups plus one of each tile height; K = 256 runs the LDS-ring
 # kernel, K = 128 the general one.

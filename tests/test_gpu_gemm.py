@@ -106,6 +106,53 @@ def test_bf16_off_grid_shape_uses_vector_path(orc):
     assert_within(C.float().cpu().numpy(), ref, bound)
 
 
+def pad_rows(B, pad):
+    """B [G][N][K] as a view of [G][N][K + pad] storage whose pad columns
+    hold NaN: a kernel that read past the first K elements of a row would
+    carry the NaN into its output."""
+    if B is None:
+        return None
+    G, N, K = B.shape
+    store = torch.full((G, N, K + pad), float("nan"), dtype=B.dtype, device=B.device)
+    store[:, :, :K] = B
+    return store[:, :, :K]
+
+
+# Weight rows further apart than K (the row pitch ldb the C ABI takes from the
+# view's strides): every kernel path -- bf16 matrix cores, fp32 matrix cores,
+# the vector-ALU kernel -- with pads of one 16-byte piece up to 256 bytes.
+@pytest.mark.parametrize("dt,N,K,swiglu,pad", [
+    ("bf16", 256, 128, False, 8), ("bf16", 256, 128, False, 128), ("bf16", 128, 256, True, 64),
+    ("bf16", 384, 128, True, 128), ("bf16", 200, 40, False, 8),
+    ("f32", 128, 256, False, 4), ("f32", 256, 128, True, 64), ("f32", 100, 40, False, 4),
+    ("f32", 72, 24, True, 12)])
+def test_padded_weight_rows(orc, dt, N, K, swiglu, pad):
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    A, B, B2, offs = make([0, 1, 127, 129, 257, 64], N, K, tdt, 300 + N + pad, swiglu)
+    Bp, B2p = pad_rows(B, pad), pad_rows(B2, pad)
+    assert Bp.stride(1) == K + pad
+    C = gpu_gemm(A, Bp, B2p, offs, tdt, swiglu)
+    ref, bound = ref_and_bound(orc, np_of(A), np_of(B), None if B2 is None else np_of(B2), offs,
+                               np.arange(A.shape[0]), swiglu, 2.0 ** -8 if dt == "bf16" else U32)
+    assert_within(C.float().cpu().numpy(), ref, bound)
+    # the same bits as with contiguous weights: the pitch changes addresses only
+    C0 = gpu_gemm(A, B, B2, offs, tdt, swiglu)
+    bits = torch.int16 if dt == "bf16" else torch.int32
+    assert torch.equal(C.view(bits), C0.view(bits))
+
+
+def test_weight_views_that_are_not_row_pitched_are_refused():
+    a = api()
+    A, B, B2, offs = make([10], 256, 64, torch.bfloat16, 5, False)
+    C = torch.empty((10, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):  # columns of a transposed matrix
+        a.moe_grouped_gemm(A, B.transpose(1, 2).contiguous().transpose(1, 2), C,
+                           torch.from_numpy(offs).to(DEV))
+    with pytest.raises(ValueError):  # B2 with another pitch than B
+        a.moe_grouped_gemm(A, pad_rows(B, 8), C, torch.from_numpy(offs).to(DEV),
+                           B2=pad_rows(B, 16), epi=a.MOE_EPI_SWIGLU)
+
+
 def test_rows_outside_groups_untouched():
     A, B, B2, offs = make([10, 20], 256, 64, torch.bfloat16, 9, False)
     a = api()

@@ -162,6 +162,26 @@ def test_decode_gate_up_split_sampled(orc):
     _sampled_check(orc, A, B, B2, offs, C, True, per_group=2)
 
 
+@pytest.mark.parametrize("sizes,N,K,swiglu,pad", [
+    ([89, 55, 41, 27, 19, 12, 9, 4], 14336, 4096, True, 128),   # decode gate/up, as the layer
+    ([300, 37, 400, 129], 256, 4096, False, 8),                  # every tile split, S = 4
+])
+def test_split_with_padded_weight_rows(orc, sizes, N, K, swiglu, pad):
+    """Split tiles with weight rows further apart than K (the layer stores
+    8 KB weight rows with 256 bytes of padding); the pad columns hold NaN,
+    so any read past a row's K elements would show in the output, and the
+    result must be bit-identical to the one with contiguous weights."""
+    from test_gpu_gemm import pad_rows
+    A, B, B2, offs = make(sizes, N, K, torch.bfloat16, 805 + pad, swiglu)
+    ws = workspace(A, B, swiglu)
+    C = run(A, pad_rows(B, pad), pad_rows(B2, pad), offs, torch.bfloat16, swiglu, ws)
+    nt = N // 128 if swiglu else N // 256
+    assert header(ws) == expected_plan(sizes, nt, K, cus())
+    _sampled_check(orc, A, B, B2, offs, C, swiglu, per_group=2)
+    C0 = run(A, B, B2, offs, torch.bfloat16, swiglu, ws)
+    assert torch.equal(C.view(torch.int16), C0.view(torch.int16))
+
+
 def test_non_monotone_offsets_stay_in_bounds(orc):
     """Offsets that go down are a caller error; the scheduler reads each
     clamped offset as the largest one up to its group, so the groups never
