@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import threading
 
 import torch
 
@@ -93,6 +94,48 @@ def _check(fn: str, status: int) -> None:
         raise MoEError(fn, status)
 
 
+_defer = threading.local()
+
+
+def _deferring() -> bool:
+    return getattr(_defer, "on", False)
+
+
+def _invoke(fn: str, cfn, *args):
+    """Call the library entry cfn with marshalled args and check the status;
+    inside deferred(), return that call as a thunk instead of making it."""
+    if _deferring():
+        def call():
+            status = cfn(*args)
+            if status != MOE_OK:
+                raise MoEError(fn, status)
+        call.entry = fn
+        return call
+    _check(fn, cfn(*args))
+    return None
+
+
+def deferred(entry, *args, **kwargs):
+    """entry(*args, **kwargs) -- one of the entry points below -- with its
+    arguments checked and marshalled now, as a thunk that makes the library
+    call (same pointers, sizes and stream: the current stream now, if none is
+    given) each time it is called.  The thunk holds the argument tensors.
+    For callers that launch the same call many times: the per-call host cost
+    is then one ctypes call.  Every buffer must be passed explicitly."""
+    _defer.on = True
+    try:
+        call = entry(*args, **kwargs)
+    finally:
+        _defer.on = False
+    if getattr(call, "entry", None) is None:
+        raise TypeError("%s is not a library call entry point" % getattr(entry, "__name__", entry))
+
+    def thunk():
+        call()
+    thunk.args = (args, kwargs)  # the argument tensors live as long as the thunk
+    return thunk
+
+
 def _ptr(t) -> C.c_void_p:
     if t is None:
         return C.c_void_p(0)
@@ -169,14 +212,17 @@ def moe_route(x, w_router, topk_idx, topk_w, *, logits=None, logit_bias=None, fl
         E = w_router.shape[0]
         dt = _dt(x)
         if ws is None:
+            if _deferring():
+                raise ValueError("moe_route under deferred() needs its workspace passed")
             ws = torch.empty(max(moe_route_workspace_size(T, d, E), 4), dtype=torch.uint8,
                              device=topk_idx.device)
         ws_bytes = ws.numel() * ws.element_size()
     if prob_sums is not None and tuple(prob_sums.shape) != (prob_sum_blocks(T), E):
         raise ValueError("prob_sums must be [ceil(T/16)][E] = [%d][%d]" % (prob_sum_blocks(T), E))
-    _check("moe_route", lib.moe_route(_ptr(x), _ptr(w_router), dt, _ptr(logit_bias), T, d, E,
-                                      k, flags, _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
-                                      _ptr(prob_sums), _ptr(ws), ws_bytes, _stream(stream)))
+    return _invoke("moe_route", lib.moe_route,
+                   _ptr(x), _ptr(w_router), dt, _ptr(logit_bias), T, d, E, k, flags, _ptr(logits),
+                   _ptr(topk_idx), _ptr(topk_w), _ptr(prob_sums), _ptr(ws), ws_bytes,
+                   _stream(stream))
 
 
 def moe_permute_workspace_size(T: int, k: int, E: int) -> int:
@@ -191,11 +237,10 @@ def moe_permute(x, topk_idx, E, n_shared, x_perm, counts, offsets, perm_src, fla
     k = topk_idx.shape[1]
     out_dt = _dt(x_perm)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check("moe_permute", lib.moe_permute(_ptr(x), _dt(x), T, d, _ptr(topk_idx), k, E, n_shared,
-                                          out_dt, _ptr(x_perm), _ptr(x_perm_scale),
-                                          _ptr(counts), _ptr(offsets), _ptr(perm_src),
-                                          _ptr(flat_to_row), _ptr(ws), ws_bytes,
-                                          _stream(stream)))
+    return _invoke("moe_permute", lib.moe_permute,
+                   _ptr(x), _dt(x), T, d, _ptr(topk_idx), k, E, n_shared, out_dt, _ptr(x_perm),
+                   _ptr(x_perm_scale), _ptr(counts), _ptr(offsets), _ptr(perm_src),
+                   _ptr(flat_to_row), _ptr(ws), ws_bytes, _stream(stream))
 
 
 PERMUTE_NOALLOC_SCRATCH_BYTES = 1 << 20
@@ -208,11 +253,10 @@ def moe_permute_noalloc(x, topk_idx, E, n_shared, x_perm, counts, offsets, perm_
     the call allocates nothing.  Calls that overlap on one GPU race."""
     T, d = x.shape
     k = topk_idx.shape[1]
-    _check("moe_permute_noalloc",
-           lib.moe_permute_noalloc(_ptr(x), _dt(x), T, d, _ptr(topk_idx), k, E, n_shared,
-                                   _dt(x_perm), _ptr(x_perm), _ptr(x_perm_scale), _ptr(counts),
-                                   _ptr(offsets), _ptr(perm_src), _ptr(flat_to_row),
-                                   _stream(stream)))
+    return _invoke("moe_permute_noalloc", lib.moe_permute_noalloc,
+                   _ptr(x), _dt(x), T, d, _ptr(topk_idx), k, E, n_shared, _dt(x_perm),
+                   _ptr(x_perm), _ptr(x_perm_scale), _ptr(counts), _ptr(offsets), _ptr(perm_src),
+                   _ptr(flat_to_row), _stream(stream))
 
 
 def moe_permute_capped(x, topk_idx, E, n_shared, capacity, x_perm, counts, offsets, perm_src,
@@ -224,12 +268,11 @@ def moe_permute_capped(x, topk_idx, E, n_shared, capacity, x_perm, counts, offse
     T, d = x.shape
     k = topk_idx.shape[1]
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check("moe_permute_capped",
-           lib.moe_permute_capped(_ptr(x), _dt(x), T, d, _ptr(topk_idx), k, E, n_shared,
-                                  int(capacity), _dt(x_perm), _ptr(x_perm), _ptr(x_perm_scale),
-                                  _ptr(counts), _ptr(offsets), _ptr(perm_src),
-                                  _ptr(flat_to_row), _ptr(overflow), _ptr(n_overflow),
-                                  _ptr(ws), ws_bytes, _stream(stream)))
+    return _invoke("moe_permute_capped", lib.moe_permute_capped,
+                   _ptr(x), _dt(x), T, d, _ptr(topk_idx), k, E, n_shared, int(capacity),
+                   _dt(x_perm), _ptr(x_perm), _ptr(x_perm_scale), _ptr(counts), _ptr(offsets),
+                   _ptr(perm_src), _ptr(flat_to_row), _ptr(overflow), _ptr(n_overflow), _ptr(ws),
+                   ws_bytes, _stream(stream))
 
 
 def moe_router_stats(prob_sums, counts, T, k, alpha, f, P, summary, *, stream=None):
@@ -239,9 +282,9 @@ def moe_router_stats(prob_sums, counts, T, k, alpha, f, P, summary, *, stream=No
     E = prob_sums.shape[1]
     if prob_sums.shape[0] != prob_sum_blocks(T):
         raise ValueError("prob_sums must have ceil(T/16) = %d rows" % prob_sum_blocks(T))
-    _check("moe_router_stats",
-           lib.moe_router_stats(_ptr(prob_sums), _ptr(counts), T, E, k, float(alpha), _ptr(f),
-                                _ptr(P), _ptr(summary), _stream(stream)))
+    return _invoke("moe_router_stats", lib.moe_router_stats,
+                   _ptr(prob_sums), _ptr(counts), T, E, k, float(alpha), _ptr(f), _ptr(P),
+                   _ptr(summary), _stream(stream))
 
 
 def moe_grouped_gemm_workspace_size(G: int, rows: int, N: int, K: int, dtype, epi: int) -> int:
@@ -263,10 +306,9 @@ def moe_grouped_gemm(A, B, C_out, offsets, *, B2=None, epi=MOE_EPI_NONE, ws=None
         raise ValueError("offsets must have G + 1 = %d entries" % (G + 1))
     pb, pb2, ldb = _weights(B, B2)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check("moe_grouped_gemm", lib.moe_grouped_gemm(_ptr(A), pb, pb2, _dt(A), _ptr(C_out),
-                                                    _dt(C_out), _ptr(offsets), G, rows, N, K,
-                                                    ldb, epi, _ptr(ws), ws_bytes,
-                                                    _stream(stream)))
+    return _invoke("moe_grouped_gemm", lib.moe_grouped_gemm,
+                   _ptr(A), pb, pb2, _dt(A), _ptr(C_out), _dt(C_out), _ptr(offsets), G, rows, N,
+                   K, ldb, epi, _ptr(ws), ws_bytes, _stream(stream))
 
 
 def moe_grouped_gemm_fp8(A_q, A_scale, B_q, B_scale, C_out, offsets, *, B2_q=None,
@@ -279,21 +321,21 @@ def moe_grouped_gemm_fp8(A_q, A_scale, B_q, B_scale, C_out, offsets, *, B2_q=Non
         raise ValueError("offsets must have G + 1 = %d entries" % (G + 1))
     pb, pb2, ldb = _weights(B_q, B2_q)
     c_dt = MOE_E4M3 if C_out.dtype in (torch.uint8, torch.float8_e4m3fn) else _dt(C_out)
-    _check("moe_grouped_gemm_fp8",
-           lib.moe_grouped_gemm_fp8(_ptr(A_q), _ptr(A_scale), pb, _ptr(B_scale), pb2,
-                                    _ptr(B2_scale), _ptr(C_out), c_dt, _ptr(C_scale),
-                                    _ptr(offsets), G, rows, N, K, ldb, epi, _stream(stream)))
+    return _invoke("moe_grouped_gemm_fp8", lib.moe_grouped_gemm_fp8,
+                   _ptr(A_q), _ptr(A_scale), pb, _ptr(B_scale), pb2, _ptr(B2_scale), _ptr(C_out),
+                   c_dt, _ptr(C_scale), _ptr(offsets), G, rows, N, K, ldb, epi, _stream(stream))
 
 
 def moe_combine(Y, flat_to_row, topk_w, out, *, n_shared=0, stream=None):
     T, k = topk_w.shape
     d = Y.shape[1]
-    _check("moe_combine", lib.moe_combine(_ptr(Y), _dt(Y), _ptr(flat_to_row), _ptr(topk_w), T, k,
-                                          d, n_shared, _ptr(out), _dt(out), _stream(stream)))
+    return _invoke("moe_combine", lib.moe_combine,
+                   _ptr(Y), _dt(Y), _ptr(flat_to_row), _ptr(topk_w), T, k, d, n_shared, _ptr(out),
+                   _dt(out), _stream(stream))
 
 
 def moe_quantize_fp8(src, q, scale, *, block_rows=128, block_cols=128, stream=None):
     R, Cn = src.shape
-    _check("moe_quantize_fp8", lib.moe_quantize_fp8(_ptr(src), _dt(src), R, Cn, block_rows,
-                                                    block_cols, _ptr(q), _ptr(scale),
-                                                    _stream(stream)))
+    return _invoke("moe_quantize_fp8", lib.moe_quantize_fp8,
+                   _ptr(src), _dt(src), R, Cn, block_rows, block_cols, _ptr(q), _ptr(scale),
+                   _stream(stream))

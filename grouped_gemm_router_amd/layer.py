@@ -76,6 +76,8 @@ class MoELayer:
             self.w_up = padded_weights(w_up)
             self.w_down = padded_weights(w_down)
         self._T = None
+        self._gen = 0  # bumped whenever alloc() replaces the buffers
+        self._fwd_key, self._fwd_steps = None, None
 
     def _quant(self, w):
         G, R, Cn = w.shape
@@ -141,44 +143,47 @@ class MoELayer:
             # out would be two roundings of the largest outputs
             self.y = torch.empty((rows, self.d), dtype=torch.float32, device=dev)
         self._T = T
+        self._gen += 1
 
     def steps(self, x, out):
-        """The five calls, as (name, thunk) pairs, for timing each one."""
-        E, ns = self.E, self.n_shared
-        s = [("route", lambda: api.moe_route(x, self.w_router, self.topk_idx, self.topk_w,
-                                             logits=self.logits, logit_bias=self.bias,
-                                             flags=self.flags, prob_sums=self.prob_sums,
-                                             ws=self.ws)),
+        """The five calls on x -> out, as (name, thunk) pairs (for timing each
+        one): marshalled once here, on the current stream, so a thunk costs
+        one ctypes call.  They stay valid while the layer's buffers do (the
+        next alloc() with another T replaces them)."""
+        ns = self.n_shared
+        d = api.deferred
+        s = [("route", d(api.moe_route, x, self.w_router, self.topk_idx, self.topk_w,
+                         logits=self.logits, logit_bias=self.bias, flags=self.flags,
+                         prob_sums=self.prob_sums, ws=self.ws)),
              ("permute", self._permute_fn(x))]
         if self.fp8:
-            s.append(("gemm_gate_up", lambda: api.moe_grouped_gemm_fp8(
-                self.x_perm, self.x_scale, self.wg_q, self.wg_s, self.h, self.offsets,
-                B2_q=self.wu_q, B2_scale=self.wu_s, C_scale=self.h_scale,
+            s.append(("gemm_gate_up", d(
+                api.moe_grouped_gemm_fp8, self.x_perm, self.x_scale, self.wg_q, self.wg_s, self.h,
+                self.offsets, B2_q=self.wu_q, B2_scale=self.wu_s, C_scale=self.h_scale,
                 epi=api.MOE_EPI_SWIGLU)))
-            s.append(("gemm_down", lambda: api.moe_grouped_gemm_fp8(
-                self.h, self.h_scale, self.wd_q, self.wd_s, self.y, self.offsets)))
+            s.append(("gemm_down", d(api.moe_grouped_gemm_fp8, self.h, self.h_scale, self.wd_q,
+                                     self.wd_s, self.y, self.offsets)))
         else:
-            s.append(("gemm_gate_up", lambda: api.moe_grouped_gemm(
-                self.x_perm, self.w_gate, self.h, self.offsets, B2=self.w_up,
-                epi=api.MOE_EPI_SWIGLU, ws=self.ws)))
-            s.append(("gemm_down", lambda: api.moe_grouped_gemm(
-                self.h, self.w_down, self.y, self.offsets, ws=self.ws)))
-        s.append(("combine", lambda: api.moe_combine(self.y, self.flat_to_row, self.topk_w, out,
-                                                     n_shared=ns)))
+            s.append(("gemm_gate_up", d(api.moe_grouped_gemm, self.x_perm, self.w_gate, self.h,
+                                        self.offsets, B2=self.w_up, epi=api.MOE_EPI_SWIGLU,
+                                        ws=self.ws)))
+            s.append(("gemm_down", d(api.moe_grouped_gemm, self.h, self.w_down, self.y,
+                                     self.offsets, ws=self.ws)))
+        s.append(("combine", d(api.moe_combine, self.y, self.flat_to_row, self.topk_w, out,
+                               n_shared=ns)))
         return s
 
     def _permute_fn(self, x):
         E, ns = self.E, self.n_shared
         cap = self.capacity(x.shape[0])
         if cap is None:
-            return lambda: api.moe_permute(x, self.topk_idx, E, ns, self.x_perm, self.counts,
-                                           self.offsets, self.perm_src, self.flat_to_row, self.ws,
-                                           x_perm_scale=self.x_scale)
-        return lambda: api.moe_permute_capped(x, self.topk_idx, E, ns, cap, self.x_perm,
-                                              self.counts, self.offsets, self.perm_src,
-                                              self.flat_to_row, self.ws, overflow=self.overflow,
-                                              n_overflow=self.n_overflow,
-                                              x_perm_scale=self.x_scale)
+            return api.deferred(api.moe_permute, x, self.topk_idx, E, ns, self.x_perm,
+                                self.counts, self.offsets, self.perm_src, self.flat_to_row,
+                                self.ws, x_perm_scale=self.x_scale)
+        return api.deferred(api.moe_permute_capped, x, self.topk_idx, E, ns, cap, self.x_perm,
+                            self.counts, self.offsets, self.perm_src, self.flat_to_row, self.ws,
+                            overflow=self.overflow, n_overflow=self.n_overflow,
+                            x_perm_scale=self.x_scale)
 
     def router_stats(self, alpha: float = 0.01):
         """Load-balance statistics of the last forward (needs keep_prob_sums):
@@ -224,7 +229,14 @@ class MoELayer:
         self.alloc(T)
         if out is None:
             out = torch.empty((T, d), dtype=self.out_dtype, device=self.device)
-        for _, fn in self.steps(x, out):
+        # the marshalled calls are kept while x, out, the stream and the
+        # buffers stay the same (a serving loop that reuses its tensors); they
+        # hold the last x and out until then
+        key = (x.data_ptr(), out.data_ptr(), torch.cuda.current_stream().cuda_stream,
+               self._gen)
+        if key != self._fwd_key:
+            self._fwd_steps, self._fwd_key = self.steps(x, out), key
+        for _, fn in self._fwd_steps:
             fn()
         return out
 

@@ -251,3 +251,30 @@ def test_padded_weights_layout():
         p = padded_weights(w)
         assert p.shape == w.shape and p.stride() == (shape[1] * ldb, ldb, 1), (shape, dt)
         assert torch.equal(p, w)
+
+
+def test_deferred_calls_marshal_now_and_call_later():
+    """api.deferred checks and marshals an entry's arguments at once and
+    returns a thunk that makes the library call each time it runs; here the
+    call is one the library rejects on the host (k = 0) before any launch."""
+    import torch
+    from grouped_gemm_router_amd import api
+
+    class Stream:
+        cuda_stream = 0
+    Y = torch.zeros((8, 64), dtype=torch.float32)
+    flat = torch.zeros((0,), dtype=torch.int32)
+    w = torch.zeros((4, 0), dtype=torch.float32)
+    out = torch.zeros((4, 64), dtype=torch.float32)
+    with pytest.raises(api.MoEError) as now:
+        api.moe_combine(Y, flat, w, out, stream=Stream())
+    thunk = api.deferred(api.moe_combine, Y, flat, w, out, stream=Stream())
+    for _ in range(2):
+        with pytest.raises(api.MoEError) as later:
+            thunk()
+        assert later.value.status == now.value.status == api.MOE_ERR_INVALID
+    with pytest.raises(TypeError):   # not a library call
+        api.deferred(api.moe_permute_workspace_size, 16, 2, 8)
+    with pytest.raises(ValueError):  # array shapes are still checked when marshalling
+        api.deferred(api.moe_grouped_gemm, torch.zeros((4, 64)), torch.zeros((2, 8, 32)),
+                     torch.zeros((4, 8)), torch.zeros((3,), dtype=torch.int32), stream=Stream())
