@@ -234,3 +234,29 @@ def test_graph_replays_match_eager(name):
         y = (x.float() * 2.0).sum()
         torch.cuda.synchronize()
         assert torch.equal(other.view(bits), eager.view(bits)) and torch.isfinite(y)
+
+
+def test_forward_keeps_and_refreshes_its_marshalled_calls():
+    """forward() keeps its five marshalled calls while x, out, the stream and
+    the buffers stay the same, and builds new ones when any changes: switching
+    between inputs, output buffers and token counts must give the same bits as
+    a fresh layer does for each input."""
+    from grouped_gemm_router_amd.layer import MoELayer
+    cfg = next(c for c in SMALL if c.name == "mixtral_small")
+    layer, x, wr, bias, (wg, wu, wd) = build_layer(cfg)
+    x2 = synth.randn(tuple(x.shape), 1.0, 4242, DEV, x.dtype)
+    x3 = x2[: cfg.T // 2 + 5].contiguous()          # another token count: new buffers
+
+    def fresh(inp):
+        f = MoELayer(wr, wg, wu, wd, cfg.k, n_shared=cfg.n_shared, bias=bias)
+        return f(inp).clone()
+    want = {id(t): fresh(t) for t in (x, x2, x3)}
+    bits = torch.int16
+    buf = torch.empty_like(want[id(x)])
+    for t in (x, x2, x, x3, x2, x, x3):
+        got = layer(t).clone()
+        assert torch.equal(got.view(bits), want[id(t)].view(bits))
+        if t.shape[0] == cfg.T:                     # the same call into a caller's buffer
+            layer(t, out=buf)
+            torch.cuda.synchronize()
+            assert torch.equal(buf.view(bits), want[id(t)].view(bits))
