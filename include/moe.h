@@ -24,7 +24,8 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers to dense row-major arrays with
- *     no strides, 16-byte aligned.  The caller allocates and frees every
+ *     no strides, 16-byte aligned (one exception: the grouped GEMMs' weights
+ *     may have a row pitch ldb >= K).  The caller allocates and frees every
  *     buffer; the library never allocates, frees, synchronises or copies
  *     device data to the host.
  *   - Every call only enqueues kernels on `stream` (a hipStream_t; NULL is
