@@ -5,7 +5,7 @@ layer's arithmetic (no routing, no permutation, no GEMM, no quantisation), so
 both the HIP path and the CPU oracle may take their inputs from it.  It
 imports torch only; it does not load the HIP library.
 
-Recipe (stated once here and in the design notes):
+Recipe:
 
 * Every tensor is drawn with ``torch.randn`` / ``torch.rand`` from its own
   ``torch.Generator`` seeded with ``seed(cfg_id, tensor, group, matrix)``;
