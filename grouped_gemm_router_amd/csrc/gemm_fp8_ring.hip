@@ -208,15 +208,19 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint8_t *__rest
   // scales(d+1), B(d+2), so waiting until only the last B's IB loads may be
   // outstanding makes A(d), scales(d) and B(d) land; one barrier per double
   // step makes them visible and frees the slots of double step d-1, which
-  // take A(d+1) and B(d+2).  Past the end the last block is re-loaded into
-  // slots nobody reads, so the count never changes.
+  // take A(d+1) and B(d+2).  The wait also covers the wave's own LDS reads
+  // (lgkmcnt 0): the compiler may sink the last multiplies of step d-1 below
+  // the barrier, and a read of a step d-1 slot still queued there could
+  // otherwise return data of the refill another wave issues right after it.
+  // Past the end the last block is re-loaded into slots nobody reads, so the
+  // count never changes.
   MOE_ISSUE_A(ring.a0, ring.s0, 0);
   MOE_ISSUE_B(ring.b0, 0);
   MOE_ISSUE_B(ring.b1, min(1, KB - 1));
 
 #define MOE_DSTEP(tA, tS, tB, nA, nS, nB, dd)                                               \
   {                                                                                         \
-    wait_vmcnt<IB>();                                                                       \
+    wait_vmcnt_lgkm0<IB>();                                                                 \
     stage_barrier();                                                                        \
     _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) {                                     \
       const int r = wm * (MI * 32) + mi * 32 + fr;                                          \

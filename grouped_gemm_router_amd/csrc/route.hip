@@ -294,12 +294,13 @@ __global__ __launch_bounds__(LTH, 1) void route_logits_split(
         acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[nb], acc[mi][nb], 0, 0, 0); \
   }
 // stage s in slot s % 3: wait for this wave's loads of stage s (those of
-// stage s + 1 may stay in flight), meet (every wave is then past stage s - 1,
-// whose slot is free), refill that slot with stage s + 2 (past the end the
-// last stage again, into a slot nobody reads, so the counts never change),
-// multiply
+// stage s + 1 may stay in flight) and for its own LDS reads (the compiler
+// may sink stage s - 1's last multiplies below the barrier, with their reads
+// still queued), meet (every wave is then past stage s - 1, whose slot is
+// free), refill that slot with stage s + 2 (past the end the last stage
+// again, into a slot nobody reads, so the counts never change), multiply
 #define MOE_RSTAGE(CA, CB, NA, NB, S)                                                          \
-  wait_vmcnt<LIA + LIB>();                                                                    \
+  wait_vmcnt_lgkm0<LIA + LIB>();                                                              \
   stage_barrier();                                                                            \
   MOE_RISSUE(NA, NB, min((S) + 2, ns - 1))                                                    \
   MOE_RCOMPUTE(CA, CB)
