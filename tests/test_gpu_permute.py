@@ -95,8 +95,11 @@ def test_permute_bit_exact(orc, T, E, k, ns, d, kind, dt):
     np.testing.assert_array_equal(np_of(x_perm), ref)
 
 
+# E4M3 rows take the three launches at every size; the DeepSeek routing
+# shape (T k = 32768) and one token past it are among the cases
 @pytest.mark.parametrize("T,E,k,ns,d", [(70, 8, 2, 0, 256), (300, 256, 8, 1, 512),
                                         (4096, 8, 2, 0, 128), (5, 3, 3, 2, 1024),
+                                        (4096, 256, 8, 1, 256), (4097, 256, 8, 1, 256),
                                         (9000, 8, 4, 1, 128)])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_permute_fp8_quantisation_bit_exact(orc, T, E, k, ns, d, dt):
