@@ -530,9 +530,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
 
 // Sum of the S partial tiles of each split tile, in slice order, then the
 // epilogue.  Work item (j, rb) is rows [16 rb, 16 rb + 16) of split tile j;
-// the grid is four workgroups per CU looping over the items, so the launch
-// stays cheap when nothing was split (the plan is only known on the
-// device).  A thread owns RPT (row, 4-column group) pairs of an item and
+// items run row block by row block across the split tiles (item = rb *
+// n_split + j), so the live blocks of short tiles are all taken in the
+// grid's first pass (decode-size layer: down 190 -> 180 us, gate/up 337 ->
+// 331 us, against tile by tile); the grid is four workgroups per CU looping
+// over the items, so the launch stays cheap when nothing was split (the
+// plan is only known on the device).  A thread owns RPT (row, 4-column group) pairs of an item and
 // issues the loads of all of them, every slice, before the first add (16
 // bytes per partial); the adds then run in slice order.
 constexpr int kReduceRows = 16;
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const char *__restric
   constexpr int RPT = kReduceRows * C4 / 256;   // (row, group) pairs per thread
   static_assert(RPT * 256 == kReduceRows * C4, "an item is a whole number of passes");
   for (int item = blockIdx.x; item < n_split * RB; item += gridDim.x) {
-    const int j = item / RB, r0 = (item % RB) * kReduceRows;
+    const int j = item % n_split, r0 = (item / n_split) * kReduceRows;
     const int4 d = reinterpret_cast<const int4 *>(ws + split_desc_offset())[j];
     const int h = d.y - d.x;
     if (r0 >= h) continue;
