@@ -170,6 +170,39 @@ def test_fp8_gemm_bf16_out(orc, sizes, N, K, swiglu):
     assert_within(C.float().cpu().numpy(), ref, bound)
 
 
+# The hardware behaviour behind the per-block allowance above, measured
+# through the library on both kernels (K = 128: the general kernel's
+# 16x16x128 instruction; K = 256: the LDS-ring kernel's 32x32x64 one).  Row
+# r of A holds L = 256, -L and s = 2^-6 at adjacent k (one inner group), B is
+# all ones, every scale 1: the exact result is s, and the products meet
+# inside one instruction, where s < L 2^-13 is lost.  s = 2^-4 (> L 2^-12)
+# survives.  Every result stays within 128 2^-12 max_k |a_k b_k| = 8 of s.
+E4M3_256, E4M3_M256, E4M3_ONE = 0x78, 0xF8, 0x38
+E4M3_2M6, E4M3_2M4 = 0x08, 0x18  # 2^-6 (smallest normal), 2^-4
+
+
+@pytest.mark.parametrize("K", [128, 256])
+def test_fp8_block_sum_loses_small_terms_beside_large_ones(K):
+    a = api()
+    rows, N = 4, 128
+    Aq = torch.zeros((rows, K), dtype=torch.uint8)
+    for r, (k0, code) in enumerate([(0, E4M3_2M6), (4, E4M3_2M6), (0, E4M3_2M4), (0, 0)]):
+        Aq[r, k0], Aq[r, k0 + 1], Aq[r, k0 + 2] = E4M3_256, E4M3_M256, code
+    Bq = torch.full((1, N, K), E4M3_ONE, dtype=torch.uint8)
+    As = torch.ones((K // 128, rows), dtype=torch.float32)
+    Bs = torch.ones((1, N // 128, K // 128), dtype=torch.float32)
+    offs = np.array([0, rows], dtype=np.int32)
+    C = torch.full((rows, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    a.moe_grouped_gemm_fp8(Aq.to(DEV), As.to(DEV), Bq.to(DEV), Bs.to(DEV), C,
+                           torch.from_numpy(offs).to(DEV))
+    torch.cuda.synchronize()
+    got = C.float().cpu().numpy()
+    exact = np.array([2.0 ** -6, 2.0 ** -6, 2.0 ** -4, 0.0])
+    assert (np.abs(got - exact[:, None]) <= 128 * 2.0 ** -12 * 256).all()
+    assert (got[0] == 0.0).all() and (got[1] == 0.0).all()   # s < L 2^-13: lost
+    assert (got[2] == 2.0 ** -4).all() and (got[3] == 0.0).all()
+
+
 def pad_rows_e4m3(Bq, pad):
     """Bq [G][N][K] E4M3 codes as a view of [G][N][K + pad] storage whose pad
     bytes hold the E4M3 NaN code 0x7F: a kernel that read past a row's first
