@@ -6,8 +6,9 @@
 // "MoE in practice" §3.2 fuses the logits with the softmax and moves top-k to
 // the GPU.
 //
-// E <= 32: one launch (route_small_bf16 / route_small_f32), scoring,
-// softmax and top-k of 16 tokens per workgroup, no workspace.
+// E <= 32: one launch (route_small_bf16_lds for bf16 with d % 64 == 0,
+// route_small_bf16 for other d, route_small_f32), scoring, softmax and
+// top-k of 16 tokens per workgroup, no workspace.
 // E > 32: two launches,
 //   logits   a split-K GEMM x [T][d] . w_router[E][d]^T on the matrix cores
 //            writing fp32 partial logits part[s][t][e] to the workspace
@@ -377,76 +378,23 @@ __device__ __forceinline__ float select_segment(float v, bool ok, int e, int k, 
   return ok ? ex / z : 0.f;
 }
 
-// ---------------------------------------------------------------------------
-// E <= 32, bf16: one launch.  A workgroup (8 waves) owns 16 tokens.  The
-// logits are a 16 x EC matrix product on the matrix cores
-// (v_mfma_f32_16x16x32_bf16, tokens as rows, NB blocks of 16 experts as
-// columns, EC = 16 NB): the waves split the d axis in 32-column steps (wave
-// w takes steps w, w + 8, ...) and load both operands straight into
-// registers (lane l: row l % 16, columns 8 (l / 16) .. + 8 of the step, 16
-// bytes), eight steps' loads issued before their MFMAs, with clamped
-// addresses and masked values (lanes of padding experts load nothing); the
-// matrix cores do the reduction over d that a lane-parallel dot product
-// would need shuffles for.  The eight waves' partial products are added in
-// wave order through LDS; then one token per ES-lane segment (ES = E rounded
-// up to 8, 16 or 32) takes the softmax and top-k, and the probability sums
-// of the 16 tokens are written per expert.  Measured on the Mixtral shapes
-// against a one-launch kernel of bf16 dot products per lane and a 63-step
-// butterfly reduce-scatter per wave (8 tokens per workgroup): the same time
-// (12.4 against 12.2 us), with fewer instructions and no shuffles.
+// The end of the one-launch bf16 routes: the eight waves' 16 x EC partial
+// logits (acc, 16x16 MFMA layout) added in wave order through LDS, then one
+// token per ES-lane segment selects, and the 16 tokens' probability sums
+// are written per expert.  Called by all 512 threads.
 template <int NB, int ES>
-__global__ __launch_bounds__(512) void route_small_bf16(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
-    const float *__restrict__ bias, int T, int d, int E, int k, int renorm,
-    float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
-    float *__restrict__ prob_sums) {
-  constexpr int NW = 8, EC = NB * 16, U = 8;
-  static_assert(ES <= EC, "segment wider than the computed columns");
+__device__ __forceinline__ void small_finish(const f32x4 (&acc)[NB], const float *__restrict__ bias,
+                                             int T, int E, int k, int renorm,
+                                             float *__restrict__ logits_out,
+                                             int32_t *__restrict__ topk_idx,
+                                             float *__restrict__ topk_w,
+                                             float *__restrict__ prob_sums) {
+  constexpr int NW = 8, EC = NB * 16;
   __shared__ float s_acc[NW][kSumBlock][EC + 1];
   __shared__ float s_p[kSumBlock][EC + 1];
   const int lane = lane_id(), wv = threadIdx.x / kWave;
   const int t0 = blockIdx.x * kSumBlock;
   const int r = lane & 15, q = lane >> 4;
-  const int nsteps = (d + 31) / 32;
-  const bool a_ok = t0 + r < T;
-  const uint16_t *xa = x + (size_t)min(t0 + r, T - 1) * d;
-  const uint16_t *wb[NB];
-  bool b_ok[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int e = b * 16 + r;
-    b_ok[b] = e < E;
-    wb[b] = wr + (size_t)min(e, E - 1) * d;
-  }
-  f32x4 acc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = f32x4{};
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  for (int s0 = wv; s0 < nsteps; s0 += NW * U) {
-    u32x4 av[U], bv[U][NB];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int cc = min((s0 + u * NW) * 32 + q * 8, d - 8);
-      av[u] = *reinterpret_cast<const u32x4 *>(xa + cc);
-      // lanes of the padding columns (e >= E) load nothing: with E = 8 that
-      // halves the router-weight requests (Mixtral shapes: 15 -> 14 us)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        bv[u][b] = zero4;
-        if (b_ok[b]) bv[u][b] = *reinterpret_cast<const u32x4 *>(wb[b] + cc);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool in = (s0 + u * NW) * 32 + q * 8 < d;
-      const bf16x8 a = __builtin_bit_cast(bf16x8, (in && a_ok) ? av[u] : zero4);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const bf16x8 w = __builtin_bit_cast(bf16x8, (in && b_ok[b]) ? bv[u][b] : zero4);
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[b], 0, 0, 0);
-      }
-    }
-  }
   // 16x16 accumulator layout: lane holds column (expert) lane % 16 and rows
   // (tokens) 4 (lane / 16) + i in register i
 #pragma unroll
@@ -493,6 +441,168 @@ __global__ __launch_bounds__(512) void route_small_bf16(
       prob_sums[(size_t)blockIdx.x * E + threadIdx.x] = sum;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// E <= 32, bf16: one launch.  A workgroup (8 waves) owns 16 tokens.  The
+// logits are a 16 x EC matrix product on the matrix cores
+// (v_mfma_f32_16x16x32_bf16, tokens as rows, NB blocks of 16 experts as
+// columns, EC = 16 NB): the waves split the d axis in 32-column steps (wave
+// w takes steps w, w + 8, ...) and load both operands straight into
+// registers (lane l: row l % 16, columns 8 (l / 16) .. + 8 of the step, 16
+// bytes), eight steps' loads issued before their MFMAs, with clamped
+// addresses and masked values (lanes of padding experts load nothing); the
+// matrix cores do the reduction over d that a lane-parallel dot product
+// would need shuffles for.  The eight waves' partial products are added in
+// wave order through LDS; then one token per ES-lane segment (ES = E rounded
+// up to 8, 16 or 32) takes the softmax and top-k, and the probability sums
+// of the 16 tokens are written per expert.  Measured on the Mixtral shapes
+// against a one-launch kernel of bf16 dot products per lane and a 63-step
+// butterfly reduce-scatter per wave (8 tokens per workgroup): the same time
+// (12.4 against 12.2 us), with fewer instructions and no shuffles.
+template <int NB, int ES>
+__global__ __launch_bounds__(512) void route_small_bf16(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+    const float *__restrict__ bias, int T, int d, int E, int k, int renorm,
+    float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    float *__restrict__ prob_sums) {
+  constexpr int NW = 8, EC = NB * 16, U = 8;
+  static_assert(ES <= EC, "segment wider than the computed columns");
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  const int t0 = blockIdx.x * kSumBlock;
+  const int r = lane & 15, q = lane >> 4;
+  const int nsteps = (d + 31) / 32;
+  const bool a_ok = t0 + r < T;
+  const uint16_t *xa = x + (size_t)min(t0 + r, T - 1) * d;
+  const uint16_t *wb[NB];
+  bool b_ok[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int e = b * 16 + r;
+    b_ok[b] = e < E;
+    wb[b] = wr + (size_t)min(e, E - 1) * d;
+  }
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  for (int s0 = wv; s0 < nsteps; s0 += NW * U) {
+    u32x4 av[U], bv[U][NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int cc = min((s0 + u * NW) * 32 + q * 8, d - 8);
+      av[u] = *reinterpret_cast<const u32x4 *>(xa + cc);
+      // lanes of the padding columns (e >= E) load nothing: with E = 8 that
+      // halves the router-weight requests (Mixtral shapes: 15 -> 14 us)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        bv[u][b] = zero4;
+        if (b_ok[b]) bv[u][b] = *reinterpret_cast<const u32x4 *>(wb[b] + cc);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = (s0 + u * NW) * 32 + q * 8 < d;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, (in && a_ok) ? av[u] : zero4);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const bf16x8 w = __builtin_bit_cast(bf16x8, (in && b_ok[b]) ? bv[u][b] : zero4);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[b], 0, 0, 0);
+      }
+    }
+  }
+  small_finish<NB, ES>(acc, bias, T, E, k, renorm, logits_out, topk_idx, topk_w, prob_sums);
+}
+
+// E <= 32, bf16, d % 64 == 0: the same product with x staged through LDS.
+// Wave w takes the 64-column chunks w, w + 8, ... of the 16 token rows and
+// moves each by two LDS-direct loads of whole 128-byte row pieces (piece p
+// of row r at slot p ^ ((r >> 1) & 7), so the fragment reads hit distinct
+// banks) into its own part of LDS, eight chunks per round (all of a wave's
+// chunks up to d = 4096); the router rows go straight to registers as
+// above.  A wave waits for all of its round's loads, then multiplies; it
+// reads only what it loaded itself, so no workgroup barrier is needed.
+// Measured against the register-staged kernel, one process, by events in
+// the layer: Mixtral shapes 17.8 -> 17.5 us, decode size 13.7 -> 13.0 us.
+constexpr int kRouteChunkRound = 8;  // chunks per round of a wave
+template <int NB, int ES>
+__global__ __launch_bounds__(512) void route_small_bf16_lds(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+    const float *__restrict__ bias, int T, int d, int E, int k, int renorm,
+    float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    float *__restrict__ prob_sums) {
+  constexpr int NW = 8, CR = kRouteChunkRound;
+  static_assert(ES <= NB * 16, "segment wider than the computed columns");
+  __shared__ u32x4 s_x[NW][CR][16 * 8];  // per wave: CR chunks of 16 rows x 8 pieces
+  const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t0 = blockIdx.x * kSumBlock;
+  const int r = lane & 15, q = lane >> 4;
+  const int nch = d / 64;
+  const int mine = nch > wv ? (nch - wv + NW - 1) / NW : 0;  // chunks of this wave
+  // LDS-direct sources: lane j of load h (0, 1) fills slot j of rows
+  // 8 h .. 8 h + 7: row 8 h + j / 8, piece (j % 8) ^ ((row >> 1) & 7)
+  const uint16_t *xs[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * h + (lane >> 3);
+    xs[h] = x + (size_t)min(t0 + row, T - 1) * d + (((lane & 7) ^ ((row >> 1) & 7)) * 8);
+  }
+  const uint16_t *wb[NB];
+  bool b_ok[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int e = b * 16 + r;
+    b_ok[b] = e < E;
+    wb[b] = wr + (size_t)min(e, E - 1) * d;
+  }
+  const bool a_ok = t0 + r < T;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{};
+  for (int j0 = 0; j0 < mine; j0 += CR) {
+    // a round always loads CR chunks (past the wave's last chunk it loads
+    // that one again and does not multiply it), so the loads stay unrolled
+    // into registers
+    u32x4 bv[CR][2][NB];
+#pragma unroll
+    for (int i = 0; i < CR; ++i) {
+      const int c = wv + NW * min(j0 + i, mine - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        __builtin_amdgcn_global_load_lds((const void *)(xs[h] + (size_t)c * 64),
+                                         (lds_void *)(&s_x[wv][i][h * 64]), 16, 0, 0);
+      // lanes of the padding experts (e >= E) load nothing
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          bv[i][st][b] = zero4;
+          if (b_ok[b])
+            bv[i][st][b] = *reinterpret_cast<const u32x4 *>(wb[b] + (size_t)c * 64 + st * 32 + q * 8);
+        }
+    }
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");  // no LDS read moves above the wait
+#pragma unroll
+    for (int i = 0; i < CR; ++i) {
+      if (j0 + i >= mine) continue;  // wave-uniform
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int p = st * 4 + q;
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, a_ok ? s_x[wv][i][r * 8 + (p ^ ((r >> 1) & 7))] : zero4);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv[i][st][b]),
+                                                          acc[b], 0, 0, 0);
+      }
+    }
+    // every fragment read of this round is complete before the next round's
+    // loads rewrite the slots
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  small_finish<NB, ES>(acc, bias, T, E, k, renorm, logits_out, topk_idx, topk_w, prob_sums);
 }
 
 // E <= 32, fp32: one launch.  A workgroup of 16 ES threads owns 16 tokens;
@@ -754,8 +864,12 @@ hipError_t launch_route(const void *x, const void *w_router, int dt, const float
       const uint16_t *xb = static_cast<const uint16_t *>(x);
       const uint16_t *wb = static_cast<const uint16_t *>(w_router);
 #define MOE_SMALL(NB, ES)                                                                    \
-  hipLaunchKernelGGL((route_small_bf16<NB, ES>), dim3(nblk), dim3(512), 0, s, xb, wb, bias, T, \
-                     d, E, k, renorm, logits, topk_idx, topk_w, prob_sums)
+  if (d % 64 == 0)                                                                           \
+    hipLaunchKernelGGL((route_small_bf16_lds<NB, ES>), dim3(nblk), dim3(512), 0, s, xb, wb,   \
+                       bias, T, d, E, k, renorm, logits, topk_idx, topk_w, prob_sums);       \
+  else                                                                                       \
+    hipLaunchKernelGGL((route_small_bf16<NB, ES>), dim3(nblk), dim3(512), 0, s, xb, wb, bias, \
+                       T, d, E, k, renorm, logits, topk_idx, topk_w, prob_sums)
       if (es == 8) MOE_SMALL(1, 8);
       else if (es == 16) MOE_SMALL(1, 16);
       else MOE_SMALL(2, 32);

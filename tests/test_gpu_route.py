@@ -124,6 +124,13 @@ def check_selection(idx, lg_ref, bound, k):
     ("bf16", 65, 512, 30, 5, False),
     # E < 8 in 8-lane segments, d = 2048 (one chunk per lane and wave)
     ("bf16", 9, 2048, 5, 2, True),
+    # d % 64 == 0 stages x through LDS: one 64-column chunk (seven waves
+    # idle), nine chunks over eight waves, two rounds of eight chunks per
+    # wave (d = 8192) with 8-, 16- and 32-lane segments
+    ("bf16", 33, 64, 8, 2, False),
+    ("bf16", 50, 576, 16, 3, True),
+    ("bf16", 70, 8192, 8, 2, False),
+    ("bf16", 40, 8192, 32, 8, True),
     # split-K MFMA logits (d % 64 == 0): 48 experts of a 256-wide tile, three
     # token tiles with a ragged tail; two expert tiles, the second ragged
     ("bf16", 257, 2048, 48, 4, False),
