@@ -72,6 +72,8 @@ constexpr int SLOTS_B2 = BN * PIECES_B;    // 16-byte slots per B double stage (
 
 __device__ __forceinline__ int swzb(int row, int p) { return p ^ ((row >> 1) & 7); }
 
+constexpr long long kLastLevelCacheBytes = 256LL << 20;  // the MI355X MALL
+
 // B-tile row of wave column wn (of NWN), 32-row block nb
 template <bool SWIGLU, int NWN>
 __device__ __forceinline__ int b_row(int wn, int nb) {
@@ -182,7 +184,7 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
                                          const uint16_t *__restrict__ B2, void *__restrict__ C,
                                          int rows, int N, int K, int ldb, int kbeg, int KT,
                                          float *__restrict__ part, u32x4 *sA0, u32x4 *sA1,
-                                         u32x4 *sB0, u32x4 *sB1, u32x4 *sB2) {
+                                         u32x4 *sB0, u32x4 *sB1, u32x4 *sB2, bool nt_store) {
   constexpr int NWN = NW / 2;                 // wave columns (2 wave rows)
   constexpr int MI = BM / 64;                 // 32-row blocks per wave
   constexpr int NB = (BN / NWN) / 32;         // 32-column blocks per wave
@@ -338,7 +340,11 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
   if constexpr (OUT_F32 && !SWIGLU) {
     // fp32 output: every store already writes whole 128-byte row pieces
     // (32 lanes x 4 bytes), so no staging; measured against the staged
-    // path: DeepSeek-shape down 2.01 -> 1.97 ms, Mixtral-shape 0.94 -> 0.93
+    // path: DeepSeek-shape down 2.01 -> 1.97 ms, Mixtral-shape 0.94 -> 0.93.
+    // An output larger than the last-level cache streams to HBM anyway and
+    // is stored non-temporally (DeepSeek shapes, 1.06 GB: down 1880 ->
+    // 1823 us, the combine that reads it 229 -> 221 us; an output that fits,
+    // as on the Mixtral shapes, stays cached for the combine)
     float *const cb = static_cast<float *>(C) + (size_t)tile.nt * BN + col;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -347,8 +353,14 @@ __device__ __forceinline__ void run_tile(const Tile &tile, const uint16_t *__res
         const int m = tile.m0 + wm * (MI * 32) + mi * 32 + 8 * (r >> 2) + rbase + (r & 3);
         if (m < tile.mend) {
           float *const rp = cb + (size_t)m * N;
+          if (nt_store) {
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) rp[b_row<SWIGLU, NWN>(wn, nb)] = acc[mi][nb][r];
+            for (int nb = 0; nb < NB; ++nb)
+              __builtin_nontemporal_store(acc[mi][nb][r], &rp[b_row<SWIGLU, NWN>(wn, nb)]);
+          } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) rp[b_row<SWIGLU, NWN>(wn, nb)] = acc[mi][nb][r];
+          }
         }
       }
     return;
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const uint16_t *__restrict__ B2, void *__restrict__ C, const int32_t *__restrict__ offsets,
     int G, int rows, int N, int K, int ldb, int nt_count, char *__restrict__ ws, int cus,
-    int xcd_run) {
+    int xcd_run, int nt_store) {
   // 2 A double stages (64 KB) and 3 B double stages (96 KB): all 160 KB of LDS.
   // The scheduler's result (8 ints) passes through the last B slot, which is
   // first loaded after every wave has passed the prologue barrier.
@@ -528,7 +540,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
   // flow cost more than the saved MFMAs there.
 #define MOE_TILE(BMV, SKIPV)                                                                  \
   run_tile<BMV, SWIGLU, OUT_F32, NW, SKIPV>(tile, A, B, B2, C, rows, N, K, ldb, kbeg, kt, part, sA0, \
-                                            sA1, sB0, sB1, sB2)
+                                            sA1, sB0, sB1, sB2, nt_store != 0)
   if (h > 128) {
     if (SWIGLU && h <= 224) MOE_TILE(256, SWIGLU); else MOE_TILE(256, false);
   } else if (h > 64) {
@@ -625,10 +637,11 @@ void launch_t(const void *A, const void *B, const void *B2, void *C, const int32
   // gate/up 3139 -> 3099 us; the down projection was slower that way, 1906 ->
   // 2011 us, and keeps the default order)
   const int xcd_run = (SWIGLU && (long long)rows <= 256LL * G) ? nt : 0;
+  const int nt_store = (OUT_F32 && !SWIGLU && (long long)rows * N * 4 > kLastLevelCacheBytes) ? 1 : 0;
   hipLaunchKernelGGL((gemm_bf16_kernel<SWIGLU, OUT_F32, NW>), dim3((unsigned)((bound + 7) / 8 * 8)),
                      dim3(NW * 64), 0, s, static_cast<const uint16_t *>(A),
                      static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(B2), C,
-                     offsets, G, rows, N, K, ldb, nt, ws, cus, xcd_run);
+                     offsets, G, rows, N, K, ldb, nt, ws, cus, xcd_run, nt_store);
   if (ws == nullptr) return;
   hipLaunchKernelGGL((split_reduce_kernel<SWIGLU, OUT_F32>), dim3((unsigned)(kReduceWGPerCU * cus)),
                      dim3(256), 0, s,
