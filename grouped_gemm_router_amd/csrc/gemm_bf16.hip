@@ -501,10 +501,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
       // XCD-local order: in every whole block of 8 xcd_run workgroups, XCD x
       // (the workgroups w = x mod 8) takes xcd_run consecutive tile ids
       if (xcd_run <= 0) return w;
-      const int B = 8 * xcd_run, blk = w / B;
-      if ((blk + 1) * B > full_end) return w;
-      const int i = w - blk * B;
-      return blk * B + (i % 8) * xcd_run + i / 8;
+      const int span = 8 * xcd_run, blk = w / span;
+      if ((blk + 1) * span > full_end) return w;
+      const int i = w - blk * span;
+      return blk * span + (i % 8) * xcd_run + i / 8;
     }
     const int jj = (w - full_end) / S;
     return jj < n_split ? full_end + jj : -1;
@@ -558,9 +558,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(
 // grid's first pass (decode-size layer: down 190 -> 180 us, gate/up 337 ->
 // 331 us, against tile by tile); the grid is four workgroups per CU looping
 // over the items, so the launch stays cheap when nothing was split (the
-// plan is only known on the device).  A thread owns RPT (row, 4-column group) pairs of an item and
-// issues the loads of all of them, every slice, before the first add (16
-// bytes per partial); the adds then run in slice order.
+// plan is only known on the device).  A thread owns RPT (row, 4-column
+// group) pairs of an item and issues the loads of all of them, every slice,
+// before the first add (16 bytes per partial); the adds then run in slice
+// order.
 constexpr int kReduceRows = 16;
 constexpr int kReduceWGPerCU = 4;
 
