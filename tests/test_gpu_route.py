@@ -39,8 +39,12 @@ def run_from_logits(lg: np.ndarray, k: int, renorm=False):
     return idx.cpu().numpy(), w.cpu().numpy()
 
 
+# every select path: one expert per lane (E <= 64), two, four (E <= 256,
+# with 16-byte loads when E % 4 == 0 and without: E = 201), eight and
+# sixteen; E = 1024 and k = 32 are the library's limits
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (37, 8, 2), (300, 8, 2), (129, 256, 8),
-                                   (64, 32, 32), (50, 1000, 32), (33, 65, 3)])
+                                   (64, 32, 32), (50, 1000, 32), (33, 65, 3), (45, 201, 7),
+                                   (70, 400, 9), (20, 1024, 32)])
 @pytest.mark.parametrize("renorm", [False, True])
 def test_from_logits_random(orc, T, E, k, renorm):
     rng = np.random.default_rng(T * 1000 + E + k)
