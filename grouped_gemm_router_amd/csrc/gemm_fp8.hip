@@ -71,7 +71,7 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
   const uint8_t *pb[B_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
-    const int m = min(tile.m0 + lrow + 32 * i, rows - 1);
+    const int m = min(tile.m0 + lrow + 32 * i, tile.mend - 1);  // dead rows: the last row
     pa[i] = Aq + (size_t)m * K + lpc * 16;
   }
   const size_t goff = (size_t)tile.g * N * ldb;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(FNTH, 1) void gemm_fp8_kernel(
     pb[i] = base + goff + (size_t)n * ldb + lpc * 16;
   }
   // activation scale row handled by this thread (threads < 128)
-  const int srow = min(tile.m0 + tid, rows - 1);
+  const int srow = min(tile.m0 + tid, tile.mend - 1);
   const float *psa = As + srow;  // [K/128][rows]
   // weight scales of this wave column: [g][n-block][kb]
   const float *psb;
