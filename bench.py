@@ -86,8 +86,9 @@ def step_bytes_flops(cfg, counts, logits_exported=False):
     out["permute"] = (pb, T * d * es + rows * d * act_es + maps
                       + (rows * (d // 128) * 4 if fp8 else 0), 0.0)
     wsc = (active * 2 * (dff // 128) * (d // 128) * 4) if fp8 else 0
+    xsc = rows * (d // 128) * 4 if fp8 else 0     # the activations' 1 x 128 scales
     hsc = rows * (dff // 128) * 4 if fp8 else 0
-    gb = rows * d * act_es + active * 2 * dff * d * w_es + wsc + rows * dff * act_es + hsc
+    gb = rows * d * act_es + xsc + active * 2 * dff * d * w_es + wsc + rows * dff * act_es + hsc
     out["gemm_gate_up"] = (gb, gb, 2.0 * rows * d * 2 * dff)
     y_alg = es                       # Y as the method stores it (bf16; fp32 layer: fp32)
     y_impl = es if fp8 or es == 4 else 4   # the bf16 layers keep Y in fp32
