@@ -94,7 +94,7 @@ def step_bytes_flops(cfg, counts, logits_exported=False):
     y_impl = es if fp8 or es == 4 else 4   # the bf16 layers keep Y in fp32
     db = rows * dff * act_es + hsc + active * d * dff * w_es + wsc // 2
     out["gemm_down"] = (db + rows * d * y_alg, db + rows * d * y_impl, 2.0 * rows * dff * d)
-    cb = T * d * es + T * k * 8 + (T * k + ns * T) * 4
+    cb = T * d * es + T * k * 4 + (T * k + ns * T) * 4  # out, gate weights, flat_to_row
     out["combine"] = (rows * d * y_alg + cb, rows * d * y_impl + cb, 0.0)
     return out
 

@@ -41,8 +41,8 @@ def test_mixtral_gemm_flops_and_bytes():
     assert bf["gemm_down"][1] == h + wd + rows * 4096 * 4
     # route: x and the router weights in, the selection out
     assert bf["route"][0] == 4096 * 4096 * 2 + 8 * 4096 * 2 + 4096 * 2 * 8
-    # combine: Y in (bf16), out, the weights and maps
-    assert bf["combine"][0] == rows * 4096 * 2 + 4096 * 4096 * 2 + 4096 * 2 * 8 + rows * 4
+    # combine: Y in (bf16), out, the gate weights and flat_to_row
+    assert bf["combine"][0] == rows * 4096 * 2 + 4096 * 4096 * 2 + 4096 * 2 * 4 + rows * 4
 
 
 def test_deepseek_counts_active_experts_and_the_shared_one():
